@@ -1,0 +1,233 @@
+"""ctypes binding of libtwell.so: argument marshalling only.
+
+Torch tensors supply device memory (``data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``); every step of the layer runs in
+the library's HIP kernels. There is no fallback: if the library is missing
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtwell.so")
+
+TWELL_F32, TWELL_BF16 = 0, 1
+TILE_C = 128
+DEV_TILE_OVERFLOW, DEV_OVF_CAPACITY, DEV_BAD_INDEX = 1, 2, 4
+
+# every extern "C" symbol include/twell.h declares
+EXPORTS = ("twell_gate_pack", "twell_ffn_fwd", "twell_fwd_workspace_bytes", "twell_to_hybrid",
+           "hybrid_ffn_bwd", "hybrid_bwd_workspace_bytes", "twell_status_str")
+
+c_i32, c_sz, c_p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+
+
+class TwellC(ctypes.Structure):
+    _fields_ = [("T", c_i32), ("d_ff", c_i32), ("width", c_i32), ("dtype", ctypes.c_int),
+                ("count", c_p), ("col", c_p), ("val", c_p)]
+
+
+class HybridC(ctypes.Structure):
+    _fields_ = [("T", c_i32), ("d_ff", c_i32), ("K", c_i32), ("max_ovf", c_i32),
+                ("dtype", ctypes.c_int), ("row_nnz", c_p), ("row_slot", c_p), ("ell_col", c_p),
+                ("ell_val", c_p), ("ovf_rows", c_p), ("dense", c_p), ("n_ovf", c_p)]
+
+
+_lib = None
+
+
+class TwellError(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libtwell.so (built by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise TwellError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                         "(the HIP library is the only implementation; there is no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S = c_p, c_i32, c_sz
+    L.twell_gate_pack.argtypes = [ctypes.c_int, P, P, I, I, ctypes.POINTER(TwellC), P, P]
+    L.twell_ffn_fwd.argtypes = [ctypes.c_int, P, ctypes.POINTER(TwellC), P, P, I, P, P, S, P, P]
+    L.twell_fwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I]
+    L.twell_fwd_workspace_bytes.restype = S
+    L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P]
+    L.hybrid_ffn_bwd.argtypes = [ctypes.c_int, P, P, ctypes.POINTER(HybridC), P, P, P, I,
+                                 P, P, P, P, P, S, P, P]
+    L.hybrid_bwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I, I]
+    L.hybrid_bwd_workspace_bytes.restype = S
+    L.twell_status_str.argtypes = [ctypes.c_int]
+    L.twell_status_str.restype = ctypes.c_char_p
+    for f in ("twell_gate_pack", "twell_ffn_fwd", "twell_to_hybrid", "hybrid_ffn_bwd"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise TwellError(f"{what}: {load().twell_status_str(rc).decode()} (status {rc})")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TWELL_BF16
+    if t.dtype == torch.float32:
+        return TWELL_F32
+    raise TwellError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else c_p(t.data_ptr())
+
+
+def _stream(device) -> c_p:
+    return c_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclass
+class Twell:
+    """TwELL arrays (device tensors) of h = ReLU(x W_g)."""
+
+    count: torch.Tensor  # [T][d_ff/128] int32
+    col: torch.Tensor    # [T][d_ff/128][width] int16
+    val: torch.Tensor    # [T][d_ff/128][width] dtype
+
+    @property
+    def T(self):
+        return self.count.shape[0]
+
+    @property
+    def d_ff(self):
+        return self.count.shape[1] * TILE_C
+
+    @property
+    def width(self):
+        return self.col.shape[2]
+
+    def c(self) -> TwellC:
+        return TwellC(self.T, self.d_ff, self.width, _dt(self.val), self.count.data_ptr(),
+                      self.col.data_ptr(), self.val.data_ptr())
+
+
+@dataclass
+class Hybrid:
+    """Hybrid ELL + dense-backup arrays (device tensors)."""
+
+    row_nnz: torch.Tensor   # [T] int32
+    row_slot: torch.Tensor  # [T] int32
+    ell_col: torch.Tensor   # [T][K] int16
+    ell_val: torch.Tensor   # [T][K] dtype
+    ovf_rows: torch.Tensor  # [max_ovf] int32
+    dense: torch.Tensor     # [max_ovf][d_ff] dtype
+    n_ovf: torch.Tensor     # [1] int32
+
+    @property
+    def T(self):
+        return self.row_nnz.shape[0]
+
+    @property
+    def K(self):
+        return self.ell_col.shape[1]
+
+    @property
+    def max_ovf(self):
+        return self.dense.shape[0]
+
+    @property
+    def d_ff(self):
+        return self.dense.shape[1]
+
+    def c(self) -> HybridC:
+        return HybridC(self.T, self.d_ff, self.K, self.max_ovf, _dt(self.ell_val),
+                       self.row_nnz.data_ptr(), self.row_slot.data_ptr(),
+                       self.ell_col.data_ptr(), self.ell_val.data_ptr(),
+                       self.ovf_rows.data_ptr(), self.dense.data_ptr(), self.n_ovf.data_ptr())
+
+
+def empty_twell(T, d_ff, width, dtype, device) -> Twell:
+    nt = d_ff // TILE_C
+    return Twell(torch.empty((T, nt), dtype=torch.int32, device=device),
+                 torch.empty((T, nt, width), dtype=torch.int16, device=device),
+                 torch.empty((T, nt, width), dtype=dtype, device=device))
+
+
+def empty_hybrid(T, d_ff, K, max_ovf, dtype, device) -> Hybrid:
+    return Hybrid(torch.empty(T, dtype=torch.int32, device=device),
+                  torch.empty(T, dtype=torch.int32, device=device),
+                  torch.empty((T, K), dtype=torch.int16, device=device),
+                  torch.empty((T, K), dtype=dtype, device=device),
+                  torch.empty(max_ovf, dtype=torch.int32, device=device),
+                  torch.empty((max_ovf, d_ff), dtype=dtype, device=device),
+                  torch.zeros(1, dtype=torch.int32, device=device))
+
+
+def gate_pack(x, wg_t, width=TILE_C, out: Twell | None = None, status=None) -> Twell:
+    T, dm = x.shape
+    if out is None:
+        out = empty_twell(T, wg_t.shape[0], width, x.dtype, x.device)
+    c = out.c()
+    _check(load().twell_gate_pack(_dt(x), _ptr(x), _ptr(wg_t), T, dm, ctypes.byref(c),
+                                  _ptr(status), _stream(x.device)), "twell_gate_pack")
+    return out
+
+
+def fwd_workspace_bytes(dtype, T, d_model, d_ff, width) -> int:
+    return int(load().twell_fwd_workspace_bytes(dtype, T, d_model, d_ff, width))
+
+
+def ffn_fwd(x, tw: Twell, wu_t, wd, y=None, workspace=None, status=None):
+    T, dm = x.shape
+    if y is None:
+        y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
+    need = fwd_workspace_bytes(_dt(x), T, dm, tw.d_ff, tw.width)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel()
+    c = tw.c()
+    _check(load().twell_ffn_fwd(_dt(x), _ptr(x), ctypes.byref(c), _ptr(wu_t), _ptr(wd), dm,
+                                _ptr(y), _ptr(workspace), nbytes, _ptr(status),
+                                _stream(x.device)), "twell_ffn_fwd")
+    return y
+
+
+def to_hybrid(tw: Twell, K, max_ovf, out: Hybrid | None = None, status=None) -> Hybrid:
+    if out is None:
+        out = empty_hybrid(tw.T, tw.d_ff, K, max_ovf, tw.val.dtype, tw.val.device)
+    ct, ch = tw.c(), out.c()
+    _check(load().twell_to_hybrid(ctypes.byref(ct), ctypes.byref(ch), _ptr(status),
+                                  _stream(tw.val.device)), "twell_to_hybrid")
+    return out
+
+
+def bwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf) -> int:
+    return int(load().hybrid_bwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf))
+
+
+def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=None):
+    """Returns (dx, dwg_t, dwu_t, dwd), all float32."""
+    T, dm = x.shape
+    d_ff = wg_t.shape[0]
+    if out is None:
+        f = dict(dtype=torch.float32, device=x.device)
+        out = (torch.empty((T, dm), **f), torch.empty((d_ff, dm), **f),
+               torch.empty((d_ff, dm), **f), torch.empty((d_ff, dm), **f))
+    need = bwd_workspace_bytes(_dt(x), T, dm, d_ff, hy.K, hy.max_ovf)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel()
+    ch = hy.c()
+    dx, dwg, dwu, dwd = out
+    _check(load().hybrid_ffn_bwd(_dt(x), _ptr(x), _ptr(dy), ctypes.byref(ch), _ptr(wg_t),
+                                 _ptr(wu_t), _ptr(wd), dm, _ptr(dx), _ptr(dwg), _ptr(dwu),
+                                 _ptr(dwd), _ptr(workspace), nbytes, _ptr(status),
+                                 _stream(x.device)), "hybrid_ffn_bwd")
+    return out

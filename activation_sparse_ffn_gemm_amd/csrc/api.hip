@@ -1,0 +1,182 @@
+// C-ABI entry points: argument validation, then launches on the caller's
+// stream. Nothing here allocates, synchronises or keeps state.
+#include "common.hpp"
+
+hipError_t launch_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int T, int dm,
+                            const twell_t *o, int32_t *status, hipStream_t s);
+hipError_t launch_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
+                          const void *wd, int dm, float *y, int32_t *status, hipStream_t s);
+hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status, hipStream_t s);
+hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
+                      const void *wg_t, const void *wu_t, const void *wd, int dm, float *dx,
+                      float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
+                      hipStream_t s);
+size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *offsets);
+
+namespace {
+
+bool a16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dtype_ok(int dt) { return dt == TWELL_BF16 || dt == TWELL_F32; }
+
+int check_dm(twell_dtype dt, int32_t dm)
+{
+    const int max_dm = dt == TWELL_BF16 ? 4096 : 2048;
+    return (dm >= 64 && dm <= max_dm && dm % 64 == 0) ? TWELL_OK : TWELL_E_SHAPE;
+}
+
+int check_dff(int32_t dff)
+{
+    return (dff >= TWELL_TILE_C && dff <= 32768 && dff % TWELL_TILE_C == 0) ? TWELL_OK
+                                                                              : TWELL_E_SHAPE;
+}
+
+int check_twell(const twell_t *h, twell_dtype dt)
+{
+    if (!h)
+        return TWELL_E_NULL;
+    if (!dtype_ok(h->dtype) || h->dtype != dt)
+        return TWELL_E_DTYPE;
+    if (h->T < 0 || h->width < 1 || h->width > TWELL_TILE_C)
+        return TWELL_E_SHAPE;
+    if (int rc = check_dff(h->d_ff))
+        return rc;
+    if (h->T > 0 && (!h->count || !h->col || !h->val))
+        return TWELL_E_NULL;
+    return TWELL_OK;
+}
+
+int check_hybrid(const hybrid_t *h, twell_dtype dt)
+{
+    if (!h)
+        return TWELL_E_NULL;
+    if (!dtype_ok(h->dtype) || h->dtype != dt)
+        return TWELL_E_DTYPE;
+    if (h->T < 0 || h->K < 1 || h->K > h->d_ff || h->K > 32767 || h->max_ovf < 0)
+        return TWELL_E_SHAPE;
+    if (int rc = check_dff(h->d_ff))
+        return rc;
+    if (!h->n_ovf)
+        return TWELL_E_NULL;
+    if (h->T > 0 && (!h->row_nnz || !h->row_slot || !h->ell_col || !h->ell_val))
+        return TWELL_E_NULL;
+    if (h->max_ovf > 0 && (!h->ovf_rows || !h->dense))
+        return TWELL_E_NULL;
+    return TWELL_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_E_HIP; }
+
+} // namespace
+
+extern "C" {
+
+const char *twell_status_str(int code)
+{
+    switch (code) {
+    case TWELL_OK: return "ok";
+    case TWELL_E_NULL: return "a required pointer is NULL";
+    case TWELL_E_SHAPE: return "a size is out of range or inconsistent";
+    case TWELL_E_DTYPE: return "unsupported or mismatched element type";
+    case TWELL_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case TWELL_E_WORKSPACE: return "workspace too small";
+    case TWELL_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, int32_t d_model,
+                    const twell_t *out, int32_t *dev_status, void *stream)
+{
+    if (!dtype_ok(dt))
+        return TWELL_E_DTYPE;
+    if ((!x && T != 0) || !wg_t || !out)
+        return TWELL_E_NULL;
+    if (int rc = check_twell(out, dt))
+        return rc;
+    if (int rc = check_dm(dt, d_model))
+        return rc;
+    if (T < 0 || out->T != T)
+        return TWELL_E_SHAPE;
+    if (!a16(x) || !a16(wg_t))
+        return TWELL_E_ALIGN;
+    if (T == 0)
+        return TWELL_OK;
+    return hip_rc(launch_gate_pack(dt, x, wg_t, T, d_model, out, dev_status, (hipStream_t)stream));
+}
+
+size_t twell_fwd_workspace_bytes(twell_dtype, int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
+                  const void *wd, int32_t d_model, float *y, void *workspace,
+                  size_t workspace_bytes, int32_t *dev_status, void *stream)
+{
+    (void)workspace;
+    if (!dtype_ok(dt))
+        return TWELL_E_DTYPE;
+    if (!h || !wu_t || !wd)
+        return TWELL_E_NULL;
+    if (int rc = check_twell(h, dt))
+        return rc;
+    if (h->T > 0 && (!x || !y))
+        return TWELL_E_NULL;
+    if (int rc = check_dm(dt, d_model))
+        return rc;
+    if (!a16(x) || !a16(wu_t) || !a16(wd) || !a16(y))
+        return TWELL_E_ALIGN;
+    if (workspace_bytes < twell_fwd_workspace_bytes(dt, h->T, d_model, h->d_ff, h->width))
+        return TWELL_E_WORKSPACE;
+    if (h->T == 0)
+        return TWELL_OK;
+    return hip_rc(launch_ffn_fwd(dt, x, h, wu_t, wd, d_model, y, dev_status, (hipStream_t)stream));
+}
+
+int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status, void *stream)
+{
+    if (!h || !out)
+        return TWELL_E_NULL;
+    if (!dtype_ok(h->dtype))
+        return TWELL_E_DTYPE;
+    if (int rc = check_twell(h, h->dtype))
+        return rc;
+    if (int rc = check_hybrid(out, h->dtype))
+        return rc;
+    if (out->T != h->T || out->d_ff != h->d_ff)
+        return TWELL_E_SHAPE;
+    return hip_rc(launch_to_hybrid(h, out, dev_status, (hipStream_t)stream));
+}
+
+size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                  int32_t K, int32_t max_ovf)
+{
+    if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
+        return 0;
+    return bwd_workspace_layout(T, d_model, d_ff, K, max_ovf, nullptr);
+}
+
+int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
+                   const void *wg_t, const void *wu_t, const void *wd, int32_t d_model,
+                   float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
+                   size_t workspace_bytes, int32_t *dev_status, void *stream)
+{
+    if (!dtype_ok(dt))
+        return TWELL_E_DTYPE;
+    if (!h || !wg_t || !wu_t || !wd || !dwg_t || !dwu_t || !dwd)
+        return TWELL_E_NULL;
+    if (int rc = check_hybrid(h, dt))
+        return rc;
+    if (h->T > 0 && (!x || !dy || !dx))
+        return TWELL_E_NULL;
+    if (int rc = check_dm(dt, d_model))
+        return rc;
+    if (!a16(x) || !a16(dy) || !a16(wg_t) || !a16(wu_t) || !a16(wd) || !a16(dx) || !a16(dwg_t) ||
+        !a16(dwu_t) || !a16(dwd) || !a16(workspace))
+        return TWELL_E_ALIGN;
+    const size_t need = hybrid_bwd_workspace_bytes(dt, h->T, d_model, h->d_ff, h->K, h->max_ovf);
+    if (workspace_bytes < need || (need && !workspace))
+        return TWELL_E_WORKSPACE;
+    return hip_rc(launch_bwd(dt, x, dy, h, wg_t, wu_t, wd, d_model, dx, dwg_t, dwu_t, dwd,
+                             workspace, dev_status, (hipStream_t)stream));
+}
+
+} // extern "C"

@@ -1,0 +1,192 @@
+/*
+ * twell.h -- C-ABI of the activation-sparse ReLU-gated FFN on MI355X (gfx950).
+ *
+ * The layer is y = (h_g (.) x W_u) W_d with h_g = ReLU(x W_g), whose gate
+ * activations are almost all exact zeros. The method is the one of "Sparser,
+ * Faster, Lighter Transformer Language Models" (Cetin, Peluchetti, Castillo,
+ * Naruse, Murakami, Jones), summarised on gist.science/it/paper/2603.23198:
+ *   section 2.B.1  TwELL (Tile-wise ELLPACK), written by the gate matmul's
+ *                  epilogue                                -> twell_gate_pack
+ *   section 2.B.2  one fused stage applying the up and down projections to
+ *                  the TwELL nonzeros only                  -> twell_ffn_fwd
+ *   section 2.B.3  TwELL -> hybrid (ELL rows + dense backup) conversion and
+ *                  the sparse<->dense products of the backward
+ *                                                   -> twell_to_hybrid,
+ *                                                      hybrid_ffn_bwd
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer unless marked (host). The caller owns
+ *     all memory, including workspaces; the library allocates nothing, frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return without synchronising.
+ *   - No global state: concurrent calls on different streams are safe as long
+ *     as their output buffers do not overlap.
+ *   - The return value is a host-side status: TWELL_OK, or a negative
+ *     TWELL_E_* code when an argument is rejected before anything is launched
+ *     (or TWELL_E_HIP if a launch failed). No exception crosses the ABI.
+ *   - Data-dependent conditions found on the device are OR-ed as
+ *     TWELL_DEV_* bits into the int32 at `dev_status` (may be NULL); the call
+ *     does not fail for them. The caller zeroes the word and reads it when it
+ *     likes.
+ *   - Row-major storage. x, dy: [T][d_model]. Weights, one contiguous d_model
+ *     vector per neuron: wg_t, wu_t, wd: [d_ff][d_model], where row i of wg_t
+ *     (wu_t) is column i of W_g (W_u) and row i of wd is row i of W_d.
+ *   - Element types: TWELL_BF16 (bfloat16 storage, float32 accumulation) or
+ *     TWELL_F32. y, dx and every weight gradient are float32.
+ *   - Limits: d_model % 64 == 0 and 64 <= d_model <= 4096 (2048 for F32);
+ *     d_ff % 128 == 0 and d_ff <= 32768; T >= 0. With T == 0 the token
+ *     arrays (x, dy, y, dx) may be NULL; the forward calls do nothing and the
+ *     backward writes zero weight gradients.
+ *     x, dy, weights, y, dx and gradients must be 16-byte aligned.
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+
+enum {
+    TWELL_OK = 0,
+    TWELL_E_NULL = -1,      /* a required pointer is NULL */
+    TWELL_E_SHAPE = -2,     /* a size is out of range or inconsistent */
+    TWELL_E_DTYPE = -3,     /* unsupported element type */
+    TWELL_E_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+    TWELL_E_WORKSPACE = -5, /* workspace smaller than the *_workspace_bytes figure */
+    TWELL_E_HIP = -6        /* the HIP runtime rejected a launch */
+};
+
+/* device status bits */
+enum {
+    TWELL_DEV_TILE_OVERFLOW = 1, /* a (row, tile) held more than `width` nonzeros */
+    TWELL_DEV_OVF_CAPACITY = 2,  /* more overflow rows than the backup's max_ovf */
+    TWELL_DEV_BAD_INDEX = 4      /* a stored column was outside [0, d_ff); entry skipped */
+};
+
+#define TWELL_TILE_C 128 /* columns per TwELL tile: the gate kernel's N tile */
+
+/*
+ * TwELL of h = ReLU(x W_g) (section 2.B.1 of the summary page: the columns
+ * are cut into tiles and each tile of each row keeps a count, the column
+ * indices and the values of its nonzeros).
+ *   count [T][d_ff/128] int32: number of g > 0 in the tile (the TRUE count,
+ *                              which may exceed width; then the first `width`
+ *                              entries are kept and TILE_OVERFLOW is raised)
+ *   col   [T][d_ff/128][width] int16: global column in [0, d_ff), ascending
+ *                              within the tile; slots >= count are untouched
+ *   val   [T][d_ff/128][width] dtype: h = g rounded to nearest even
+ * width in [1, 128]; 128 is lossless.
+ */
+typedef struct {
+    int32_t T, d_ff, width;
+    twell_dtype dtype;
+    int32_t *count;
+    int16_t *col;
+    void *val;
+} twell_t;
+
+/*
+ * Hybrid ELL + dense backup (section 2.B.3 of the summary page: rows with few
+ * nonzeros in a compact ELL matrix, overflow rows redirected to a dense
+ * backup). A row with row_nnz <= K is an ELL row; any other row is an
+ * overflow row and goes whole to the backup.
+ *   row_nnz  [T] int32: stored entries of the row (sum over tiles of
+ *                       min(count, width))
+ *   row_slot [T] int32: -1 for an ELL row, else the row's backup slot; slots
+ *                       are given in ascending row order
+ *   ell_col  [T][K] int16, ell_val [T][K] dtype: the row's entries in
+ *                       ascending column order (ELL rows only; other slots
+ *                       are untouched)
+ *   ovf_rows [max_ovf] int32: row of each backup slot, ascending
+ *   dense    [max_ovf][d_ff] dtype: h at the row's columns, 0 elsewhere
+ *   n_ovf    int32 (device scalar): TRUE number of overflow rows; if it
+ *            exceeds max_ovf, OVF_CAPACITY is raised and rows past the
+ *            capacity are not stored (the backward is then undefined)
+ */
+typedef struct {
+    int32_t T, d_ff, K, max_ovf;
+    twell_dtype dtype;
+    int32_t *row_nnz;
+    int32_t *row_slot;
+    int16_t *ell_col;
+    void *ell_val;
+    int32_t *ovf_rows;
+    void *dense;
+    int32_t *n_ovf;
+} hybrid_t;
+
+/*
+ * Gate matmul g = x W_g with the TwELL packing of h = ReLU(g) done in the
+ * matmul's epilogue (section 2.B.1 of the summary page; the dothoosh.com
+ * article: the conversion moved into the kernel's epilogue, tiles matched to
+ * the matmul tile). g is never written to memory.
+ *   x [T][d_model], wg_t [d_ff][d_model] (dtype dt); out (host struct with
+ *   device arrays) sized as documented at twell_t, out->T == T,
+ *   out->dtype == dt. Every count of every row < T is written.
+ * Errors: NULL / SHAPE / DTYPE / ALIGN / HIP.
+ */
+int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, int32_t d_model,
+                    const twell_t *out, int32_t *dev_status, void *stream);
+
+/*
+ * Fused up and down projections over the TwELL nonzeros (section 2.B.2 of the
+ * summary page): y[t] = sum over stored (i, h) of row t of
+ * h * (x[t] . wu_t[i]) * wd[i], float32 accumulation. y [T][d_model] float32
+ * is overwritten. workspace: at least twell_fwd_workspace_bytes(...) bytes
+ * (may be NULL when that is 0).
+ * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
+ */
+int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
+                  const void *wd, int32_t d_model, float *y, void *workspace,
+                  size_t workspace_bytes, int32_t *dev_status, void *stream);
+
+size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                 int32_t width);
+
+/*
+ * TwELL -> hybrid conversion (section 2.B.3 of the summary page: a dedicated
+ * conversion kernel). h and out must agree on T, d_ff and dtype;
+ * 1 <= K <= d_ff; max_ovf >= 0. Writes every row_nnz, row_slot and n_ovf,
+ * the ELL rows of ELL rows and the backup rows of the first max_ovf overflow
+ * rows (whole rows, zeros included).
+ * Errors: NULL / SHAPE / DTYPE / HIP.
+ */
+int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status, void *stream);
+
+/*
+ * Backward of y = (h (.) x W_u) W_d on the pattern P held by a hybrid
+ * (section 2.B.3 of the summary page: sparse-to-dense and dense-to-sparse
+ * products, no dense work on zeros). An entry is in P iff it is stored with a
+ * nonzero value; ReLU' = 1 on P. With u = x W_u and da = dy W_d^T sampled on
+ * P, a = h u, du = da h and dg = da u:
+ *   dx = du W_u^T + dg W_g^T,  dW_d = a^T dy,  dW_u = x^T du,  dW_g = x^T dg.
+ * ELL rows use gathers; backup rows use dense MFMA products.
+ *   dy [T][d_model] dtype dt; dx [T][d_model] float32; dwg_t, dwu_t, dwd
+ *   [d_ff][d_model] float32 (storage layouts: dwg_t = dW_g^T, dwu_t = dW_u^T,
+ *   dwd = dW_d); all overwritten. workspace: at least
+ *   hybrid_bwd_workspace_bytes(...) bytes.
+ * Undefined if the hybrid's OVF_CAPACITY bit was raised.
+ * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
+ */
+int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
+                   const void *wg_t, const void *wu_t, const void *wd, int32_t d_model,
+                   float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
+                   size_t workspace_bytes, int32_t *dev_status, void *stream);
+
+size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                  int32_t K, int32_t max_ovf);
+
+/* Static text for a TWELL_* status code (host). */
+const char *twell_status_str(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */

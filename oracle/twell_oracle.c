@@ -317,21 +317,27 @@ int orc_bwd_hybrid(const double *x, const double *dy, int T, int dm, int dff,
         free(sg);
     }
 
-    /* weight gradients: sums over tokens in ascending t; threads split columns */
-#pragma omp parallel for schedule(static)
-    for (int k = 0; k < dm; ++k) {
-        for (int i = 0; i < dff; ++i) {
-            dwd[(i64)i * dm + k] = 0.0;
-            dwu_t[(i64)i * dm + k] = 0.0;
-            dwg_t[(i64)i * dm + k] = 0.0;
-        }
+    /* weight gradients: every dW[i][k] sums its terms in ascending t; threads
+     * split the model columns k into independent blocks of 64 */
+    int nkb = (dm + 63) / 64;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int kb = 0; kb < nkb; ++kb) {
+        int k0 = kb * 64, k1 = k0 + 64 < dm ? k0 + 64 : dm;
+        for (int i = 0; i < dff; ++i)
+            for (int k = k0; k < k1; ++k) {
+                dwd[(i64)i * dm + k] = 0.0;
+                dwu_t[(i64)i * dm + k] = 0.0;
+                dwg_t[(i64)i * dm + k] = 0.0;
+            }
         for (int t = 0; t < T; ++t) {
-            double xk = x[(i64)t * dm + k], dyk = dy[(i64)t * dm + k];
+            const double *xt = x + (i64)t * dm, *dyt = dy + (i64)t * dm;
             for (i64 e = r.off[t]; e < r.off[t + 1]; ++e) {
-                i64 o = (i64)r.col[e] * dm + k;
-                dwd[o] += ca[e] * dyk;
-                dwu_t[o] += cdu[e] * xk;
-                dwg_t[o] += cdg[e] * xk;
+                i64 o = (i64)r.col[e] * dm;
+                for (int k = k0; k < k1; ++k) {
+                    dwd[o + k] += ca[e] * dyt[k];
+                    dwu_t[o + k] += cdu[e] * xt[k];
+                    dwg_t[o + k] += cdg[e] * xt[k];
+                }
             }
         }
     }

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/twell.h declares, and rejects bad arguments on the host before any
+launch (the error paths return before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_sparse_ffn_gemm_amd import _lib as tw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twell.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return tw.load()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(tw.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.twell_status_str(code)
+    assert L.twell_status_str(99) == b"unknown status"
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced (the calls fail validation first)
+
+
+def twell_c(T=4, d_ff=256, width=128, dtype=tw.TWELL_BF16, ptr=FAKE):
+    return tw.TwellC(T, d_ff, width, dtype, ptr, ptr, ptr)
+
+
+def hybrid_c(T=4, d_ff=256, K=16, max_ovf=4, dtype=tw.TWELL_BF16, ptr=FAKE):
+    return tw.HybridC(T, d_ff, K, max_ovf, dtype, *([ptr] * 7))
+
+
+def gate(L, dt=tw.TWELL_BF16, x=FAKE, w=FAKE, T=4, dm=64, out=None):
+    out = out or twell_c(T=T)
+    return L.twell_gate_pack(dt, x, w, T, dm, ctypes.byref(out), None, None)
+
+
+def test_gate_pack_validation(L):
+    assert gate(L, dt=7) == -3
+    assert gate(L, x=0) == -1
+    assert gate(L, out=twell_c(dtype=tw.TWELL_F32)) == -3       # dtype mismatch
+    assert gate(L, dm=96) == -2                                   # d_model % 64
+    assert gate(L, dm=8192) == -2                                 # d_model too large
+    assert gate(L, dt=tw.TWELL_F32, dm=4096,
+                out=twell_c(dtype=tw.TWELL_F32)) == -2            # fp32 limit 2048
+    assert gate(L, out=twell_c(d_ff=200)) == -2                   # d_ff % 128
+    assert gate(L, out=twell_c(d_ff=65536)) == -2                 # int16 columns
+    assert gate(L, out=twell_c(width=0)) == -2
+    assert gate(L, out=twell_c(width=129)) == -2
+    assert gate(L, T=5, out=twell_c(T=4)) == -2                   # T mismatch
+    assert gate(L, x=FAKE + 2) == -4                              # misaligned
+    assert gate(L, out=twell_c(ptr=0)) == -1                      # NULL arrays
+    assert gate(L, T=0, out=twell_c(T=0, ptr=0)) == 0             # T == 0: no-op
+
+
+def test_ffn_fwd_validation(L):
+    t = twell_c()
+    f = lambda **k: L.twell_ffn_fwd(k.get("dt", tw.TWELL_BF16), k.get("x", FAKE),
+                                    ctypes.byref(k.get("t", t)), FAKE, FAKE, k.get("dm", 64),
+                                    k.get("y", FAKE), None, 0, None, None)
+    assert f(dt=9) == -3
+    assert f(y=0) == -1
+    assert f(dm=100) == -2
+    assert f(y=FAKE + 4) == -4
+    assert f(t=twell_c(dtype=tw.TWELL_F32)) == -3
+    assert f(t=twell_c(T=0, ptr=0)) == 0
+
+
+def test_to_hybrid_validation(L):
+    f = lambda t, h: L.twell_to_hybrid(ctypes.byref(t), ctypes.byref(h), None, None)
+    assert f(twell_c(), hybrid_c(T=5)) == -2            # T mismatch
+    assert f(twell_c(), hybrid_c(K=0)) == -2
+    assert f(twell_c(), hybrid_c(K=300)) == -2          # K > d_ff
+    assert f(twell_c(), hybrid_c(max_ovf=-1)) == -2
+    assert f(twell_c(), hybrid_c(dtype=tw.TWELL_F32)) == -3
+    assert f(twell_c(), hybrid_c(ptr=0)) == -1
+    assert f(twell_c(d_ff=384), hybrid_c()) == -2       # d_ff mismatch
+
+
+def test_bwd_validation(L):
+    h = hybrid_c()
+    need = L.hybrid_bwd_workspace_bytes(tw.TWELL_BF16, 4, 64, 256, 16, 4)
+    assert need > 0
+
+    def f(ws=FAKE, nbytes=None, dm=64, dx=FAKE, hh=h, dt=tw.TWELL_BF16):
+        return L.hybrid_ffn_bwd(dt, FAKE, FAKE, ctypes.byref(hh), FAKE, FAKE, FAKE, dm, dx,
+                                FAKE, FAKE, FAKE, ws, need if nbytes is None else nbytes,
+                                None, None)
+    assert f(nbytes=need - 1) == -5
+    assert f(ws=0) == -5
+    assert f(dx=0) == -1
+    assert f(dm=32) == -2
+    assert f(dx=FAKE + 8) == -4
+    assert f(dt=tw.TWELL_F32) == -3
+    assert f(hh=hybrid_c(max_ovf=-2)) == -2

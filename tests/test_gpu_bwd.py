@@ -1,0 +1,151 @@
+"""GPU parity of hybrid_ffn_bwd against the oracle's backward, through the C-ABI.
+
+The hybrid fed to the GPU is the oracle's (values rounded to the storage
+dtype), and the oracle's backward runs on exactly those values: inputs flow
+oracle -> GPU only. The ReLU derivative is discontinuous, so the pattern must
+be the same on both sides; the GPU's own pattern is checked in test_gpu_fwd.
+"""
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_ffn_gemm_amd import _lib as tw
+from activation_sparse_ffn_gemm_amd import synth
+from helpers import assert_close, f64, oracle_twell_for_gpu, to_storage
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NAMES = ("dx", "dwg_t", "dwu_t", "dwd")
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def oracle_hybrid(orc, d, dtype, K, max_ovf, rows=None):
+    """Oracle TwELL -> hybrid of inputs d, values rounded to storage dtype."""
+    x = f64(d["x"] if rows is None else d["x"][rows])
+    g = orc.gate(x, f64(d["wg_t"]))
+    tw_r, _ = oracle_twell_for_gpu(orc, g, 128, dtype, "cpu")
+    return orc.to_hybrid(tw_r, K, max_ovf)
+
+
+def upload_hybrid(ref: dict, dtype: str) -> tw.Hybrid:
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    mo = ref["max_ovf"]
+    return tw.Hybrid(
+        torch.from_numpy(ref["row_nnz"].copy()).to(DEV),
+        torch.from_numpy(ref["row_slot"].copy()).to(DEV),
+        torch.from_numpy(np.maximum(ref["ell_col"], 0).astype(np.int16)).to(DEV),
+        torch.from_numpy(ref["ell_val"]).to(tdt).to(DEV),
+        torch.from_numpy(ref["ovf_rows"][:mo].copy()).to(DEV) if mo else
+        torch.zeros(0, dtype=torch.int32, device=DEV),
+        torch.from_numpy(ref["dense"][:mo]).to(tdt).to(DEV).reshape(mo, ref["d_ff"]),
+        torch.tensor([ref["n_ovf"]], dtype=torch.int32, device=DEV))
+
+
+def run_bwd(d, hy, dtype):
+    x, dy, wg, wu, wd = (d[k].to(DEV) for k in ("x", "dy", "wg_t", "wu_t", "wd"))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = tw.ffn_bwd(x, dy, hy, wg, wu, wd, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return out
+
+
+def oracle_bwd(orc, d, ref):
+    return orc.bwd_hybrid(f64(d["x"]), f64(d["dy"]), ref, f64(d["wg_t"]), f64(d["wu_t"]),
+                          f64(d["wd"]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,dm,dff,K,skew", [(1, 64, 128, 8, 0), (150, 192, 384, 12, 9),
+                                             (300, 512, 1024, 40, 21), (77, 320, 256, 128, 0)])
+def test_bwd_integer_exact(orc, dtype, T, dm, dff, K, skew):
+    """Integer inputs: ELL gathers and the backup rows' hi/lo MFMA products are
+    exact, so every gradient matches the oracle bit for bit."""
+    announce("bwd int", dtype, T, dm, dff, K, skew)
+    d = synth.make_integer_inputs(T, dm, dff, dtype, 0.03, with_dy=True, skew_rows=skew)
+    ref = oracle_hybrid(orc, d, dtype, K, 64)
+    assert (ref["n_ovf"] > 0) == (skew > 0)
+    got = run_bwd(d, upload_hybrid(ref, dtype), dtype)
+    want = oracle_bwd(orc, d, ref)
+    for n, a, b in zip(NAMES, got, want):
+        assert np.array_equal(f64(a), b), n
+
+
+@pytest.mark.parametrize("w", [
+    synth.Workload("small-f32", 96, 256, 512, "f32", 0.03, skew_frac=0.1, skew_density=0.4,
+                   K=40, max_ovf=16),
+    synth.Workload("small-bf16", 200, 384, 640, "bf16", 0.02, skew_frac=0.05, skew_density=0.3,
+                   K=48, max_ovf=16),
+    synth.Workload("all-ell-bf16", 256, 1024, 2816, "bf16", 0.01, K=128, max_ovf=8),
+], ids=lambda w: w.name)
+def test_bwd_gaussian(orc, w):
+    announce("bwd gauss", w.name)
+    d = synth.make_inputs(w, with_dy=True)
+    ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
+    got = run_bwd(d, upload_hybrid(ref, w.dtype), w.dtype)
+    want = oracle_bwd(orc, d, ref)
+    for n, a, b in zip(NAMES, got, want):
+        assert_close(a, b, w.dtype, n)
+
+
+def test_bwd_training_layer_full(orc):
+    """The skewed 1.5B training layer at full size (T = 8192, 410 backup rows):
+    every gradient element against the oracle on the same hybrid."""
+    w = synth.TRAIN_1P5B
+    announce("bwd training layer full")
+    d = synth.make_inputs(w, with_dy=True)
+    ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
+    assert ref["n_ovf"] == 410
+    got = run_bwd(d, upload_hybrid(ref, w.dtype), w.dtype)
+    want = oracle_bwd(orc, d, ref)
+    for n, a, b in zip(NAMES, got, want):
+        assert_close(a, b, w.dtype, n)
+
+
+def test_bwd_deterministic(orc):
+    w = synth.Workload("det", 512, 256, 768, "bf16", 0.02, skew_frac=0.05, skew_density=0.3,
+                       K=40, max_ovf=64)
+    announce("bwd determinism")
+    d = synth.make_inputs(w, with_dy=True)
+    hy = upload_hybrid(oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf), w.dtype)
+    a = run_bwd(d, hy, w.dtype)
+    b = run_bwd(d, hy, w.dtype)
+    for n, p, q in zip(NAMES, a, b):
+        assert torch.equal(p, q), n
+
+
+def test_bwd_empty_and_no_backup(orc):
+    """T == 0 writes zero weight gradients; max_ovf == 0 runs ELL rows only."""
+    announce("bwd empty")
+    d = synth.make_integer_inputs(40, 128, 256, "bf16", 0.03, with_dy=True)
+    wg, wu, wd = (d[k].to(DEV) for k in ("wg_t", "wu_t", "wd"))
+    hy0 = tw.empty_hybrid(0, 256, 16, 0, torch.bfloat16, DEV)
+    f = dict(dtype=torch.float32, device=DEV)
+    out = (torch.empty((0, 128), **f),) + tuple(torch.full((256, 128), 7.0, **f) for _ in range(3))
+    x0 = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    tw.ffn_bwd(x0, x0, hy0, wg, wu, wd, out=out)
+    torch.cuda.synchronize()
+    for o in out[1:]:
+        assert int(torch.count_nonzero(o)) == 0
+    ref = oracle_hybrid(orc, d, "bf16", 128, 0)
+    assert ref["n_ovf"] == 0
+    got = run_bwd(d, upload_hybrid(ref, "bf16"), "bf16")
+    for n, a, b in zip(NAMES, got, oracle_bwd(orc, d, ref)):
+        assert np.array_equal(f64(a), b), n
+
+
+def test_backward_end_to_end_integer(orc):
+    """GPU gate_pack -> to_hybrid -> bwd on integer inputs equals the oracle's
+    backward on its own hybrid (patterns are exact, so they agree)."""
+    announce("bwd e2e int")
+    d = synth.make_integer_inputs(384, 256, 768, "bf16", 0.02, with_dy=True, skew_rows=19)
+    ref = oracle_hybrid(orc, d, "bf16", 48, 32)
+    x, wg = d["x"].to(DEV), d["wg_t"].to(DEV)
+    t = tw.gate_pack(x, wg)
+    hy = tw.to_hybrid(t, 48, 32)
+    got = run_bwd(d, hy, "bf16")
+    for n, a, b in zip(NAMES, got, oracle_bwd(orc, d, ref)):
+        assert np.array_equal(f64(a), b), n

@@ -27,8 +27,8 @@ MUTANTS = {
     "bwd da from up weights": ("double da = dot(dyt, wd + (i64)i * dm, dm);\n                ca[e]",
                                "double da = dot(dyt, wu_t + (i64)i * dm, dm);\n                ca[e]"),
     "bwd dx sign": ("dxt[k] = su[k] + sg[k];", "dxt[k] = su[k] - sg[k];"),
-    "bwd dW_u from dy": ("dwu_t[o] += cdu[e] * xk;", "dwu_t[o] += cdu[e] * dyk;"),
-    "bwd dW_d from x": ("dwd[o] += ca[e] * dyk;", "dwd[o] += ca[e] * xk;"),
+    "bwd dW_u from dy": ("dwu_t[o + k] += cdu[e] * xt[k];", "dwu_t[o + k] += cdu[e] * dyt[k];"),
+    "bwd dW_d from x": ("dwd[o + k] += ca[e] * dyt[k];", "dwd[o + k] += ca[e] * xt[k];"),
     "bwd drops dg term of dx": ("sg[k] += cdg[e] * wgi[k];", "sg[k] += 0.0 * wgi[k];"),
 }
 
