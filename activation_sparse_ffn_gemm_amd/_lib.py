@@ -32,6 +32,46 @@ class TwellC(ctypes.Structure):
                 ("count", c_p), ("col", c_p), ("val", c_p)]
 
 
+TIMING_MAX = 24
+
+
+class TimingC(ctypes.Structure):
+    _fields_ = [("events", c_p * (TIMING_MAX + 1)), ("n_events", c_i32), ("n_used", c_i32),
+                ("names", ctypes.c_char_p * TIMING_MAX)]
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of library calls on the current stream.
+
+    ``timer.arg()`` gives the struct to pass to one call; after the stream is
+    synchronised, ``timer.collect()`` returns [(kernel name, ms), ...] of the
+    last call and ``timer.add(totals)`` accumulates them into a dict.
+    """
+
+    def __init__(self):
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(TIMING_MAX + 1)]
+        for e in self.ev:  # materialise the underlying events
+            e.record()
+        torch.cuda.synchronize()
+        self.c = TimingC()
+        for k, e in enumerate(self.ev):
+            self.c.events[k] = e.cuda_event
+        self.c.n_events = TIMING_MAX + 1
+
+    def arg(self):
+        return ctypes.byref(self.c)
+
+    def collect(self):
+        out = []
+        for k in range(self.c.n_used - 1):
+            out.append((self.c.names[k].decode(), self.ev[k].elapsed_time(self.ev[k + 1])))
+        return out
+
+    def add(self, totals: dict):
+        for name, ms in self.collect():
+            totals[name] = totals.get(name, 0.0) + ms
+
+
 class HybridC(ctypes.Structure):
     _fields_ = [("T", c_i32), ("d_ff", c_i32), ("K", c_i32), ("max_ovf", c_i32),
                 ("dtype", ctypes.c_int), ("row_nnz", c_p), ("row_slot", c_p), ("ell_col", c_p),
@@ -55,13 +95,14 @@ def load() -> ctypes.CDLL:
                          "(the HIP library is the only implementation; there is no fallback)")
     L = ctypes.CDLL(LIB_PATH)
     P, I, S = c_p, c_i32, c_sz
-    L.twell_gate_pack.argtypes = [ctypes.c_int, P, P, I, I, ctypes.POINTER(TwellC), P, P]
-    L.twell_ffn_fwd.argtypes = [ctypes.c_int, P, ctypes.POINTER(TwellC), P, P, I, P, P, S, P, P]
+    L.twell_gate_pack.argtypes = [ctypes.c_int, P, P, I, I, ctypes.POINTER(TwellC), P, P, P]
+    L.twell_ffn_fwd.argtypes = [ctypes.c_int, P, ctypes.POINTER(TwellC), P, P, I, P, P, S, P, P,
+                                P]
     L.twell_fwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I]
     L.twell_fwd_workspace_bytes.restype = S
-    L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P]
+    L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P, P]
     L.hybrid_ffn_bwd.argtypes = [ctypes.c_int, P, P, ctypes.POINTER(HybridC), P, P, P, I,
-                                 P, P, P, P, P, S, P, P]
+                                 P, P, P, P, P, S, P, P, P]
     L.hybrid_bwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I, I]
     L.hybrid_bwd_workspace_bytes.restype = S
     L.twell_status_str.argtypes = [ctypes.c_int]
@@ -170,13 +211,19 @@ def empty_hybrid(T, d_ff, K, max_ovf, dtype, device) -> Hybrid:
                   torch.zeros(1, dtype=torch.int32, device=device))
 
 
-def gate_pack(x, wg_t, width=TILE_C, out: Twell | None = None, status=None) -> Twell:
+def _timing(t):
+    return None if t is None else t.arg()
+
+
+def gate_pack(x, wg_t, width=TILE_C, out: Twell | None = None, status=None,
+              timing: KernelTimer | None = None) -> Twell:
     T, dm = x.shape
     if out is None:
         out = empty_twell(T, wg_t.shape[0], width, x.dtype, x.device)
     c = out.c()
     _check(load().twell_gate_pack(_dt(x), _ptr(x), _ptr(wg_t), T, dm, ctypes.byref(c),
-                                  _ptr(status), _stream(x.device)), "twell_gate_pack")
+                                  _ptr(status), _timing(timing), _stream(x.device)),
+           "twell_gate_pack")
     return out
 
 
@@ -184,7 +231,8 @@ def fwd_workspace_bytes(dtype, T, d_model, d_ff, width) -> int:
     return int(load().twell_fwd_workspace_bytes(dtype, T, d_model, d_ff, width))
 
 
-def ffn_fwd(x, tw: Twell, wu_t, wd, y=None, workspace=None, status=None):
+def ffn_fwd(x, tw: Twell, wu_t, wd, y=None, workspace=None, status=None,
+            timing: KernelTimer | None = None):
     T, dm = x.shape
     if y is None:
         y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
@@ -195,16 +243,17 @@ def ffn_fwd(x, tw: Twell, wu_t, wd, y=None, workspace=None, status=None):
     c = tw.c()
     _check(load().twell_ffn_fwd(_dt(x), _ptr(x), ctypes.byref(c), _ptr(wu_t), _ptr(wd), dm,
                                 _ptr(y), _ptr(workspace), nbytes, _ptr(status),
-                                _stream(x.device)), "twell_ffn_fwd")
+                                _timing(timing), _stream(x.device)), "twell_ffn_fwd")
     return y
 
 
-def to_hybrid(tw: Twell, K, max_ovf, out: Hybrid | None = None, status=None) -> Hybrid:
+def to_hybrid(tw: Twell, K, max_ovf, out: Hybrid | None = None, status=None,
+              timing: KernelTimer | None = None) -> Hybrid:
     if out is None:
         out = empty_hybrid(tw.T, tw.d_ff, K, max_ovf, tw.val.dtype, tw.val.device)
     ct, ch = tw.c(), out.c()
     _check(load().twell_to_hybrid(ctypes.byref(ct), ctypes.byref(ch), _ptr(status),
-                                  _stream(tw.val.device)), "twell_to_hybrid")
+                                  _timing(timing), _stream(tw.val.device)), "twell_to_hybrid")
     return out
 
 
@@ -212,7 +261,8 @@ def bwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf) -> int:
     return int(load().hybrid_bwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf))
 
 
-def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=None):
+def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=None,
+            timing: KernelTimer | None = None):
     """Returns (dx, dwg_t, dwu_t, dwd), all float32."""
     T, dm = x.shape
     d_ff = wg_t.shape[0]
@@ -229,5 +279,5 @@ def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=
     _check(load().hybrid_ffn_bwd(_dt(x), _ptr(x), _ptr(dy), ctypes.byref(ch), _ptr(wg_t),
                                  _ptr(wu_t), _ptr(wd), dm, _ptr(dx), _ptr(dwg), _ptr(dwu),
                                  _ptr(dwd), _ptr(workspace), nbytes, _ptr(status),
-                                 _stream(x.device)), "hybrid_ffn_bwd")
+                                 _timing(timing), _stream(x.device)), "hybrid_ffn_bwd")
     return out

@@ -3,14 +3,18 @@
 #include "common.hpp"
 
 hipError_t launch_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int T, int dm,
-                            const twell_t *o, int32_t *status, hipStream_t s);
+                            const twell_t *o, int32_t *status, twell_timing_t *timing,
+                            hipStream_t s);
 hipError_t launch_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
-                          const void *wd, int dm, float *y, int32_t *status, hipStream_t s);
-hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status, hipStream_t s);
+                          const void *wd, int dm, float *y, void *ws, int32_t *status,
+                          twell_timing_t *timing, hipStream_t s);
+size_t fwd_workspace(int T, int dff, int W);
+hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status,
+                            twell_timing_t *timing, hipStream_t s);
 hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
                       const void *wg_t, const void *wu_t, const void *wd, int dm, float *dx,
                       float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
-                      hipStream_t s);
+                      twell_timing_t *timing, hipStream_t s);
 size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *offsets);
 
 namespace {
@@ -86,7 +90,8 @@ const char *twell_status_str(int code)
 }
 
 int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, int32_t d_model,
-                    const twell_t *out, int32_t *dev_status, void *stream)
+                    const twell_t *out, int32_t *dev_status, twell_timing_t *timing,
+                    void *stream)
 {
     if (!dtype_ok(dt))
         return TWELL_E_DTYPE;
@@ -102,16 +107,24 @@ int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, 
         return TWELL_E_ALIGN;
     if (T == 0)
         return TWELL_OK;
-    return hip_rc(launch_gate_pack(dt, x, wg_t, T, d_model, out, dev_status, (hipStream_t)stream));
+    return hip_rc(launch_gate_pack(dt, x, wg_t, T, d_model, out, dev_status, timing,
+                                   (hipStream_t)stream));
 }
 
-size_t twell_fwd_workspace_bytes(twell_dtype, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                 int32_t width)
+{
+    (void)d_model;
+    if (!dtype_ok(dt) || T < 0 || d_ff < TWELL_TILE_C || width < 1)
+        return 0;
+    return fwd_workspace(T, d_ff, width);
+}
 
 int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
                   const void *wd, int32_t d_model, float *y, void *workspace,
-                  size_t workspace_bytes, int32_t *dev_status, void *stream)
+                  size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
+                  void *stream)
 {
-    (void)workspace;
     if (!dtype_ok(dt))
         return TWELL_E_DTYPE;
     if (!h || !wu_t || !wd)
@@ -124,14 +137,19 @@ int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *w
         return rc;
     if (!a16(x) || !a16(wu_t) || !a16(wd) || !a16(y))
         return TWELL_E_ALIGN;
-    if (workspace_bytes < twell_fwd_workspace_bytes(dt, h->T, d_model, h->d_ff, h->width))
+    const size_t need = twell_fwd_workspace_bytes(dt, h->T, d_model, h->d_ff, h->width);
+    if (workspace_bytes < need || (need && !workspace))
         return TWELL_E_WORKSPACE;
+    if (!a16(workspace))
+        return TWELL_E_ALIGN;
     if (h->T == 0)
         return TWELL_OK;
-    return hip_rc(launch_ffn_fwd(dt, x, h, wu_t, wd, d_model, y, dev_status, (hipStream_t)stream));
+    return hip_rc(launch_ffn_fwd(dt, x, h, wu_t, wd, d_model, y, workspace, dev_status, timing,
+                                 (hipStream_t)stream));
 }
 
-int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status, void *stream)
+int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
+                    twell_timing_t *timing, void *stream)
 {
     if (!h || !out)
         return TWELL_E_NULL;
@@ -143,7 +161,7 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status, 
         return rc;
     if (out->T != h->T || out->d_ff != h->d_ff)
         return TWELL_E_SHAPE;
-    return hip_rc(launch_to_hybrid(h, out, dev_status, (hipStream_t)stream));
+    return hip_rc(launch_to_hybrid(h, out, dev_status, timing, (hipStream_t)stream));
 }
 
 size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
@@ -157,7 +175,8 @@ size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, in
 int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
                    const void *wg_t, const void *wu_t, const void *wd, int32_t d_model,
                    float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
-                   size_t workspace_bytes, int32_t *dev_status, void *stream)
+                   size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
+                   void *stream)
 {
     if (!dtype_ok(dt))
         return TWELL_E_DTYPE;
@@ -176,7 +195,7 @@ int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t
     if (workspace_bytes < need || (need && !workspace))
         return TWELL_E_WORKSPACE;
     return hip_rc(launch_bwd(dt, x, dy, h, wg_t, wu_t, wd, d_model, dx, dwg_t, dwu_t, dwd,
-                             workspace, dev_status, (hipStream_t)stream));
+                             workspace, dev_status, timing, (hipStream_t)stream));
 }
 
 } // extern "C"

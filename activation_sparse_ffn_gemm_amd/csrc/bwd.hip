@@ -6,46 +6,55 @@
 // With u = x W_u and da = dy W_d^T sampled on P, a = h u, du = da h, dg = da u:
 //   dx = du W_u^T + dg W_g^T,  dW_d = a^T dy,  dW_u = x^T du,  dW_g = x^T dg.
 //
-// ELL rows (gathers, fp32 accumulation):
-//   1. token pass: one wave per ELL row computes u and da for each entry
-//      (dense-to-sparse dots with the entry's wu_t and wd rows), keeps the
-//      entry's (a, du, dg) and accumulates dx[t] from the entry's wu_t and
-//      wg_t rows (sparse-to-dense);
-//   2. a stable column transpose of the ELL entries (per-block histograms,
-//      a scan, and an in-order fill), so the weight gradients need no atomics
-//      and sum each neuron's entries in ascending row order (deterministic);
-//   3. neuron pass: one wave per neuron sums its entries' x and dy rows into
-//      its dW rows, writing every row (zero for unused neurons).
+// ELL rows (gathers, fp32 accumulation, no atomics, deterministic):
+//   1. masks:  per block of 64 rows and per neuron, a 64-bit mask of the
+//      rows holding that neuron; its popcount is the block's count;
+//   2. scans:  per neuron, the prefix of those counts over blocks, then the
+//      prefix over neurons (column pointers). Entry (t, i) then sits at
+//      colptr[i] + prefix[i][block(t)] + popcount(mask bits below t): the
+//      column-major order of the entries, rows ascending inside a column;
+//   3. fill: each ELL slot writes its row index at its column-major position;
+//   4. neuron pass (dense-to-sparse, then sparse^T-to-dense): a wave per
+//      neuron keeps its wu_t and wd rows in registers and walks its entries in
+//      row order; per entry it gathers x[t] and dy[t] once, computes
+//      u = x[t] . wu_t[i] and da = dy[t] . wd[i], then a, du, dg, adds
+//      a dy[t], du x[t], dg x[t] to its three dW rows, and keeps du, dg for
+//      the dx pass. Every dW row is written (zero rows for unused neurons);
+//   5. dx (sparse-to-dense): a wave per (row, part of d_model) sums
+//      du wu_t[i] + dg wg_t[i] over the row's entries.
+// Rows are gathered with 4-byte lanes (rows.hpp).
 // Backup rows (dense MFMA, fp32 accumulation):
-//   4. U/DA: u and da of every backup row and neuron (two 128x128-tile GEMMs
+//   6. U/DA: u and da of every backup row and neuron (two 128x128-tile GEMMs
 //      over d_model), then a, du, dg (dg zero where h is zero);
-//   5. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T, scattered to their rows;
-//   6. DW:   dW += [a | du | dg]^T [dy | x | x] over the backup rows.
+//   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T, scattered to their rows;
+//   8. DW:   dW += [a | du | dg]^T [dy | x | x] over the backup rows.
 // For bf16 inputs, the fp32 intermediates a, du, dg enter the MFMA as a pair
-// of bf16 (hi + lo, 16 significant bits), so products 5 and 6 run over a K
+// of bf16 (hi + lo, 16 significant bits), so products 7 and 8 run over a K
 // twice as long; fp32 inputs use fp32 MFMA directly.
 #include "mfma_tile.hpp"
+#include "rows.hpp"
 
 namespace {
 
 constexpr int NT = 256;
-constexpr int TB = 64;     // rows per block of the column transpose
-constexpr int CH = 16384;  // columns per LDS chunk of the transpose (64 KB of counters)
+constexpr int BR = 64;    // rows per mask block (one bit each)
+constexpr int CH = 8192;  // neurons per LDS chunk of the mask launch (64 KB)
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t coef, cnt, colptr, csc, inter, total;
+    size_t coef, masks, cnt, colptr, csc, inter, total;
     int nblk, pad_ovf;
 };
 
 Layout layout(int T, int dff, int K, int max_ovf)
 {
     Layout L;
-    L.nblk = (T + TB - 1) / TB;
+    L.nblk = (T + BR - 1) / BR;
     L.pad_ovf = (max_ovf + mt::TILE - 1) / mt::TILE * mt::TILE;
     size_t o = 0;
-    L.coef = o;   o += up256((size_t)3 * T * K * 4);
+    L.coef = o;   o += up256((size_t)2 * T * K * 4); // du, dg per ELL slot
+    L.masks = o;  o += up256((size_t)L.nblk * dff * 8);
     L.cnt = o;    o += up256((size_t)L.nblk * dff * 4);
     L.colptr = o; o += up256((size_t)(dff + 1) * 4);
     L.csc = o;    o += up256((size_t)T * K * 4);
@@ -54,179 +63,62 @@ Layout layout(int T, int dff, int K, int max_ovf)
     return L;
 }
 
-// ------------------------------------------------------------ 1. ELL token pass
-template <int DT, int NCH, int G>
-__global__ __launch_bounds__(NT) void bwd_ell_kernel(
-    const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
+// ------------------------------------------------------------ 1. masks
+__global__ __launch_bounds__(NT) void ell_mask_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
-    const int16_t *__restrict__ ell_col, const void *__restrict__ ell_val, int T, int K, int dff,
-    const uint8_t *__restrict__ wg, const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd,
-    int dm, float *__restrict__ dx, float *__restrict__ coef, int32_t *__restrict__ status)
+    const int16_t *__restrict__ ell_col, int T, int K, int dff, int nblk,
+    uint64_t *__restrict__ masks, int32_t *__restrict__ cnt)
 {
-    using E = elem<DT>;
-    constexpr int P = E::per16;
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (t >= T || row_slot[t] >= 0)
-        return; // a backup row's dx comes from the dense products
-    const size_t rowbytes = (size_t)dm * sizeof(typename E::storage);
-    const size_t TK = (size_t)T * K;
-
-    float xr[NCH][P], dr[NCH][P], acc[NCH][P];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const size_t off = (size_t)(c * 64 + lane) * 16;
-        const bool in = off < rowbytes;
-        E::widen(in ? ldg16(x + (size_t)t * rowbytes + off) : make_uint4(0, 0, 0, 0), xr[c]);
-        E::widen(in ? ldg16(dy + (size_t)t * rowbytes + off) : make_uint4(0, 0, 0, 0), dr[c]);
-#pragma unroll
-        for (int k = 0; k < P; ++k)
-            acc[c][k] = 0.f;
-    }
-    const int n = min(row_nnz[t], K);
-    for (int s0 = 0; s0 < n; s0 += G) {
-        int ci[G];
-        float hv[G];
-        bool ok[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int s = s0 + g;
-            int c = 0;
-            float h = 0.f;
-            if (s < n) {
-                c = ell_col[(size_t)t * K + s];
-                h = E::load1(ell_val, (size_t)t * K + s);
-                if (c < 0 || c >= dff) {
-                    raise_status(status, TWELL_DEV_BAD_INDEX);
-                    c = 0;
-                    h = 0.f;
-                }
-            }
-            ci[g] = c;
-            hv[g] = h;
-            ok[g] = s < n && h != 0.f;
-        }
-        uint4 vu[G][NCH], vd[G][NCH], vg[G][NCH];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const size_t off = (size_t)(c * 64 + lane) * 16;
-                const bool in = ok[g] && off < rowbytes;
-                const size_t ro = (size_t)ci[g] * rowbytes + off;
-                vu[g][c] = in ? ldg16(wu + ro) : make_uint4(0, 0, 0, 0);
-                vd[g][c] = in ? ldg16(wd + ro) : make_uint4(0, 0, 0, 0);
-                vg[g][c] = in ? ldg16(wg + ro) : make_uint4(0, 0, 0, 0);
-            }
-        float pu[G], pd[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float su = 0.f, sd = 0.f;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                float w1[P], w2[P];
-                E::widen(vu[g][c], w1);
-                E::widen(vd[g][c], w2);
-#pragma unroll
-                for (int k = 0; k < P; ++k) {
-                    su += xr[c][k] * w1[k];
-                    sd += dr[c][k] * w2[k];
-                }
-            }
-            pu[g] = su;
-            pd[g] = sd;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            pu[g] = wave_sum(pu[g]);
-            pd[g] = wave_sum(pd[g]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int s = s0 + g;
-            if (s >= n)
-                continue;
-            const float u = pu[g], da = pd[g], h = hv[g];
-            const float a = ok[g] ? h * u : 0.f, du = ok[g] ? da * h : 0.f, dg = ok[g] ? da * u : 0.f;
-            if (lane == 0) {
-                const size_t e = (size_t)t * K + s;
-                coef[e] = a;
-                coef[TK + e] = du;
-                coef[2 * TK + e] = dg;
-            }
-            if (ok[g]) {
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-                    float w1[P], w3[P];
-                    E::widen(vu[g][c], w1);
-                    E::widen(vg[g][c], w3);
-#pragma unroll
-                    for (int k = 0; k < P; ++k)
-                        acc[c][k] += du * w1[k] + dg * w3[k];
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const size_t el = (size_t)(c * 64 + lane) * P;
-        if (el < (size_t)dm) {
-            float4 *d = (float4 *)(dx + (size_t)t * dm + el);
-#pragma unroll
-            for (int q = 0; q < P / 4; ++q)
-                d[q] = make_float4(acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]);
-        }
-    }
-}
-
-// ------------------------------------------------------------ 2. column transpose
-DEVI bool ell_row(const int32_t *row_slot, int t) { return row_slot[t] < 0; }
-
-__global__ __launch_bounds__(NT) void csc_hist_kernel(
-    const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
-    const int16_t *__restrict__ ell_col, int T, int K, int dff, int32_t *__restrict__ cnt)
-{
-    extern __shared__ int hist[];
+    __shared__ unsigned long long m[CH];
     const int b = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c0 = blockIdx.y * CH, c1 = min(dff, c0 + CH);
     for (int i = threadIdx.x; i < c1 - c0; i += NT)
-        hist[i] = 0;
+        m[i] = 0ull;
     __syncthreads();
-    for (int t = b * TB + wv; t < min(T, (b + 1) * TB); t += NT / 64) {
-        if (!ell_row(row_slot, t))
+    for (int t = b * BR + wv; t < min(T, (b + 1) * BR); t += NT / 64) {
+        if (row_slot[t] >= 0)
             continue;
         const int n = min(row_nnz[t], K);
+        const unsigned long long bit = 1ull << (t - b * BR);
         for (int s = lane; s < n; s += 64) {
             const int c = ell_col[(size_t)t * K + s];
             if (c >= c0 && c < c1)
-                atomicAdd(&hist[c - c0], 1);
+                atomicOr(&m[c - c0], bit);
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < c1 - c0; i += NT)
-        cnt[(size_t)b * dff + c0 + i] = hist[i];
+    for (int i = threadIdx.x; i < c1 - c0; i += NT) {
+        masks[(size_t)b * dff + c0 + i] = m[i];
+        cnt[(size_t)(c0 + i) * nblk + b] = __popcll(m[i]);
+    }
 }
 
-// per column: exclusive prefix over blocks (in place); column totals to colptr
-__global__ __launch_bounds__(NT) void csc_cols_kernel(int32_t *__restrict__ cnt, int nblk, int dff,
-                                                      int32_t *__restrict__ colptr)
+// ------------------------------------------------------------ 2. scans
+// one wave per neuron: exclusive prefix of its block counts (in place), total
+__global__ __launch_bounds__(NT) void blk_prefix_kernel(int32_t *__restrict__ cnt, int nblk, int dff,
+                                                         int32_t *__restrict__ colptr)
 {
-    const int i = blockIdx.x * NT + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
     if (i >= dff)
         return;
-    int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-        const int v = cnt[(size_t)b * dff + i];
-        cnt[(size_t)b * dff + i] = run;
-        run += v;
+    int carry = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+        const int b = b0 + lane;
+        const int v = b < nblk ? cnt[(size_t)i * nblk + b] : 0;
+        const int incl = wave_incl_scan(v, lane);
+        if (b < nblk)
+            cnt[(size_t)i * nblk + b] = carry + incl - v;
+        carry += __shfl(incl, 63, 64);
     }
-    colptr[i] = run;
+    if (lane == 0)
+        colptr[i] = carry;
 }
 
 constexpr int SCAN_NT = 1024;
 
 // in-place exclusive scan of colptr[0..dff); colptr[dff] = total
-__global__ __launch_bounds__(SCAN_NT) void csc_colptr_kernel(int32_t *__restrict__ colptr, int dff)
+__global__ __launch_bounds__(SCAN_NT) void colptr_kernel(int32_t *__restrict__ colptr, int dff)
 {
     __shared__ int wsum[SCAN_NT / 64];
     __shared__ int carry;
@@ -255,92 +147,184 @@ __global__ __launch_bounds__(SCAN_NT) void csc_colptr_kernel(int32_t *__restrict
         colptr[dff] = carry;
 }
 
-// one wave per block of TB rows, rows in ascending order: each entry goes to
-// colptr[c] + (entries of column c in earlier blocks) + (earlier in this block)
-__global__ __launch_bounds__(64) void csc_fill_kernel(
+// ------------------------------------------------------------ 3. fill
+__global__ __launch_bounds__(NT) void csc_fill_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
-    const int16_t *__restrict__ ell_col, int T, int K, int dff, const int32_t *__restrict__ cnt,
-    const int32_t *__restrict__ colptr, int32_t *__restrict__ csc)
+    const int16_t *__restrict__ ell_col, int T, int K, int dff, int nblk,
+    const uint64_t *__restrict__ masks, const int32_t *__restrict__ blkpre,
+    const int32_t *__restrict__ colptr, int32_t *__restrict__ csc, int32_t *__restrict__ status)
 {
-    extern __shared__ int cursor[];
-    const int b = blockIdx.x, lane = threadIdx.x;
-    const int c0 = blockIdx.y * CH, c1 = min(dff, c0 + CH);
-    for (int i = lane; i < c1 - c0; i += 64)
-        cursor[i] = 0;
-    __syncthreads();
-    for (int t = b * TB; t < min(T, (b + 1) * TB); ++t) {
-        if (!ell_row(row_slot, t))
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+    if (t >= T || row_slot[t] >= 0)
+        return;
+    const int n = min(row_nnz[t], K), blk = t / BR;
+    const unsigned long long below = (1ull << (t % BR)) - 1ull;
+    for (int s = lane; s < n; s += 64) {
+        const int c = ell_col[(size_t)t * K + s];
+        if (c < 0 || c >= dff) { // corrupt entry: skipped (the masks skip it too), reported
+            raise_status(status, TWELL_DEV_BAD_INDEX);
             continue;
-        const int n = min(row_nnz[t], K);
-        for (int s = lane; s < n; s += 64) {
-            const int c = ell_col[(size_t)t * K + s];
-            if (c >= c0 && c < c1) { // columns of a row are distinct, so lanes never collide
-                const int r = cursor[c - c0];
-                cursor[c - c0] = r + 1;
-                csc[colptr[c] + cnt[(size_t)b * dff + c] + r] = t * K + s;
-            }
         }
+        const int p = colptr[c] + blkpre[(size_t)c * nblk + blk] +
+                      __popcll(masks[(size_t)blk * dff + c] & below);
+        csc[p] = t * K + s;
     }
 }
 
-// ------------------------------------------------------------ 3. neuron pass
-template <int DT, int NCH>
-__global__ __launch_bounds__(NT) void dw_ell_kernel(
-    const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy, int T, int K, int dff, int dm,
+// ------------------------------------------------------------ 4. neuron pass
+// NW words per lane cover the whole row (dots); the wave accumulates the NWP
+// words of part `part` (PARTS = NW / NWP parts, one per blockIdx.y).
+template <int DT, int NW, int NWP, int G>
+__global__ __launch_bounds__(NT) void bwd_neuron_kernel(
     const int32_t *__restrict__ colptr, const int32_t *__restrict__ csc,
-    const float *__restrict__ coef, float *__restrict__ dwg, float *__restrict__ dwu,
+    const void *__restrict__ ell_val, int T, int K, int dff, const uint8_t *__restrict__ x,
+    const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd,
+    int dm, float *__restrict__ coef, float *__restrict__ dwg, float *__restrict__ dwu,
     float *__restrict__ dwd)
 {
     using E = elem<DT>;
-    constexpr int P = E::per16;
+    using R = Row<DT, NW>;
+    using RP = Row<DT, NWP>;
+    constexpr int EPW = R::EPW;
     const int lane = threadIdx.x & 63;
     const int i = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
     if (i >= dff)
         return;
-    const size_t rowbytes = (size_t)dm * sizeof(typename E::storage);
+    const int part = blockIdx.y;
+    const R geo(dm, lane, 0);
+    const RP pgeo(dm, lane, part);
     const long TK = (long)T * K;
-    float ad[NCH][P], au[NCH][P], ag[NCH][P];
+    uint32_t wuw[NW], wdw[NW];
+    geo.load_w(wu, i, wuw);
+    geo.load_w(wd, i, wdw);
+    float ad[NWP][EPW], au[NWP][EPW], ag[NWP][EPW];
+    pgeo.zero_f(ad);
+    pgeo.zero_f(au);
+    pgeo.zero_f(ag);
+    const int p0 = colptr[i], p1 = colptr[i + 1];
+    for (int pb = p0; pb < p1; pb += 64) {
+        // lane L prefetches entry pb + L: its ELL slot, row and stored h
+        const int p = pb + lane;
+        int idx = -1;
+        float h = 0.f;
+        if (p < p1) {
+            idx = csc[p];
+            if (idx >= 0 && idx < TK)
+                h = E::load1(ell_val, idx);
+            else
+                idx = -1;
+        }
+        const int tt = idx >= 0 ? idx / K : 0;
+        const int m = min(64, p1 - pb);
+        for (int e0 = 0; e0 < m; e0 += G) {
+            uint32_t vx[G][NW], vd[G][NW];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+            for (int g = 0; g < G; ++g) {
+                const int tr = bcast(tt, min(e0 + g, m - 1));
+                geo.load_w(x, tr, vx[g]);
+                geo.load_w(dy, tr, vd[g]);
+            }
 #pragma unroll
-        for (int k = 0; k < P; ++k)
-            ad[c][k] = au[c][k] = ag[c][k] = 0.f;
-    const int e1 = colptr[i + 1];
-    for (int e = colptr[i]; e < e1; ++e) {
-        const int idx = csc[e];
-        if (idx < 0 || idx >= TK)
-            continue;
-        const int t = idx / K;
-        const float a = coef[idx], du = coef[TK + idx], dg = coef[2 * TK + idx];
+            for (int g = 0; g < G; ++g) {
+                float su = 0.f, sd = 0.f;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const size_t off = (size_t)(c * 64 + lane) * 16;
-            if (off < rowbytes) {
-                float xv[P], dv[P];
-                E::widen(ldg16(x + (size_t)t * rowbytes + off), xv);
-                E::widen(ldg16(dy + (size_t)t * rowbytes + off), dv);
+                for (int c = 0; c < NW; ++c) {
+                    float a1[EPW], b1[EPW], a2[EPW], b2[EPW];
+                    geo.widen(vx[g][c], a1);
+                    geo.widen(wuw[c], b1);
+                    geo.widen(vd[g][c], a2);
+                    geo.widen(wdw[c], b2);
 #pragma unroll
-                for (int k = 0; k < P; ++k) {
-                    ad[c][k] += a * dv[k];
-                    au[c][k] += du * xv[k];
-                    ag[c][k] += dg * xv[k];
+                    for (int e = 0; e < EPW; ++e) {
+                        su += a1[e] * b1[e];
+                        sd += a2[e] * b2[e];
+                    }
+                }
+                const float u = wave_sum(su), da = wave_sum(sd);
+                const bool in = e0 + g < m;
+                const float hh = in ? bcast(h, e0 + g) : 0.f;
+                const float a = hh * u, du = da * hh, dg = hh != 0.f ? da * u : 0.f;
+                // the lane that owns this entry keeps du, dg for the dx pass
+                if (in && lane == e0 + g && idx >= 0) {
+                    coef[idx] = du;
+                    coef[TK + idx] = dg;
+                }
+                // this wave's part of the row: words c = part * NWP + c2 (static
+                // indices; the part test is uniform across the wave)
+#pragma unroll
+                for (int c = 0; c < NW; ++c) {
+                    if (c / NWP != part)
+                        continue;
+                    const int c2 = c % NWP;
+                    float xv[EPW], dv[EPW];
+                    geo.widen(vx[g][c], xv);
+                    geo.widen(vd[g][c], dv);
+#pragma unroll
+                    for (int e = 0; e < EPW; ++e) {
+                        ad[c2][e] += a * dv[e];
+                        au[c2][e] += du * xv[e];
+                        ag[c2][e] += dg * xv[e];
+                    }
                 }
             }
         }
     }
+    pgeo.store_f(dwd, i, ad);
+    pgeo.store_f(dwu, i, au);
+    pgeo.store_f(dwg, i, ag);
+}
+
+// ------------------------------------------------------------ 5. dx
+template <int DT, int NW, int G>
+__global__ __launch_bounds__(NT) void bwd_dx_kernel(
+    const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
+    const int16_t *__restrict__ ell_col, const float *__restrict__ coef, int T, int K, int dff,
+    const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wg, int dm,
+    float *__restrict__ dx)
+{
+    using R = Row<DT, NW>;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+    if (t >= T || row_slot[t] >= 0)
+        return; // a backup row's dx comes from the dense products
+    const R geo(dm, lane, blockIdx.y);
+    const size_t TK = (size_t)T * K, rb = (size_t)t * K;
+    float acc[NW][R::EPW];
+    geo.zero_f(acc);
+    const int n = min(row_nnz[t], K);
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        // each lane fetches one entry, then the wave walks them in order
+        const int s = s0 + lane;
+        int ci = 0;
+        float cu = 0.f, cg = 0.f;
+        if (s < n) {
+            ci = ell_col[rb + s];
+            cu = coef[rb + s];
+            cg = coef[TK + rb + s];
+            if (ci < 0 || ci >= dff) {
+                ci = 0;
+                cu = cg = 0.f;
+            }
+        }
+        const int m = min(64, n - s0);
+        for (int e0 = 0; e0 < m; e0 += G) {
+            uint32_t vu[G][NW], vg[G][NW];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const size_t el = (size_t)(c * 64 + lane) * P;
-        if (el < (size_t)dm) {
-            const size_t o = (size_t)i * dm + el;
+            for (int g = 0; g < G; ++g) {
+                const int c = bcast(ci, min(e0 + g, m - 1));
+                geo.load_w(wu, c, vu[g]);
+                geo.load_w(wg, c, vg[g]);
+            }
 #pragma unroll
-            for (int q = 0; q < P / 4; ++q) {
-                *(float4 *)(dwd + o + 4 * q) = make_float4(ad[c][4 * q], ad[c][4 * q + 1], ad[c][4 * q + 2], ad[c][4 * q + 3]);
-                *(float4 *)(dwu + o + 4 * q) = make_float4(au[c][4 * q], au[c][4 * q + 1], au[c][4 * q + 2], au[c][4 * q + 3]);
-                *(float4 *)(dwg + o + 4 * q) = make_float4(ag[c][4 * q], ag[c][4 * q + 1], ag[c][4 * q + 2], ag[c][4 * q + 3]);
+            for (int g = 0; g < G; ++g) {
+                const bool in = e0 + g < m;
+                geo.axpy(acc, in ? bcast(cu, e0 + g) : 0.f, vu[g]);
+                geo.axpy(acc, in ? bcast(cg, e0 + g) : 0.f, vg[g]);
             }
         }
     }
+    geo.store_f(dx, t, acc);
 }
 
 // ------------------------------------------------------------ 4-6. backup rows
@@ -533,66 +517,79 @@ __global__ __launch_bounds__(mt::NT, 2) void ovf_dw_kernel(
             }
 }
 
-template <int DT, int NCH>
-hipError_t launch_nch(const void *x, const void *dy, const hybrid_t *h, const void *wg,
-                      const void *wu, const void *wd, int dm, float *dx, float *dwg, float *dwu,
-                      float *dwd, uint8_t *ws, int32_t *status, hipStream_t s)
+template <int DT, int NW>
+void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg, const void *wu,
+                const void *wd, int dm, float *dx, float *dwg, float *dwu, float *dwd, uint8_t *ws,
+                int32_t *status, Timer &tm, hipStream_t s)
 {
     const int T = h->T, K = h->K, dff = h->d_ff;
     const Layout L = layout(T, dff, K, h->max_ovf);
     float *coef = (float *)(ws + L.coef);
+    uint64_t *masks = (uint64_t *)(ws + L.masks);
     int32_t *cnt = (int32_t *)(ws + L.cnt), *colptr = (int32_t *)(ws + L.colptr);
     int32_t *csc = (int32_t *)(ws + L.csc);
     void *inter = ws + L.inter;
     const size_t stride = (size_t)L.pad_ovf * dff;
     const uint8_t *xb = (const uint8_t *)x, *dyb = (const uint8_t *)dy;
-    constexpr int G = NCH <= 2 ? 2 : 1;
-    const int nch = (dff + CH - 1) / CH;
-    const size_t lds_hist = (size_t)min(dff, CH) * sizeof(int);
+    const int rgroups = (T + NT / 64 - 1) / (NT / 64), ngroups = (dff + NT / 64 - 1) / (NT / 64);
+    constexpr int NWN = NW < 16 ? NW : 16;          // neuron pass: accumulated words per lane
+    constexpr int GN = NW <= 8 ? 4 : (NW <= 16 ? 2 : 1);
+    constexpr int NWP = NW < ACC_NW ? NW : ACC_NW; // dx pass: words per lane of one part
+    const int parts = row_parts<DT>(dm, NWP);
 
     if (T > 0) {
-        hipLaunchKernelGGL((bwd_ell_kernel<DT, NCH, G>), dim3((T + 3) / 4), dim3(NT), 0, s, xb, dyb,
-                           h->row_nnz, h->row_slot, h->ell_col, h->ell_val, T, K, dff,
-                           (const uint8_t *)wg, (const uint8_t *)wu, (const uint8_t *)wd, dm, dx,
-                           coef, status);
-        hipLaunchKernelGGL(csc_hist_kernel, dim3(L.nblk, nch), dim3(NT), lds_hist, s, h->row_nnz,
-                           h->row_slot, h->ell_col, T, K, dff, cnt);
+        hipLaunchKernelGGL(ell_mask_kernel, dim3(L.nblk, (dff + CH - 1) / CH), dim3(NT), 0, s,
+                           h->row_nnz, h->row_slot, h->ell_col, T, K, dff, L.nblk, masks, cnt);
+        tm.mark("ell_mask_kernel");
     }
-    hipLaunchKernelGGL(csc_cols_kernel, dim3((dff + NT - 1) / NT), dim3(NT), 0, s, cnt, L.nblk,
-                       dff, colptr);
-    hipLaunchKernelGGL(csc_colptr_kernel, dim3(1), dim3(SCAN_NT), 0, s, colptr, dff);
-    if (T > 0)
-        hipLaunchKernelGGL(csc_fill_kernel, dim3(L.nblk, nch), dim3(64), lds_hist, s, h->row_nnz,
-                           h->row_slot, h->ell_col, T, K, dff, cnt, colptr, csc);
-    hipLaunchKernelGGL((dw_ell_kernel<DT, NCH>), dim3((dff + 3) / 4), dim3(NT), 0, s, xb, dyb, T,
-                       K, dff, dm, colptr, csc, coef, dwg, dwu, dwd);
+    hipLaunchKernelGGL(blk_prefix_kernel, dim3(ngroups), dim3(NT), 0, s, cnt, L.nblk, dff, colptr);
+    tm.mark("blk_prefix_kernel");
+    hipLaunchKernelGGL(colptr_kernel, dim3(1), dim3(SCAN_NT), 0, s, colptr, dff);
+    tm.mark("colptr_kernel");
+    if (T > 0) {
+        hipLaunchKernelGGL(csc_fill_kernel, dim3(rgroups), dim3(NT), 0, s, h->row_nnz,
+                           h->row_slot, h->ell_col, T, K, dff, L.nblk, masks, cnt, colptr, csc,
+                           status);
+        tm.mark("csc_fill_kernel");
+    }
+    hipLaunchKernelGGL((bwd_neuron_kernel<DT, NW, NWN, GN>), dim3(ngroups, NW / NWN), dim3(NT),
+                       0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
+                       (const uint8_t *)wd, dm, coef, dwg, dwu, dwd);
+    tm.mark("bwd_neuron_kernel");
+    if (T > 0) {
+        hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, 8>), dim3(rgroups, parts), dim3(NT), 0, s,
+                           h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dff,
+                           (const uint8_t *)wu, (const uint8_t *)wg, dm, dx);
+        tm.mark("bwd_dx_kernel");
+    }
     if (h->max_ovf > 0 && T > 0) {
         const int mt_tiles = L.pad_ovf / mt::TILE;
         hipLaunchKernelGGL((ovf_ud_kernel<DT>), dim3(dff / mt::TILE, mt_tiles), dim3(mt::NT), 0, s,
                            xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
                            (const uint8_t *)wd, dm, dff, h->dense, inter, stride);
+        tm.mark("ovf_ud_kernel");
         const int nt_dm = (dm + mt::TILE - 1) / mt::TILE;
         hipLaunchKernelGGL((ovf_dx_kernel<DT>), dim3(nt_dm, mt_tiles), dim3(mt::NT), 0, s, inter,
                            stride, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
                            (const uint8_t *)wg, dm, dff, dx);
+        tm.mark("ovf_dx_kernel");
         hipLaunchKernelGGL((ovf_dw_kernel<DT>), dim3(nt_dm, dff / mt::TILE, 3), dim3(mt::NT), 0, s,
                            inter, stride, h->ovf_rows, h->n_ovf, h->max_ovf, xb, dyb, dm, dff, dwd,
                            dwu, dwg);
+        tm.mark("ovf_dw_kernel");
     }
-    return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_dt(const void *x, const void *dy, const hybrid_t *h, const void *wg,
-                     const void *wu, const void *wd, int dm, float *dx, float *dwg, float *dwu,
-                     float *dwd, uint8_t *ws, int32_t *status, hipStream_t s)
+void launch_dt(const void *x, const void *dy, const hybrid_t *h, const void *wg, const void *wu,
+               const void *wd, int dm, float *dx, float *dwg, float *dwu, float *dwd, uint8_t *ws,
+               int32_t *status, Timer &tm, hipStream_t s)
 {
-    const int nch = (dm * (int)sizeof(typename elem<DT>::storage) + 1023) / 1024;
 #define TW_CASE(N) \
-    case N: return launch_nch<DT, N>(x, dy, h, wg, wu, wd, dm, dx, dwg, dwu, dwd, ws, status, s);
-    switch (nch) {
-        TW_CASE(1) TW_CASE(2) TW_CASE(3) TW_CASE(4) TW_CASE(5) TW_CASE(6) TW_CASE(7)
-    default: return launch_nch<DT, 8>(x, dy, h, wg, wu, wd, dm, dx, dwg, dwu, dwd, ws, status, s);
+    case N: launch_all<DT, N>(x, dy, h, wg, wu, wd, dm, dx, dwg, dwu, dwd, ws, status, tm, s); break;
+    switch (row_nw<DT>(dm)) {
+        TW_CASE(1) TW_CASE(2) TW_CASE(4) TW_CASE(8) TW_CASE(16)
+    default: launch_all<DT, 32>(x, dy, h, wg, wu, wd, dm, dx, dwg, dwu, dwd, ws, status, tm, s);
     }
 #undef TW_CASE
 }
@@ -605,10 +602,11 @@ size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *
     const Layout L = layout(T, dff, K, max_ovf);
     if (offsets) {
         offsets[0] = L.coef;
-        offsets[1] = L.cnt;
-        offsets[2] = L.colptr;
-        offsets[3] = L.csc;
-        offsets[4] = L.inter;
+        offsets[1] = L.masks;
+        offsets[2] = L.cnt;
+        offsets[3] = L.colptr;
+        offsets[4] = L.csc;
+        offsets[5] = L.inter;
     }
     return L.total;
 }
@@ -616,11 +614,14 @@ size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *
 hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
                       const void *wg_t, const void *wu_t, const void *wd, int dm, float *dx,
                       float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
-                      hipStream_t s)
+                      twell_timing_t *timing, hipStream_t s)
 {
+    Timer tm(timing, s);
     if (dt == TWELL_BF16)
-        return launch_dt<TWELL_BF16>(x, dy, h, wg_t, wu_t, wd, dm, dx, dwg_t, dwu_t, dwd,
-                                     (uint8_t *)ws, status, s);
-    return launch_dt<TWELL_F32>(x, dy, h, wg_t, wu_t, wd, dm, dx, dwg_t, dwu_t, dwd,
-                                (uint8_t *)ws, status, s);
+        launch_dt<TWELL_BF16>(x, dy, h, wg_t, wu_t, wd, dm, dx, dwg_t, dwu_t, dwd,
+                              (uint8_t *)ws, status, tm, s);
+    else
+        launch_dt<TWELL_F32>(x, dy, h, wg_t, wu_t, wd, dm, dx, dwg_t, dwu_t, dwd,
+                             (uint8_t *)ws, status, tm, s);
+    return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -76,11 +77,117 @@ DEVI int wave_incl_scan(int v, int lane)
 
 DEVI uint32_t lanemask_lt32(int lane32) { return (1u << lane32) - 1u; }
 
+// Broadcast lane `src` (wave-uniform) of v to every lane, through a scalar register.
+DEVI int bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+DEVI float bcast(float v, int src)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 DEVI void raise_status(int32_t *status, int bits)
 {
     if (status)
         atomicOr(status, bits);
 }
 
-// Host-side launch helpers (defined in api.hip).
-int twell_launch_check();
+// ---- XCD-aware work split. MI355X has 8 XCDs, each with its own L2, and
+// hands consecutive workgroup ids to the XCDs in turn, so workgroup b runs on
+// XCD b % 8. Kernels that gather weight or activation rows give each XCD one
+// eighth of the data (a range of neuron tiles, or a slice of d_model
+// columns) so that its share stays resident in that XCD's L2.
+constexpr int NXCD = 8;
+
+// Slice of d_model columns for XCD-split gathers: each lane of a wave owns NE
+// consecutive elements (VB bytes), a wave covers 64 * NE columns.
+template <int DT, int VB> struct Vec {
+    static constexpr int NW = VB / 4;
+    static constexpr int NE = DT == TWELL_BF16 ? 2 * NW : NW;
+    uint32_t w[NW];
+    DEVI void load(const uint8_t *p)
+    {
+        if constexpr (NW == 1) {
+            w[0] = *(const uint32_t *)p;
+        } else if constexpr (NW == 2) {
+            const uint2 v = *(const uint2 *)p;
+            w[0] = v.x; w[1] = v.y;
+        } else if constexpr (NW == 3) {
+            const uint3 v = *(const uint3 *)p;
+            w[0] = v.x; w[1] = v.y; w[2] = v.z;
+        } else {
+            const uint4 v = *(const uint4 *)p;
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        }
+    }
+    DEVI void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            w[i] = 0;
+    }
+    DEVI void widen(float *o) const
+    {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            if constexpr (DT == TWELL_BF16) {
+                o[2 * i] = bf16_lo(w[i]);
+                o[2 * i + 1] = bf16_hi(w[i]);
+            } else {
+                o[i] = __uint_as_float(w[i]);
+            }
+        }
+    }
+};
+
+// Bytes per lane (4, 8, 12 or 16) of a d_model slice: the narrowest whose
+// slices number at most NXCD (12 only when it divides d_model evenly).
+inline int slice_bytes(int dt, int dm)
+{
+    const int esz = dt == TWELL_BF16 ? 2 : 4;
+    for (int vb : {4, 8}) {
+        const int cols = 64 * vb / esz;
+        if ((dm + cols - 1) / cols <= NXCD)
+            return vb;
+    }
+    const int c12 = 64 * 12 / esz;
+    if (dm % c12 == 0 && dm / c12 <= NXCD)
+        return 12;
+    return 16;
+}
+
+DEVI void store_f32(float *dst, const float *v, int n)
+{
+    if (n % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < n / 4; ++q)
+            ((float4 *)dst)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else if (n % 2 == 0) {
+#pragma unroll
+        for (int q = 0; q < n / 2; ++q)
+            ((float2 *)dst)[q] = make_float2(v[2 * q], v[2 * q + 1]);
+    } else {
+        for (int q = 0; q < n; ++q)
+            dst[q] = v[q];
+    }
+}
+
+// ---- optional kernel timing of one API call (see twell_timing_t)
+struct Timer {
+    twell_timing_t *t;
+    hipStream_t s;
+    Timer(twell_timing_t *t_, hipStream_t s_) : t(t_), s(s_)
+    {
+        if (t) {
+            t->n_used = 0;
+            if (t->n_events > 0 && hipEventRecord((hipEvent_t)t->events[0], s) == hipSuccess)
+                t->n_used = 1;
+        }
+    }
+    void mark(const char *name)
+    {
+        if (!t || t->n_used <= 0 || t->n_used >= t->n_events || t->n_used > TWELL_TIMING_MAX)
+            return;
+        t->names[t->n_used - 1] = name;
+        if (hipEventRecord((hipEvent_t)t->events[t->n_used], s) == hipSuccess)
+            ++t->n_used;
+    }
+};

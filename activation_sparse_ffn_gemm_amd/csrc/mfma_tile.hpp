@@ -21,7 +21,11 @@ constexpr int TILE = 128;
 constexpr int ROWB = 128;
 constexpr int NT = 256;
 
-DEVI int swz(int r, int c) { return r * ROWB + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk c of LDS row r (128-byte rows). A 128-bit
+// fragment read serves 16 lanes per LDS cycle across 64 banks: 16 consecutive
+// rows, same chunk. Row r starts at bank 32 * (r % 2), so XOR-ing the chunk with
+// (r / 2) % 8 gives those 16 rows 16 distinct bank groups (no conflicts).
+DEVI int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <int DT> DEVI void mma_group(floatx16_t &acc, const uint4 &a, const uint4 &b);
 

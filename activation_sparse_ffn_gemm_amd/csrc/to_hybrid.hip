@@ -122,27 +122,32 @@ __global__ __launch_bounds__(256) void hyb_dense_kernel(
 }
 
 template <int DT>
-hipError_t launch(const twell_t *h, const hybrid_t *o, int32_t *status, hipStream_t s)
+hipError_t launch(const twell_t *h, const hybrid_t *o, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int nt = h->d_ff / TWELL_TILE_C;
     if (h->T > 0)
         hipLaunchKernelGGL(hyb_rows_kernel<DT>, dim3((h->T + 3) / 4), dim3(256), 0, s, h->count,
                            h->col, h->val, h->T, nt, h->width, o->K, o->row_nnz, o->ell_col,
                            o->ell_val);
+    tm.mark("hyb_rows_kernel");
     hipLaunchKernelGGL(hyb_slots_kernel, dim3(1), dim3(SCAN_NT), 0, s, o->row_nnz, h->T, o->K,
                        o->max_ovf, o->row_slot, o->ovf_rows, o->n_ovf, status);
+    tm.mark("hyb_slots_kernel");
     const int nslots = min(o->max_ovf, h->T);
     if (nslots > 0)
         hipLaunchKernelGGL(hyb_dense_kernel<DT>, dim3(nslots), dim3(256), 0, s, h->count, h->col,
                            h->val, nt, h->width, h->d_ff, o->max_ovf, o->ovf_rows, o->n_ovf,
                            o->dense, status);
+    tm.mark("hyb_dense_kernel");
     return hipGetLastError();
 }
 
 } // namespace
 
-hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status, hipStream_t s)
+hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status,
+                            twell_timing_t *timing, hipStream_t s)
 {
-    return h->dtype == TWELL_BF16 ? launch<TWELL_BF16>(h, o, status, s)
-                                  : launch<TWELL_F32>(h, o, status, s);
+    Timer tm(timing, s);
+    return h->dtype == TWELL_BF16 ? launch<TWELL_BF16>(h, o, status, tm, s)
+                                  : launch<TWELL_F32>(h, o, status, tm, s);
 }

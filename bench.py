@@ -1,0 +1,265 @@
+"""Benchmark of the activation-sparse ReLU-gated FFN hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+twell_gate_pack (gate GEMM + TwELL epilogue) -> twell_ffn_fwd (fused up/down)
+-> twell_to_hybrid -> hybrid_ffn_bwd (dx, dW_g, dW_u, dW_d for a synthetic
+dy). The default workload is the 0.5B-scale layer at 1% gate density
+(T = 4096 tokens, d_model = 1024, d_ff = 2816, bf16). Inputs are resident in
+HBM before the timed region. Prints one JSON line.
+
+Beside the step it reports: per-stage times (HIP events on the stream the
+kernels run on), the roofline of the dominant kernel, the same layer run dense
+in bf16 by torch (forward, and forward + backward), and the CPU oracle timed
+on this host (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "0.5b-1pct": dict(T=4096, d_model=1024, d_ff=2816, density=0.01, width=32, K=128,
+                      max_ovf=256, skew_frac=0.0, skew_density=0.0),
+    "1.5b-1pct": dict(T=8192, d_model=2048, d_ff=5632, density=0.01, width=32, K=128,
+                      max_ovf=512, skew_frac=0.0, skew_density=0.0),
+    "1.5b-train-skewed": dict(T=8192, d_model=2048, d_ff=5632, density=0.01, width=128, K=128,
+                              max_ovf=1024, skew_frac=0.05, skew_density=0.30),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="0.5b-1pct", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense torch leg")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="only run a plain device copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the layer is not sharded "
+                                   "across GPUs (bench.py --gpus 1)"}), flush=True)
+        sys.exit(2)
+    import torch
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if a.copy_calib:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    from activation_sparse_ffn_gemm_amd import _lib as tw
+    from activation_sparse_ffn_gemm_amd import synth
+
+    cfg = WORKLOADS[a.workload]
+    w = synth.Workload(a.workload, cfg["T"], cfg["d_model"], cfg["d_ff"], "bf16", cfg["density"],
+                       skew_frac=cfg["skew_frac"], skew_density=cfg["skew_density"],
+                       K=cfg["K"], max_ovf=cfg["max_ovf"], width=cfg["width"])
+    d = synth.make_inputs(w, with_dy=True)
+    x, wg, wu, wd, dy = (d[k].to(dev) for k in ("x", "wg_t", "wu_t", "wd", "dy"))
+    T, dm, dff = w.T, w.d_model, w.d_ff
+
+    # preallocated outputs and workspaces: the timed region allocates nothing
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    twl = tw.empty_twell(T, dff, w.width, torch.bfloat16, dev)
+    y = torch.empty((T, dm), dtype=torch.float32, device=dev)
+    fws_n = tw.fwd_workspace_bytes(tw.TWELL_BF16, T, dm, dff, w.width)
+    fws = torch.empty(max(fws_n, 1), dtype=torch.uint8, device=dev)
+    hy = tw.empty_hybrid(T, dff, w.K, w.max_ovf, torch.bfloat16, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = (torch.empty((T, dm), **f32), torch.empty((dff, dm), **f32),
+             torch.empty((dff, dm), **f32), torch.empty((dff, dm), **f32))
+    bws = torch.empty(tw.bwd_workspace_bytes(tw.TWELL_BF16, T, dm, dff, w.K, w.max_ovf),
+                      dtype=torch.uint8, device=dev)
+
+    stages = ("gate_pack", "ffn_fwd", "to_hybrid", "bwd")
+    timers = {k: tw.KernelTimer() for k in stages}
+
+    def step(timed=False):
+        tm = timers if timed else {k: None for k in stages}
+        tw.gate_pack(x, wg, width=w.width, out=twl, status=st, timing=tm["gate_pack"])
+        tw.ffn_fwd(x, twl, wu, wd, y=y, workspace=fws, status=st, timing=tm["ffn_fwd"])
+        tw.to_hybrid(twl, w.K, w.max_ovf, out=hy, status=st, timing=tm["to_hybrid"])
+        tw.ffn_bwd(x, dy, hy, wg, wu, wd, out=grads, workspace=bws, status=st,
+                   timing=tm["bwd"])
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(st.item()) != 0:
+        raise SystemExit(f"device status {int(st.item())}: a TwELL tile or the backup overflowed")
+    nnz = int(torch.minimum(twl.count, torch.tensor(w.width, device=dev)).sum())
+    n_ovf = int(hy.n_ovf.item())
+    ell_rows = hy.row_slot < 0
+    nnz_ell = int(hy.row_nnz[ell_rows].sum())
+
+    # timed region: K steps back to back, bracketed by synchronisation; the
+    # first and last of each call's events bracket the whole step
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record()
+    for _ in range(a.steps):
+        step()
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e_start.elapsed_time(e_end) / a.steps
+
+    # per-kernel durations: the same steps again, each call with its events
+    kern_ms, stage_ms = {}, {k: 0.0 for k in stages}
+    for _ in range(a.steps):
+        step(timed=True)
+        torch.cuda.synchronize()
+        for k in stages:
+            for name, ms in timers[k].collect():
+                kern_ms[name] = kern_ms.get(name, 0.0) + ms / a.steps
+                stage_ms[k] += ms / a.steps
+
+    # ---- roofline of the dominant kernel: algorithmic work of one launch
+    row_b = dm * 2                        # one bf16 row of d_model
+    twell_b = T * (dff // 128) * 4 + nnz * 4
+    work = {
+        "gate_pack_kernel": ("mfma", 2.0 * T * dm * dff, "2 d_model d_ff flop per token"),
+        "fwd_up_kernel": ("hbm", nnz * row_b + T * row_b + twell_b + nnz * 4,
+                          "one wu_t row per nonzero + x + TwELL + a"),
+        "fwd_down_kernel": ("hbm", nnz * row_b + twell_b + nnz * 4 + T * dm * 4,
+                            "one wd row per nonzero + TwELL + a + y"),
+        "bwd_sddmm_kernel": ("hbm", nnz_ell * 2 * row_b + 2 * T * row_b + nnz_ell * 20,
+                             "wu_t and wd rows per ELL nonzero + x, dy + coefficients"),
+        "bwd_dx_kernel": ("hbm", nnz_ell * 2 * row_b + nnz_ell * 10 + T * dm * 4,
+                          "wu_t and wg_t rows per ELL nonzero + coefficients + dx"),
+        "bwd_dw_kernel": ("hbm", nnz_ell * 2 * row_b + nnz_ell * 16 + 3 * dff * dm * 4,
+                          "x and dy rows per ELL nonzero + coefficients + 3 dW"),
+    }
+    peak = {"mfma": BF16_PEAK_TFLOPS, "hbm": HBM_PEAK_GBS}
+    unit = {"mfma": "TFLOP/s", "hbm": "GB/s"}
+    scale = {"mfma": 1e12, "hbm": 1e9}
+    per_kernel = {}
+    for name, ms in kern_ms.items():
+        ent = {"ms": round(ms, 4)}
+        if name in work:
+            b, wk, desc = work[name]
+            ach = wk / (ms * 1e-3) / scale[b]
+            ent.update(bound=b, achieved=round(ach, 1), unit=unit[b],
+                       frac=round(ach / peak[b], 4), work=wk, work_unit=desc)
+        per_kernel[name] = ent
+    dom = max((k for k in kern_ms if k in work), key=lambda k: kern_ms[k])
+    b, wk, desc = work[dom]
+    ach = wk / (kern_ms[dom] * 1e-3) / scale[b]
+    roofline = {"kernel": dom, "bound": b, "achieved": round(ach, 1), "peak": peak[b],
+                "unit": unit[b], "frac": round(ach / peak[b], 4), "traffic": None,
+                "launch_ms": round(kern_ms[dom], 4), "work_per_launch": wk, "work_unit": desc}
+
+    # ---- dense bf16 layer, same shapes, torch (hipBLASLt) as a timed black box
+    dense = None
+    if not a.no_dense:
+        wgu_t = torch.cat([wg, wu], 0).t().contiguous()  # [d_model][2 d_ff]
+        wd_c = wd.contiguous()
+
+        def dense_fwd(xx):
+            gu = xx @ wgu_t
+            return (torch.relu(gu[:, :dff]) * gu[:, dff:]) @ wd_c
+
+        p_gu = wgu_t.clone().requires_grad_(True)
+        p_d = wd_c.clone().requires_grad_(True)
+        xr = x.clone().requires_grad_(True)
+
+        def dense_train():
+            gu = xr @ p_gu
+            yy = (torch.relu(gu[:, :dff]) * gu[:, dff:]) @ p_d
+            yy.backward(dy)
+
+        def timeit(fn, n):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        with torch.no_grad():
+            fwd_ms = timeit(lambda: dense_fwd(x), a.steps)
+        train_ms = timeit(dense_train, a.steps)
+        dense = {"fwd_tokens_per_s": round(T / (fwd_ms * 1e-3), 1), "fwd_ms": round(fwd_ms, 4),
+                 "train_tokens_per_s": round(T / (train_ms * 1e-3), 1),
+                 "train_ms": round(train_ms, 4),
+                 "train_tflops": round(9 * 2.0 * T * dm * dff / (train_ms * 1e-3) / 1e12, 1)}
+        del p_gu, p_d, xr
+
+    # ---- CPU oracle on this host (bounded sample of the same workload)
+    cpu = None
+    if not a.no_cpu:
+        import numpy as np
+        from oracle import oracle as orc
+        f64 = lambda t: t.double().numpy()
+        X, WG, WU, WD, DY = (f64(d[k]) for k in ("x", "wg_t", "wu_t", "wd", "dy"))
+        Ts = T
+        reps, toks, el = 0, 0, 0.0
+        while el < 10.0 and reps < 50:
+            t1 = time.perf_counter()
+            g = orc.gate(X[:Ts], WG)
+            tws = orc.twell_pack(g, W=w.width)
+            tws["val"] = f64(torch.from_numpy(tws["val"]).to(torch.bfloat16))
+            orc.ffn_twell(X[:Ts], tws, WU, WD)
+            hys = orc.to_hybrid(tws, w.K, w.max_ovf)
+            orc.bwd_hybrid(X[:Ts], DY[:Ts], hys, WG, WU, WD)
+            el += time.perf_counter() - t1
+            toks += Ts
+            reps += 1
+        cpu = {"value": round(toks / el, 1), "unit": "tokens/s", "cores": orc.num_threads(),
+               "kind": "oracle",
+               "sample": f"{reps} x the full step (gate, TwELL pack, sparse up/down, hybrid, "
+                         f"backward) over all {Ts} tokens of the batch, float64, {el:.1f} s"}
+
+    out = {
+        "metric": "FFN-layer tokens/s at 1% gate density (fwd + TwELL->hybrid + bwd step)",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs and weights, gate offset "
+                                 "for the target density)",
+        "config": {"workload": a.workload, "T": T, "d_model": dm, "d_ff": dff,
+                   "density": w.density, "measured_density": round(nnz / (T * dff), 5),
+                   "nnz": nnz, "nnz_ell": nnz_ell, "n_ovf": n_ovf, "twell_width": w.width,
+                   "K": w.K, "max_ovf": w.max_ovf},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "fwd_tokens_per_s": round(T / ((stage_ms["gate_pack"] + stage_ms["ffn_fwd"]) * 1e-3), 1),
+        "roofline": roofline,
+        "kernels": per_kernel,
+        "dense_bf16": dense,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

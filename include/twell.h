@@ -72,6 +72,22 @@ enum {
 #define TWELL_TILE_C 128 /* columns per TwELL tile: the gate kernel's N tile */
 
 /*
+ * Optional per-call kernel timing (host struct, caller-owned; pass NULL for
+ * none). The caller creates up to TWELL_TIMING_MAX + 1 hipEvent_t handles and
+ * puts them in events[0 .. n_events). A call records events[0] on its stream
+ * before its first kernel and events[k] right after its k-th kernel, sets
+ * n_used to the number of events it recorded and names[k - 1] to the name of
+ * the k-th kernel. Recording stops when the events run out.
+ */
+#define TWELL_TIMING_MAX 24
+typedef struct {
+    void *events[TWELL_TIMING_MAX + 1];
+    int32_t n_events;
+    int32_t n_used;
+    const char *names[TWELL_TIMING_MAX];
+} twell_timing_t;
+
+/*
  * TwELL of h = ReLU(x W_g) (section 2.B.1 of the summary page: the columns
  * are cut into tiles and each tile of each row keeps a count, the column
  * indices and the values of its nonzeros).
@@ -132,19 +148,21 @@ typedef struct {
  * Errors: NULL / SHAPE / DTYPE / ALIGN / HIP.
  */
 int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, int32_t d_model,
-                    const twell_t *out, int32_t *dev_status, void *stream);
+                    const twell_t *out, int32_t *dev_status, twell_timing_t *timing,
+                    void *stream);
 
 /*
  * Fused up and down projections over the TwELL nonzeros (section 2.B.2 of the
  * summary page): y[t] = sum over stored (i, h) of row t of
  * h * (x[t] . wu_t[i]) * wd[i], float32 accumulation. y [T][d_model] float32
  * is overwritten. workspace: at least twell_fwd_workspace_bytes(...) bytes
- * (may be NULL when that is 0).
+ * (it holds one float32 per TwELL slot).
  * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
  */
 int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
                   const void *wd, int32_t d_model, float *y, void *workspace,
-                  size_t workspace_bytes, int32_t *dev_status, void *stream);
+                  size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
+                  void *stream);
 
 size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                  int32_t width);
@@ -157,7 +175,8 @@ size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int
  * rows (whole rows, zeros included).
  * Errors: NULL / SHAPE / DTYPE / HIP.
  */
-int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status, void *stream);
+int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
+                    twell_timing_t *timing, void *stream);
 
 /*
  * Backward of y = (h (.) x W_u) W_d on the pattern P held by a hybrid
@@ -177,7 +196,8 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status, 
 int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
                    const void *wg_t, const void *wu_t, const void *wd, int32_t d_model,
                    float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
-                   size_t workspace_bytes, int32_t *dev_status, void *stream);
+                   size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
+                   void *stream);
 
 size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                   int32_t K, int32_t max_ovf);

@@ -50,7 +50,7 @@ def hybrid_c(T=4, d_ff=256, K=16, max_ovf=4, dtype=tw.TWELL_BF16, ptr=FAKE):
 
 def gate(L, dt=tw.TWELL_BF16, x=FAKE, w=FAKE, T=4, dm=64, out=None):
     out = out or twell_c(T=T)
-    return L.twell_gate_pack(dt, x, w, T, dm, ctypes.byref(out), None, None)
+    return L.twell_gate_pack(dt, x, w, T, dm, ctypes.byref(out), None, None, None)
 
 
 def test_gate_pack_validation(L):
@@ -75,17 +75,22 @@ def test_ffn_fwd_validation(L):
     t = twell_c()
     f = lambda **k: L.twell_ffn_fwd(k.get("dt", tw.TWELL_BF16), k.get("x", FAKE),
                                     ctypes.byref(k.get("t", t)), FAKE, FAKE, k.get("dm", 64),
-                                    k.get("y", FAKE), None, 0, None, None)
+                                    k.get("y", FAKE), k.get("ws", FAKE), k.get("nb", 1 << 30),
+                                    None, None, None)
     assert f(dt=9) == -3
     assert f(y=0) == -1
     assert f(dm=100) == -2
     assert f(y=FAKE + 4) == -4
     assert f(t=twell_c(dtype=tw.TWELL_F32)) == -3
     assert f(t=twell_c(T=0, ptr=0)) == 0
+    need = L.twell_fwd_workspace_bytes(tw.TWELL_BF16, 4, 64, 256, 128)
+    if need:
+        assert f(nb=need - 1) == -5                       # workspace too small
+        assert f(ws=FAKE + 4) == -4
 
 
 def test_to_hybrid_validation(L):
-    f = lambda t, h: L.twell_to_hybrid(ctypes.byref(t), ctypes.byref(h), None, None)
+    f = lambda t, h: L.twell_to_hybrid(ctypes.byref(t), ctypes.byref(h), None, None, None)
     assert f(twell_c(), hybrid_c(T=5)) == -2            # T mismatch
     assert f(twell_c(), hybrid_c(K=0)) == -2
     assert f(twell_c(), hybrid_c(K=300)) == -2          # K > d_ff
@@ -103,7 +108,7 @@ def test_bwd_validation(L):
     def f(ws=FAKE, nbytes=None, dm=64, dx=FAKE, hh=h, dt=tw.TWELL_BF16):
         return L.hybrid_ffn_bwd(dt, FAKE, FAKE, ctypes.byref(hh), FAKE, FAKE, FAKE, dm, dx,
                                 FAKE, FAKE, FAKE, ws, need if nbytes is None else nbytes,
-                                None, None)
+                                None, None, None)
     assert f(nbytes=need - 1) == -5
     assert f(ws=0) == -5
     assert f(dx=0) == -1
