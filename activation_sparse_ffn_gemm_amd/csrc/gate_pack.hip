@@ -5,13 +5,17 @@
 //
 // One workgroup computes a 192-token x 256-neuron block of g: two TwELL
 // column tiles for 192 rows, g never leaving the registers. Eight wave64s (two
-// per SIMD, so one computes while the other waits on memory) split it 2 x 4;
-// each wave owns 96 rows x 64 columns = 3 x 2 MFMA 32x32 blocks. The tile
-// keeps 192 x 256 x 64 MACs per 56 KB K step (114 flop per byte of L2
-// traffic) and, for 4096 tokens x 2816 neurons, gives 242 workgroups: one
-// round on 256 CUs. K steps of 128 bytes per row (64 bf16 / 32 f32) go
-// through double-buffered, XOR-swizzled LDS, the next step's global loads in
-// flight during the current step's MFMAs.
+// per SIMD) split it 2 x 4; each wave owns 96 rows x 64 columns = 3 x 2 MFMA
+// 32x32 blocks. For 4096 tokens x 2816 neurons this gives 242 workgroups, one
+// round on 256 CUs.
+//
+// Operands stream through LDS in K steps of 64 bytes per row (32 bf16 /
+// 16 f32), NST steps resident at once: the loads of step k + NST - 1 are
+// issued while step k is computed. The loads go straight from global memory
+// to LDS (4 bytes per lane, no register staging); each wave waits only for its
+// own loads of the step it is about to use, then a barrier covers the others'.
+// LDS rows are XOR-swizzled in 16-byte chunks so that the 16 lanes a 128-bit
+// fragment read serves per cycle hit 16 distinct groups of the 64 banks.
 //
 // Epilogue, per row: one ballot per 32-column block gives the g > 0 mask;
 // popcounts give the count in each wave's 64 columns, which the two waves of a
@@ -22,10 +26,43 @@
 namespace {
 
 constexpr int BM = 192, BN = 256;
-constexpr int ROWB = 128; // bytes of one LDS row per K step
+constexpr int ROWB = 64; // bytes of one LDS row per K step
 constexpr int NT = 512;
+constexpr int NST = 4; // K steps resident in LDS
 constexpr int WM = 96, WN = 64, MI = 3, NI = 2; // per wave: 96 x 64 = 3 x 2 blocks of 32x32
-constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT; // 16-byte chunks per thread per step
+constexpr int STAGE = (BM + BN) * ROWB;          // bytes per K step
+constexpr int BLK = 256;                          // bytes one wave's 4-byte-lane load writes
+constexpr int NBLK = STAGE / BLK, WBLK = NBLK / (NT / 64); // 256-byte blocks: total, per wave
+static_assert(NBLK % (NT / 64) == 0, "blocks must split evenly over the waves");
+static_assert(BM % 4 == 0, "a block must not straddle the two operands");
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// One 4-byte-per-lane load from global memory straight into LDS: lane l's word
+// lands at LDS byte lds + 4 l. Written as assembly so that the compiler, which
+// would otherwise make every LDS read and barrier wait for all such loads in
+// flight, leaves the waiting to the explicit vmcnt waits of the K loop.
+DEVI void lds_dma4(const uint8_t *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(g), "s"(lds)
+                 : "m0");
+}
+
+// Byte offset of 16-byte chunk c (0..3) of LDS row r (64-byte rows). Rows
+// r, r+4, r+8, r+12 start on the same bank; XOR-ing the chunk with (r / 4) % 4
+// separates them, so 16 consecutive rows at one chunk use 16 distinct groups.
+DEVI int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// Wait until at most n of this wave's vector-memory operations are pending
+// (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt
+// at their maximum, i.e. not waited on).
+template <int n> DEVI void wait_vm()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int DT>
 __global__ __launch_bounds__(NT, 1) void gate_pack_kernel(
@@ -35,8 +72,7 @@ __global__ __launch_bounds__(NT, 1) void gate_pack_kernel(
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t L[NST][STAGE];
     __shared__ int cnt_lds[BM][4];
 
     // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD k takes the
@@ -47,53 +83,36 @@ __global__ __launch_bounds__(NT, 1) void gate_pack_kernel(
     const int tile = (blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
     if (tile >= total)
         return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int half = lane >> 5, l32 = lane & 31;
     const int m0 = (tile / n_nt) * BM, n0 = (tile % n_nt) * BN;
     const int nt = dff / TWELL_TILE_C;
     const size_t rowbytes = (size_t)dm * esz;
+    const int nk = (int)(rowbytes / ROWB);
 
-    // Two register stages: the global loads of step k + 2 are issued while
-    // step k is computed, so each load has two steps of MFMA work to land.
-    uint4 ra0[A_CH], rb0[B_CH], ra1[A_CH], rb1[B_CH];
-    // Loads are branch-free (rows past the operand are clamped, then zeroed on
-    // the way into LDS) so the compiler can keep two steps of loads in flight.
-    const uint8_t *pa[A_CH], *pb[B_CH];
-    bool oka[A_CH], okb[B_CH];
+    // This wave's 256-byte blocks of a stage: block b holds tile rows
+    // 4b .. 4b+3 (A rows, then B rows). Lane l writes bytes 4l .. 4l+3 of it,
+    // i.e. word l&3 of swizzled chunk (l&15)>>2 of row 4b + l/16, so it loads
+    // that word of the source chunk the swizzle maps there. Rows past the
+    // operand read a clamped row: they only feed outputs that are not stored.
+    const uint8_t *src[WBLK];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int q = tid + NT * i, r = q >> 3, c = q & 7;
-        oka[i] = m0 + r < T;
-        pa[i] = x + (size_t)min(m0 + r, T - 1) * rowbytes + c * 16;
+    for (int i = 0; i < WBLK; ++i) {
+        const int b = wave * WBLK + i;
+        const int r = 4 * b + (lane >> 4);
+        const int c = ((lane & 15) >> 2) ^ ((r >> 2) & 3);
+        const uint8_t *row = r < BM ? x + (size_t)min(m0 + r, T - 1) * rowbytes
+                                    : wg + (size_t)min(n0 + r - BM, dff - 1) * rowbytes;
+        src[i] = row + c * 16 + (lane & 3) * 4;
     }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8 *)&L[0][0] + wave * WBLK * BLK;
+    auto issue = [&](int kt) {
+        const uint32_t dst = lds0 + (kt % NST) * STAGE;
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int q = tid + NT * i, r = q >> 3, c = q & 7;
-        okb[i] = n0 + r < dff;
-        pb[i] = wg + (size_t)min(n0 + r, dff - 1) * rowbytes + c * 16;
-    }
-    auto gload = [&](int kt, uint4 (&ra)[A_CH], uint4 (&rb)[B_CH]) {
-        const size_t koff = (size_t)kt * ROWB;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            ra[i] = ldg16(pa[i] + koff);
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            rb[i] = ldg16(pb[i] + koff);
-    };
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-    auto sstore = [&](int b, const uint4 (&ra)[A_CH], const uint4 (&rb)[B_CH]) {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int q = tid + NT * i;
-            *(uint4 *)(As[b] + mt::swz(q >> 3, q & 7)) = oka[i] ? ra[i] : z4;
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int q = tid + NT * i;
-            *(uint4 *)(Bs[b] + mt::swz(q >> 3, q & 7)) = okb[i] ? rb[i] : z4;
-        }
+        for (int i = 0; i < WBLK; ++i)
+            lds_dma4(src[i] + (size_t)kt * ROWB, dst + i * BLK);
     };
 
     floatx16_t acc[MI][NI];
@@ -105,46 +124,38 @@ __global__ __launch_bounds__(NT, 1) void gate_pack_kernel(
             for (int e = 0; e < 16; ++e)
                 acc[mi][ni][e] = 0.f;
 
-    auto compute = [&](int b) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nk)
+            issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's loads of step kt are done once at most the later steps' pend
+        const int later = min(nk - 1, kt + NST - 2) - kt;
+        if (later >= 2)
+            wait_vm<2 * WBLK>();
+        else if (later == 1)
+            wait_vm<WBLK>();
+        else
+            wait_vm<0>();
+        __syncthreads(); // all loads of step kt are in; step kt - 1 is consumed
+        if (kt + NST - 1 < nk)
+            issue(kt + NST - 1);
+        const uint8_t *As = L[kt % NST], *Bs = As + BM * ROWB;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
             uint4 fa[MI], fb[NI];
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
-                fa[mi] = *(const uint4 *)(As[b] + mt::swz(wm * WM + mi * 32 + l32, 2 * g + half));
+                fa[mi] = *(const uint4 *)(As + swz(wm * WM + mi * 32 + l32, 2 * g + half));
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
-                fb[ni] = *(const uint4 *)(Bs[b] + mt::swz(wn * WN + ni * 32 + l32, 2 * g + half));
+                fb[ni] = *(const uint4 *)(Bs + swz(wn * WN + ni * 32 + l32, 2 * g + half));
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
                     mt::mma_group<DT>(acc[mi][ni], fa[mi], fb[ni]);
         }
-    };
-    // step kt: fetch step kt + 2 into `ld` (which held step kt, already in
-    // LDS), compute step kt from LDS buffer b, then put step kt + 1 (held in
-    // `st`) into the other LDS buffer
-    auto iter = [&](int kt, int nk, int b, uint4 (&lda)[A_CH], uint4 (&ldb)[B_CH],
-                    const uint4 (&sta)[A_CH], const uint4 (&stb)[B_CH]) {
-        if (kt + 2 < nk)
-            gload(kt + 2, lda, ldb);
-        compute(b);
-        if (kt + 1 < nk)
-            sstore(b ^ 1, sta, stb);
-        __syncthreads();
-    };
-
-    const int nk = (int)(rowbytes / ROWB);
-    gload(0, ra0, rb0);
-    sstore(0, ra0, rb0);
-    if (nk > 1)
-        gload(1, ra1, rb1);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        iter(kt, nk, 0, ra0, rb0, ra1, rb1);
-        if (kt + 1 < nk)
-            iter(kt + 1, nk, 1, ra1, rb1, ra0, rb0);
     }
 
     // ---- epilogue: waves wn and wn ^ 1 share TwELL tile j = n0/128 + wn/2

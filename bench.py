@@ -36,6 +36,50 @@ WORKLOADS = {
 }
 
 
+# Source files whose text decides each kernel's memory traffic: counters taken
+# on other sources describe another kernel and are not reported.
+CSRC = os.path.join(ROOT, "activation_sparse_ffn_gemm_amd", "csrc")
+KERNEL_SOURCES = {
+    "gate_pack_kernel": "gate_pack.hip", "ffn_fwd_kernel": "ffn_fwd.hip",
+    "hyb_rows_kernel": "to_hybrid.hip", "hyb_slots_kernel": "to_hybrid.hip",
+    "hyb_dense_kernel": "to_hybrid.hip",
+}
+
+
+def kernel_sources_sha256(kernel):
+    """sha256 over the kernel's .hip file and every shared header."""
+    import hashlib
+    h = hashlib.sha256()
+    names = [KERNEL_SOURCES.get(kernel, "bwd.hip")]
+    names += sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
+    for f in names:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
+    reads for a plain copy of known size), or None with the reason."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as fh:
+        rec = json.load(fh)
+    k = rec.get("kernels", {}).get(kernel)
+    if rec.get("workload") != workload or k is None:
+        return None, "no counters for this kernel and workload"
+    if k["sources_sha256"] != kernel_sources_sha256(kernel):
+        return None, "kernel sources changed since the counters were taken"
+    cal = rec["copy_calibration"]
+    sf = cal["bytes"] / (cal["fetch_kib"] * 1024.0)
+    sw = cal["bytes"] / (cal["write_kib"] * 1024.0)
+    b = k["fetch_kib"] * 1024.0 * sf + k["write_kib"] * 1024.0 * sw
+    return round(b), (f"rocprofv3 FETCH_SIZE {k['fetch_kib']:.0f} KiB x {sf:.3f} + WRITE_SIZE "
+                      f"{k['write_kib']:.0f} KiB x {sw:.3f} per launch (copy-calibrated)")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -137,21 +181,31 @@ def main():
                 kern_ms[name] = kern_ms.get(name, 0.0) + ms / a.steps
                 stage_ms[k] += ms / a.steps
 
-    # ---- roofline of the dominant kernel: algorithmic work of one launch
-    row_b = dm * 2                        # one bf16 row of d_model
-    twell_b = T * (dff // 128) * 4 + nnz * 4
+    # ---- roofline of each kernel: algorithmic work of one launch. Bytes count
+    # every row a kernel's algorithm reads (a gathered row once per use, as
+    # the gather performs it), the index/value arrays it reads and what it
+    # writes; flops count the dense contractions' 2 m n k.
+    n_t = dff // 128
+    row_b = dm * 2                               # one bf16 row of d_model
+    T_ell = T - n_ovf
+    twell_b = T * n_t * 4 + nnz * 4              # count + (int16 col, bf16 val) per entry
     work = {
-        "gate_pack_kernel": ("mfma", 2.0 * T * dm * dff, "2 d_model d_ff flop per token"),
-        "fwd_up_kernel": ("hbm", nnz * row_b + T * row_b + twell_b + nnz * 4,
-                          "one wu_t row per nonzero + x + TwELL + a"),
-        "fwd_down_kernel": ("hbm", nnz * row_b + twell_b + nnz * 4 + T * dm * 4,
-                            "one wd row per nonzero + TwELL + a + y"),
-        "bwd_sddmm_kernel": ("hbm", nnz_ell * 2 * row_b + 2 * T * row_b + nnz_ell * 20,
-                             "wu_t and wd rows per ELL nonzero + x, dy + coefficients"),
-        "bwd_dx_kernel": ("hbm", nnz_ell * 2 * row_b + nnz_ell * 10 + T * dm * 4,
-                          "wu_t and wg_t rows per ELL nonzero + coefficients + dx"),
-        "bwd_dw_kernel": ("hbm", nnz_ell * 2 * row_b + nnz_ell * 16 + 3 * dff * dm * 4,
-                          "x and dy rows per ELL nonzero + coefficients + 3 dW"),
+        "gate_pack_kernel": ("mfma", 2.0 * T * dm * dff,
+                             "2 d_model d_ff flop per token (TwELL written in the epilogue)"),
+        "ffn_fwd_kernel": ("hbm", nnz * 2 * row_b + T * row_b + T * dm * 4 + twell_b,
+                           "per nonzero one wu_t row + one wd row; x, y, TwELL once"),
+        "hyb_rows_kernel": ("hbm", T * n_t * 4 + nnz * 4 + nnz_ell * 4 + 8 * T,
+                            "TwELL counts + entries read; ELL entries, row_nnz written"),
+        "hyb_dense_kernel": ("hbm", (nnz - nnz_ell) * 4 + n_ovf * dff * 2,
+                             "backup rows' entries read, dense backup written"),
+        "bwd_neuron_kernel": ("hbm", nnz_ell * (2 * row_b + 4 + 2 + 8) + dff * (2 * row_b + 3 * dm * 4),
+                              "per ELL nonzero one x row + one dy row + CSC slot, h, du/dg; "
+                              "per neuron wu_t + wd rows and three fp32 dW rows"),
+        "bwd_dx_kernel": ("hbm", nnz_ell * (2 * row_b + 10) + 8 * T + T_ell * dm * 4,
+                          "per ELL nonzero one wu_t row + one wg_t row + col, du, dg; dx rows"),
+        "ovf_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "u_O and da_O: 2 GEMMs"),
+        "ovf_dx_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "dx_O: 2 GEMMs"),
+        "ovf_dw_kernel": ("mfma", 3 * 2.0 * n_ovf * dm * dff, "dW_g, dW_u, dW_d += : 3 GEMMs"),
     }
     peak = {"mfma": BF16_PEAK_TFLOPS, "hbm": HBM_PEAK_GBS}
     unit = {"mfma": "TFLOP/s", "hbm": "GB/s"}
@@ -159,18 +213,20 @@ def main():
     per_kernel = {}
     for name, ms in kern_ms.items():
         ent = {"ms": round(ms, 4)}
-        if name in work:
+        if name in work and work[name][1] > 0:
             b, wk, desc = work[name]
             ach = wk / (ms * 1e-3) / scale[b]
             ent.update(bound=b, achieved=round(ach, 1), unit=unit[b],
                        frac=round(ach / peak[b], 4), work=wk, work_unit=desc)
         per_kernel[name] = ent
-    dom = max((k for k in kern_ms if k in work), key=lambda k: kern_ms[k])
+    dom = max((k for k in kern_ms if k in work and work[k][1] > 0), key=lambda k: kern_ms[k])
     b, wk, desc = work[dom]
     ach = wk / (kern_ms[dom] * 1e-3) / scale[b]
+    traffic, traffic_note = measured_traffic(dom, a.workload)
     roofline = {"kernel": dom, "bound": b, "achieved": round(ach, 1), "peak": peak[b],
-                "unit": unit[b], "frac": round(ach / peak[b], 4), "traffic": None,
-                "launch_ms": round(kern_ms[dom], 4), "work_per_launch": wk, "work_unit": desc}
+                "unit": unit[b], "frac": round(ach / peak[b], 4), "traffic": traffic,
+                "traffic_note": traffic_note, "launch_ms": round(kern_ms[dom], 4),
+                "work_per_launch": wk, "work_unit": desc}
 
     # ---- dense bf16 layer, same shapes, torch (hipBLASLt) as a timed black box
     dense = None
@@ -238,7 +294,7 @@ def main():
                          f"backward) over all {Ts} tokens of the batch, float64, {el:.1f} s"}
 
     out = {
-        "metric": "FFN-layer tokens/s at 1% gate density (fwd + TwELL->hybrid + bwd step)",
+        "metric": "FFN-layer tokens/s at 1% gate density vs dense bf16; % MFMA/HBM peak",
         "value": round(T / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -246,7 +302,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs and weights, gate offset "
                                  "for the target density)",
-        "config": {"workload": a.workload, "T": T, "d_model": dm, "d_ff": dff,
+        "config": {"workload": a.workload, "step": "gate GEMM + TwELL pack, fused up/down, "
+                   "TwELL->hybrid, hybrid backward (dx, dW_g, dW_u, dW_d)", "T": T, "d_model": dm, "d_ff": dff,
                    "density": w.density, "measured_density": round(nnz / (T * dff), 5),
                    "nnz": nnz, "nnz_ell": nnz_ell, "n_ovf": n_ovf, "twell_width": w.width,
                    "K": w.K, "max_ovf": w.max_ovf},
