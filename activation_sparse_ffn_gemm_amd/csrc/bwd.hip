@@ -175,8 +175,8 @@ __global__ __launch_bounds__(NT) void csc_fill_kernel(
 // ------------------------------------------------------------ 4. neuron pass
 // NW words per lane cover the whole row (dots); the wave accumulates the NWP
 // words of part `part` (PARTS = NW / NWP parts, one per blockIdx.y).
-template <int DT, int NW, int NWP, int G>
-__global__ __launch_bounds__(NT) void bwd_neuron_kernel(
+template <int DT, int NW, int NWP, int G, int S>
+__global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
     const int32_t *__restrict__ colptr, const int32_t *__restrict__ csc,
     const void *__restrict__ ell_val, int T, int K, int dff, const uint8_t *__restrict__ x,
     const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd,
@@ -187,11 +187,10 @@ __global__ __launch_bounds__(NT) void bwd_neuron_kernel(
     using R = Row<DT, NW>;
     using RP = Row<DT, NWP>;
     constexpr int EPW = R::EPW;
-    const int lane = threadIdx.x & 63;
-    const int i = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (i >= dff)
-        return;
-    const int part = blockIdx.y;
+    constexpr int PL = NWP * 64 * EPW; // elements of one part of a row
+    __shared__ __attribute__((aligned(16))) float red[S > 1 ? S : 1][S > 1 ? PL : 4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int i = blockIdx.x, part = blockIdx.y;
     const R geo(dm, lane, 0);
     const RP pgeo(dm, lane, part);
     const long TK = (long)T * K;
@@ -202,10 +201,13 @@ __global__ __launch_bounds__(NT) void bwd_neuron_kernel(
     pgeo.zero_f(ad);
     pgeo.zero_f(au);
     pgeo.zero_f(ag);
+    // The neuron's entries are dealt to the S waves round-robin (entry p0 + w,
+    // p0 + w + S, ...), so the chain of dependent gathers each wave walks is
+    // 1/S of the list; the S partial dW rows are summed in LDS below.
     const int p0 = colptr[i], p1 = colptr[i + 1];
-    for (int pb = p0; pb < p1; pb += 64) {
-        // lane L prefetches entry pb + L: its ELL slot, row and stored h
-        const int p = pb + lane;
+    for (int pb = p0 + wv; pb < p1; pb += 64 * S) {
+        // lane L prefetches this wave's entry pb + S L: its ELL slot, row and h
+        const int p = pb + S * lane;
         int idx = -1;
         float h = 0.f;
         if (p < p1) {
@@ -216,63 +218,88 @@ __global__ __launch_bounds__(NT) void bwd_neuron_kernel(
                 idx = -1;
         }
         const int tt = idx >= 0 ? idx / K : 0;
-        const int m = min(64, p1 - pb);
+        const int m = min(64, (p1 - pb + S - 1) / S);
+        // stream the m entries through G register buffers: the x and dy rows
+        // of entry e + G are requested as soon as entry e has been used
+        uint32_t vx[G][NW], vd[G][NW];
+        auto fetch = [&](int e, uint32_t (&xr)[NW], uint32_t (&dr)[NW]) {
+            const int tr = bcast(tt, min(e, m - 1));
+            geo.load_w(x, tr, xr);
+            geo.load_w(dy, tr, dr);
+        };
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            fetch(g, vx[g], vd[g]);
         for (int e0 = 0; e0 < m; e0 += G) {
-            uint32_t vx[G][NW], vd[G][NW];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int tr = bcast(tt, min(e0 + g, m - 1));
-                geo.load_w(x, tr, vx[g]);
-                geo.load_w(dy, tr, vd[g]);
-            }
+                const int e = e0 + g;
+                const float u = wave_sum(geo.dotw(vx[g], wuw));
+                const float da = wave_sum(geo.dotw(vd[g], wdw));
+                if (e < m) { // uniform
+                    const float hh = bcast(h, e);
+                    const float a = hh * u, du = da * hh, dg = hh != 0.f ? da * u : 0.f;
+                    // the lane that owns this entry keeps du, dg for the dx pass
+                    if (lane == e && idx >= 0) {
+                        coef[idx] = du;
+                        coef[TK + idx] = dg;
+                    }
+                    // this wave's part of the row: words c = part * NWP + c2
+                    // (static indices; the part test is uniform across the wave)
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float su = 0.f, sd = 0.f;
+                    for (int c = 0; c < NW; ++c) {
+                        if (c / NWP != part)
+                            continue;
+                        const int c2 = c % NWP;
+                        float xv[EPW], dv[EPW];
+                        geo.widen(vx[g][c], xv);
+                        geo.widen(vd[g][c], dv);
 #pragma unroll
-                for (int c = 0; c < NW; ++c) {
-                    float a1[EPW], b1[EPW], a2[EPW], b2[EPW];
-                    geo.widen(vx[g][c], a1);
-                    geo.widen(wuw[c], b1);
-                    geo.widen(vd[g][c], a2);
-                    geo.widen(wdw[c], b2);
-#pragma unroll
-                    for (int e = 0; e < EPW; ++e) {
-                        su += a1[e] * b1[e];
-                        sd += a2[e] * b2[e];
+                        for (int q = 0; q < EPW; ++q) {
+                            ad[c2][q] += a * dv[q];
+                            au[c2][q] += du * xv[q];
+                            ag[c2][q] += dg * xv[q];
+                        }
                     }
                 }
-                const float u = wave_sum(su), da = wave_sum(sd);
-                const bool in = e0 + g < m;
-                const float hh = in ? bcast(h, e0 + g) : 0.f;
-                const float a = hh * u, du = da * hh, dg = hh != 0.f ? da * u : 0.f;
-                // the lane that owns this entry keeps du, dg for the dx pass
-                if (in && lane == e0 + g && idx >= 0) {
-                    coef[idx] = du;
-                    coef[TK + idx] = dg;
-                }
-                // this wave's part of the row: words c = part * NWP + c2 (static
-                // indices; the part test is uniform across the wave)
-#pragma unroll
-                for (int c = 0; c < NW; ++c) {
-                    if (c / NWP != part)
-                        continue;
-                    const int c2 = c % NWP;
-                    float xv[EPW], dv[EPW];
-                    geo.widen(vx[g][c], xv);
-                    geo.widen(vd[g][c], dv);
-#pragma unroll
-                    for (int e = 0; e < EPW; ++e) {
-                        ad[c2][e] += a * dv[e];
-                        au[c2][e] += du * xv[e];
-                        ag[c2][e] += dg * xv[e];
-                    }
-                }
+                fetch(e + G, vx[g], vd[g]);
             }
         }
     }
-    pgeo.store_f(dwd, i, ad);
-    pgeo.store_f(dwu, i, au);
-    pgeo.store_f(dwg, i, ag);
+    // sum the S partial rows in a fixed order (wave 0 first) and write each
+    // dW row once; element q of the part is word q / EPW, half q % EPW
+    const int n_el = dm - part * PL < PL ? dm - part * PL : PL;
+    auto reduce_store = [&](const float (&acc)[NWP][EPW], float *out) {
+#pragma unroll
+        for (int c = 0; c < NWP; ++c)
+#pragma unroll
+            for (int e = 0; e < EPW; ++e)
+                red[wv][(c * 64 + lane) * EPW + e] = acc[c][e];
+        __syncthreads();
+        float *o = out + (size_t)i * dm + (size_t)part * PL;
+        for (int q = 4 * threadIdx.x; q < n_el; q += 4 * 64 * S) {
+            float4 sum = *(const float4 *)&red[0][q];
+#pragma unroll
+            for (int w = 1; w < S; ++w) {
+                const float4 v = *(const float4 *)&red[w][q];
+                sum.x += v.x;
+                sum.y += v.y;
+                sum.z += v.z;
+                sum.w += v.w;
+            }
+            *(float4 *)(o + q) = sum;
+        }
+        __syncthreads();
+    };
+    if constexpr (S == 1) {
+        pgeo.store_f(dwd, i, ad);
+        pgeo.store_f(dwu, i, au);
+        pgeo.store_f(dwg, i, ag);
+    } else {
+        reduce_store(ad, dwd);
+        reduce_store(au, dwu);
+        reduce_store(ag, dwg);
+    }
 }
 
 // ------------------------------------------------------------ 5. dx
@@ -308,19 +335,26 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
             }
         }
         const int m = min(64, n - s0);
+        // stream the m entries through G register buffers: the rows of entry
+        // e + G are requested as soon as entry e has been used
+        uint32_t vu[G][NW], vg[G][NW];
+        auto fetch = [&](int e, uint32_t (&u)[NW], uint32_t (&g)[NW]) {
+            const int c = bcast(ci, min(e, m - 1));
+            geo.load_w(wu, c, u);
+            geo.load_w(wg, c, g);
+        };
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            fetch(g, vu[g], vg[g]);
         for (int e0 = 0; e0 < m; e0 += G) {
-            uint32_t vu[G][NW], vg[G][NW];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const int c = bcast(ci, min(e0 + g, m - 1));
-                geo.load_w(wu, c, vu[g]);
-                geo.load_w(wg, c, vg[g]);
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const bool in = e0 + g < m;
-                geo.axpy(acc, in ? bcast(cu, e0 + g) : 0.f, vu[g]);
-                geo.axpy(acc, in ? bcast(cg, e0 + g) : 0.f, vg[g]);
+                const int e = e0 + g;
+                if (e < m) { // uniform
+                    geo.axpy(acc, bcast(cu, e), vu[g]);
+                    geo.axpy(acc, bcast(cg, e), vg[g]);
+                }
+                fetch(e + G, vu[g], vg[g]);
             }
         }
     }
@@ -533,7 +567,11 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     const uint8_t *xb = (const uint8_t *)x, *dyb = (const uint8_t *)dy;
     const int rgroups = (T + NT / 64 - 1) / (NT / 64), ngroups = (dff + NT / 64 - 1) / (NT / 64);
     constexpr int NWN = NW < 16 ? NW : 16;          // neuron pass: accumulated words per lane
-    constexpr int GN = NW <= 8 ? 4 : (NW <= 16 ? 2 : 1);
+    // entries in flight per wave (neuron pass, dx pass); waves sharing one
+    // neuron's entries (narrow rows only: wide rows leave no registers for it)
+    constexpr int GN = NW <= 16 ? 2 : 1;
+    constexpr int GD = NW <= 4 ? 4 : 2;
+    constexpr int NSPLIT = NW <= 8 ? 4 : 1;
     constexpr int NWP = NW < ACC_NW ? NW : ACC_NW; // dx pass: words per lane of one part
     const int parts = row_parts<DT>(dm, NWP);
 
@@ -552,12 +590,12 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                            status);
         tm.mark("csc_fill_kernel");
     }
-    hipLaunchKernelGGL((bwd_neuron_kernel<DT, NW, NWN, GN>), dim3(ngroups, NW / NWN), dim3(NT),
-                       0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
+    hipLaunchKernelGGL((bwd_neuron_kernel<DT, NW, NWN, GN, NSPLIT>), dim3(dff, NW / NWN),
+                       dim3(64 * NSPLIT), 0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
                        (const uint8_t *)wd, dm, coef, dwg, dwu, dwd);
     tm.mark("bwd_neuron_kernel");
     if (T > 0) {
-        hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, 8>), dim3(rgroups, parts), dim3(NT), 0, s,
+        hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, GD>), dim3(rgroups, parts), dim3(NT), 0, s,
                            h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dff,
                            (const uint8_t *)wu, (const uint8_t *)wg, dm, dx);
         tm.mark("bwd_dx_kernel");

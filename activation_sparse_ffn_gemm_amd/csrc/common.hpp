@@ -9,6 +9,7 @@
 #include "twell.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
@@ -56,12 +57,25 @@ template <> struct elem<TWELL_F32> {
 DEVI uint4 ldg16(const void *p) { return *(const uint4 *)p; }
 
 // Sum over the 64 lanes of a wavefront; every lane gets the total.
+// Within each row of 16 lanes the sum is formed with DPP lane moves (no LDS
+// traffic): swap neighbours (quad_perm 1,0,3,2), swap pairs (2,3,0,1), mirror
+// each half-row, mirror the row. Every lane then holds its row's sum; the four
+// row sums are read into scalar registers and added in a fixed order.
+template <int CTRL> DEVI float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 DEVI float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v); // row_half_mirror
+    v += dpp_mov<0x140>(v); // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 DEVI int wave_incl_scan(int v, int lane)
@@ -90,85 +104,9 @@ DEVI void raise_status(int32_t *status, int bits)
         atomicOr(status, bits);
 }
 
-// ---- XCD-aware work split. MI355X has 8 XCDs, each with its own L2, and
-// hands consecutive workgroup ids to the XCDs in turn, so workgroup b runs on
-// XCD b % 8. Kernels that gather weight or activation rows give each XCD one
-// eighth of the data (a range of neuron tiles, or a slice of d_model
-// columns) so that its share stays resident in that XCD's L2.
+// MI355X has 8 XCDs, each with its own L2, and hands consecutive workgroup
+// ids to the XCDs in turn: workgroup b runs on XCD b % 8.
 constexpr int NXCD = 8;
-
-// Slice of d_model columns for XCD-split gathers: each lane of a wave owns NE
-// consecutive elements (VB bytes), a wave covers 64 * NE columns.
-template <int DT, int VB> struct Vec {
-    static constexpr int NW = VB / 4;
-    static constexpr int NE = DT == TWELL_BF16 ? 2 * NW : NW;
-    uint32_t w[NW];
-    DEVI void load(const uint8_t *p)
-    {
-        if constexpr (NW == 1) {
-            w[0] = *(const uint32_t *)p;
-        } else if constexpr (NW == 2) {
-            const uint2 v = *(const uint2 *)p;
-            w[0] = v.x; w[1] = v.y;
-        } else if constexpr (NW == 3) {
-            const uint3 v = *(const uint3 *)p;
-            w[0] = v.x; w[1] = v.y; w[2] = v.z;
-        } else {
-            const uint4 v = *(const uint4 *)p;
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-        }
-    }
-    DEVI void zero()
-    {
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-            w[i] = 0;
-    }
-    DEVI void widen(float *o) const
-    {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            if constexpr (DT == TWELL_BF16) {
-                o[2 * i] = bf16_lo(w[i]);
-                o[2 * i + 1] = bf16_hi(w[i]);
-            } else {
-                o[i] = __uint_as_float(w[i]);
-            }
-        }
-    }
-};
-
-// Bytes per lane (4, 8, 12 or 16) of a d_model slice: the narrowest whose
-// slices number at most NXCD (12 only when it divides d_model evenly).
-inline int slice_bytes(int dt, int dm)
-{
-    const int esz = dt == TWELL_BF16 ? 2 : 4;
-    for (int vb : {4, 8}) {
-        const int cols = 64 * vb / esz;
-        if ((dm + cols - 1) / cols <= NXCD)
-            return vb;
-    }
-    const int c12 = 64 * 12 / esz;
-    if (dm % c12 == 0 && dm / c12 <= NXCD)
-        return 12;
-    return 16;
-}
-
-DEVI void store_f32(float *dst, const float *v, int n)
-{
-    if (n % 4 == 0) {
-#pragma unroll
-        for (int q = 0; q < n / 4; ++q)
-            ((float4 *)dst)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-    } else if (n % 2 == 0) {
-#pragma unroll
-        for (int q = 0; q < n / 2; ++q)
-            ((float2 *)dst)[q] = make_float2(v[2 * q], v[2 * q + 1]);
-    } else {
-        for (int q = 0; q < n; ++q)
-            dst[q] = v[q];
-    }
-}
 
 // ---- optional kernel timing of one API call (see twell_timing_t)
 struct Timer {

@@ -37,17 +37,20 @@ DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *
         const size_t src = ((size_t)t * nt + j) * W;
         for (int p0 = 0; p0 < tot; p0 += LIST) {
             for (int s0 = max(0, p0 - excl); s0 < n && excl + s0 < p0 + LIST; s0 += 8) {
+                // branch-free: every lane issues its 8 (or 16) loads before any
+                // is used; slots past the tile's width re-read its last slot
                 int c[8];
                 float v[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const bool in = s0 + u < n;
-                    c[u] = in ? col[src + s0 + u] : 0;
-                    if constexpr (VALS)
-                        v[u] = in ? E::load1(val, src + s0 + u) : 0.f;
-                    else
-                        v[u] = 0.f;
+                    const size_t q = src + min(s0 + u, W - 1);
+                    c[u] = col[q];
+                    v[u] = VALS ? E::load1(val, q) : 0.f;
                 }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u >= n)
+                        c[u] = 0, v[u] = 0.f;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int e = excl + s0 + u - p0;
@@ -92,33 +95,31 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
     const RP part(dm, lane, blockIdx.y);
     uint32_t xw[NW];
     geo.load_w(x, t, xw);
-    float xr[NW][R::EPW];
-#pragma unroll
-    for (int c = 0; c < NW; ++c)
-        geo.widen(xw[c], xr[c]);
     float acc[NWP][RP::EPW];
     part.zero_f(acc);
     for_row_entries<DT, true>(count, col, val, t, nt, W, 0, nt, nt * TWELL_TILE_C, lane,
                               lslot[wv], lcol[wv], lval[wv], status, [&](int ne) {
-        for (int b0 = 0; b0 < ne; b0 += 64) {
-            const int e = b0 + lane;
-            const int mci = e < ne ? lcol[wv][e] : 0;
-            const float mh = e < ne ? lval[wv][e] : 0.f;
-            const int m = min(64, ne - b0);
-            for (int e0 = 0; e0 < m; e0 += G) {
-                uint32_t vu[G][NW], vd[G][NWP];
+        // Stream the staged entries through G register buffers: the rows of
+        // entry e + G are requested as soon as entry e has been used, so G
+        // entries' gathers stay in flight while the wave computes. Requests
+        // past the list re-read its last entry and are not used.
+        uint32_t vu[G][NW], vd[G][NWP];
+        auto fetch = [&](int e, uint32_t (&u)[NW], uint32_t (&d)[NWP]) {
+            const int ci = lcol[wv][min(e, ne - 1)];
+            geo.load_w(wu, ci, u);
+            part.load_w(wd, ci, d);
+        };
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int ci = bcast(mci, min(e0 + g, m - 1));
-                    geo.load_w(wu, ci, vu[g]);
-                    part.load_w(wd, ci, vd[g]);
-                }
+        for (int g = 0; g < G; ++g)
+            fetch(g, vu[g], vd[g]);
+        for (int e0 = 0; e0 < ne; e0 += G) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float u = wave_sum(geo.dot(xr, vu[g]));
-                    const float a = e0 + g < m ? bcast(mh, e0 + g) * u : 0.f;
-                    part.axpy(acc, a, vd[g]);
-                }
+            for (int g = 0; g < G; ++g) {
+                const int e = e0 + g;
+                const float u = wave_sum(geo.dotw(xw, vu[g]));
+                if (e < ne) // uniform
+                    part.axpy(acc, lval[wv][e] * u, vd[g]);
+                fetch(e + G, vu[g], vd[g]);
             }
         }
     });
@@ -130,7 +131,7 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
                int32_t *status, hipStream_t s)
 {
     constexpr int NWP = NW < 16 ? NW : 16; // whole rows up to d_model 2048 (bf16)
-    constexpr int G = NW <= 4 ? 8 : (NW <= 8 ? 4 : (NW <= 16 ? 2 : 1));
+    constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
     const int parts = row_parts<DT>(dm, NWP);
     const int groups = (h->T + NT / 64 - 1) / (NT / 64);
     hipLaunchKernelGGL((ffn_fwd_kernel<DT, NW, NWP, G>), dim3(groups, parts), dim3(NT), 0, s,

@@ -10,7 +10,11 @@
 
 #include "common.hpp"
 
-constexpr int ACC_NW = 8; // words per lane in kernels that hold a row of accumulators
+constexpr int ACC_NW = 8;
+
+// Fourth word of a raw buffer descriptor on gfx9-family parts: 32-bit data
+// format (needed for the range check of untyped loads), everything else 0.
+constexpr int BUF_DWORD3 = 0x00020000; // words per lane in kernels that hold a row of accumulators
 
 template <int DT, int NW> struct Row {
     static constexpr int EPW = DT == TWELL_BF16 ? 2 : 1; // elements per word
@@ -22,13 +26,20 @@ template <int DT, int NW> struct Row {
     DEVI bool in(int c) const { return base + c * 64 + lane < ndw; }
     DEVI int word(int c) const { return base + c * 64 + lane; }
 
-    // words of row r of a [rows][d_model] matrix
+    // Words of row r of a [rows][d_model] matrix. The row index must be the
+    // same in every lane: the loads go through a buffer descriptor built in
+    // scalar registers for this row (and part), so every load needs only the
+    // lane's byte offset plus an immediate, and lanes past the end of the row
+    // read 0 from the descriptor's range check (no branches, no clamping).
     DEVI void load_w(const uint8_t *m, int r, uint32_t (&w)[NW]) const
     {
-        const uint32_t *p = (const uint32_t *)m + (size_t)r * ndw;
+        const size_t row = (size_t)__builtin_amdgcn_readfirstlane(r) * ndw + base;
+        const int bytes = ndw > base ? (ndw - base) * 4 : 0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(m + row * 4), (short)0, bytes, BUF_DWORD3);
 #pragma unroll
         for (int c = 0; c < NW; ++c)
-            w[c] = in(c) ? p[word(c)] : 0u;
+            w[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (c * 64 + lane) * 4, 0, 0);
     }
 
     DEVI void widen(uint32_t w, float (&f)[EPW]) const
@@ -70,6 +81,22 @@ template <int DT, int NW> struct Row {
 #pragma unroll
             for (int e = 0; e < EPW; ++e)
                 s += f[c][e] * v[e];
+        }
+        return s;
+    }
+
+    // this lane's share of the dot product of two stored rows (bf16 words go
+    // through the two-way bf16 dot instruction with float32 accumulation)
+    DEVI float dotw(const uint32_t (&a)[NW], const uint32_t (&b)[NW]) const
+    {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < NW; ++c) {
+            if constexpr (EPW == 2)
+                s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[c]),
+                                                    __builtin_bit_cast(bf16x2_t, b[c]), s, false);
+            else
+                s += __uint_as_float(a[c]) * __uint_as_float(b[c]);
         }
         return s;
     }
