@@ -38,7 +38,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int BR = 64;    // rows per mask block (one bit each)
-constexpr int CH = 8192;  // neurons per LDS chunk of the mask launch (64 KB)
+constexpr int CH = 1024;  // neurons per workgroup of the mask launch (8 KB of LDS)
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -64,55 +64,93 @@ Layout layout(int T, int dff, int K, int max_ovf)
 }
 
 // ------------------------------------------------------------ 1. masks
-__global__ __launch_bounds__(NT) void ell_mask_kernel(
+// One workgroup per (block of 64 rows, chunk of CH neurons): the masks of the
+// chunk are built in LDS, then written once, coalesced, with their popcounts:
+// masks and cnt are both [nblk][dff].
+DEVI void ell_mask_block(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
-    const int16_t *__restrict__ ell_col, int T, int K, int dff, int nblk,
-    uint64_t *__restrict__ masks, int32_t *__restrict__ cnt)
+    const int16_t *__restrict__ ell_col, int T, int K, int dff,
+    uint64_t *__restrict__ masks, int32_t *__restrict__ cnt, int b, int chunk,
+    unsigned long long *m, int *rn)
 {
-    __shared__ unsigned long long m[CH];
-    const int b = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int c0 = blockIdx.y * CH, c1 = min(dff, c0 + CH);
+    const int c0 = chunk * CH, c1 = min(dff, c0 + CH);
+    const int r0 = b * BR, nr = min(T - r0, BR);
     for (int i = threadIdx.x; i < c1 - c0; i += NT)
         m[i] = 0ull;
+    // stored entries of each of the block's rows (0 for backup rows)
+    if (threadIdx.x < BR)
+        rn[threadIdx.x] = threadIdx.x < nr && row_slot[r0 + threadIdx.x] < 0
+                              ? min(row_nnz[r0 + threadIdx.x], K) : 0;
     __syncthreads();
-    for (int t = b * BR + wv; t < min(T, (b + 1) * BR); t += NT / 64) {
-        if (row_slot[t] >= 0)
-            continue;
-        const int n = min(row_nnz[t], K);
-        const unsigned long long bit = 1ull << (t - b * BR);
-        for (int s = lane; s < n; s += 64) {
-            const int c = ell_col[(size_t)t * K + s];
-            if (c >= c0 && c < c1)
-                atomicOr(&m[c - c0], bit);
+    // every ELL slot of the block's rows, 8 per thread at a time: loads
+    // unconditional (slot clamped into the block), bits set for stored slots
+    const int nslot = nr * K;
+    const int16_t *base = ell_col + (size_t)r0 * K;
+    for (int q0 = 0; q0 < nslot; q0 += 8 * NT) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            c[u] = base[min(q0 + u * NT + (int)threadIdx.x, nslot - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u * NT + threadIdx.x, r = q / K;
+            if (q < nslot && q - r * K < rn[r] && c[u] >= c0 && c[u] < c1)
+                atomicOr(&m[c[u] - c0], 1ull << r);
         }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < c1 - c0; i += NT) {
         masks[(size_t)b * dff + c0 + i] = m[i];
-        cnt[(size_t)(c0 + i) * nblk + b] = __popcll(m[i]);
+        cnt[(size_t)b * dff + c0 + i] = __popcll(m[i]);
     }
 }
 
 // ------------------------------------------------------------ 2. scans
-// one wave per neuron: exclusive prefix of its block counts (in place), total
+// One workgroup per 64 neurons (a lane each); its four waves take a quarter
+// of the blocks each. Pass 1 sums each wave's counts, the waves' sums are
+// combined in LDS, pass 2 rewrites the counts as exclusive prefixes over the
+// blocks (in place) and the last wave stores the neuron's total, which the
+// column-pointer scan turns into offsets. Loads are unconditional (indices
+// clamped, values masked) so each pass keeps U loads in flight per lane.
 __global__ __launch_bounds__(NT) void blk_prefix_kernel(int32_t *__restrict__ cnt, int nblk, int dff,
                                                          int32_t *__restrict__ colptr)
 {
-    const int lane = threadIdx.x & 63;
-    const int i = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (i >= dff)
-        return;
-    int carry = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 64) {
-        const int b = b0 + lane;
-        const int v = b < nblk ? cnt[(size_t)i * nblk + b] : 0;
-        const int incl = wave_incl_scan(v, lane);
-        if (b < nblk)
-            cnt[(size_t)i * nblk + b] = carry + incl - v;
-        carry += __shfl(incl, 63, 64);
+    constexpr int U = 8;
+    __shared__ int tot[NT / 64][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int i = blockIdx.x * 64 + lane, ic = min(i, dff - 1);
+    const int per = (nblk + NT / 64 - 1) / (NT / 64);
+    const int b0 = wv * per, b1 = min(nblk, b0 + per);
+    int run = 0;
+    for (int b = b0; b < b1; b += U) {
+        int v[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            v[q] = cnt[(size_t)min(b + q, b1 - 1) * dff + ic];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            run += b + q < b1 ? v[q] : 0;
     }
-    if (lane == 0)
-        colptr[i] = carry;
+    tot[wv][lane] = run;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wv; ++w)
+        base += tot[w][lane];
+    if (wv == NT / 64 - 1 && i < dff)
+        colptr[i] = base + run;
+    run = base;
+    for (int b = b0; b < b1; b += U) {
+        int v[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            v[q] = cnt[(size_t)min(b + q, b1 - 1) * dff + ic];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            if (b + q < b1 && i < dff) {
+                cnt[(size_t)(b + q) * dff + i] = run;
+                run += v[q];
+            }
+    }
 }
 
 constexpr int SCAN_NT = 1024;
@@ -166,7 +204,7 @@ __global__ __launch_bounds__(NT) void csc_fill_kernel(
             raise_status(status, TWELL_DEV_BAD_INDEX);
             continue;
         }
-        const int p = colptr[c] + blkpre[(size_t)c * nblk + blk] +
+        const int p = colptr[c] + blkpre[(size_t)blk * dff + c] +
                       __popcll(masks[(size_t)blk * dff + c] & below);
         csc[p] = t * K + s;
     }
@@ -377,20 +415,23 @@ template <> DEVI void put_inter<TWELL_F32>(void *inter, size_t stride, int q, si
     ((float *)inter)[q * stride + o] = v;
 }
 
+// LDS of the backup-row GEMM tiles: two double-buffered 128 x 128-byte stages
+typedef uint8_t (*Tiles)[mt::TILE * mt::ROWB];
+constexpr int TILE_LDS = 4 * mt::TILE * mt::ROWB; // As[2] + Bs[2]: 64 KB
+
 template <int DT>
-__global__ __launch_bounds__(mt::NT, 2) void ovf_ud_kernel(
+DEVI void ovf_ud_tile(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff,
-    const void *__restrict__ dense, void *__restrict__ inter, size_t stride)
+    const void *__restrict__ dense, void *__restrict__ inter, size_t stride, int bx, int by,
+    Tiles As, Tiles Bs)
 {
     using E = elem<DT>;
     const int n_ovf = min(*n_ovf_p, max_ovf);
-    const int m0 = blockIdx.y * mt::TILE, n0 = blockIdx.x * mt::TILE;
+    const int m0 = by * mt::TILE, n0 = bx * mt::TILE;
     if (m0 >= n_ovf)
         return;
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][mt::TILE * mt::ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][mt::TILE * mt::ROWB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const size_t rowbytes = (size_t)dm * sizeof(typename E::storage);
     const int nk = (int)(rowbytes / mt::ROWB);
@@ -440,21 +481,20 @@ __global__ __launch_bounds__(mt::NT, 2) void ovf_ud_kernel(
 }
 
 template <int DT>
-__global__ __launch_bounds__(mt::NT, 2) void ovf_dx_kernel(
+DEVI void ovf_dx_tile(
     const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
-    const uint8_t *__restrict__ wg, int dm, int dff, float *__restrict__ dx)
+    const uint8_t *__restrict__ wg, int dm, int dff, float *__restrict__ dx, int bx, int by,
+    Tiles As, Tiles Bs)
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
     constexpr int KE = mt::ROWB / esz;
     constexpr int NSEG = DT == TWELL_BF16 ? 4 : 2; // (du hi, du lo, dg hi, dg lo) or (du, dg)
     const int n_ovf = min(*n_ovf_p, max_ovf);
-    const int m0 = blockIdx.y * mt::TILE, n0 = blockIdx.x * mt::TILE;
+    const int m0 = by * mt::TILE, n0 = bx * mt::TILE;
     if (m0 >= n_ovf)
         return;
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][mt::TILE * mt::ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][mt::TILE * mt::ROWB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const size_t rowbytes = (size_t)dm * esz;
     const int spseg = dff / KE; // K steps per segment
@@ -495,11 +535,11 @@ __global__ __launch_bounds__(mt::NT, 2) void ovf_dx_kernel(
 }
 
 template <int DT>
-__global__ __launch_bounds__(mt::NT, 2) void ovf_dw_kernel(
+DEVI void ovf_dw_tile(
     const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ x,
     const uint8_t *__restrict__ dy, int dm, int dff, float *__restrict__ dwd,
-    float *__restrict__ dwu, float *__restrict__ dwg)
+    float *__restrict__ dwu, float *__restrict__ dwg, int bx, int by, int z, Tiles As, Tiles Bs)
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
@@ -508,11 +548,9 @@ __global__ __launch_bounds__(mt::NT, 2) void ovf_dw_kernel(
     const int n_ovf = min(*n_ovf_p, max_ovf);
     if (n_ovf <= 0)
         return;
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][mt::TILE * mt::ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][mt::TILE * mt::ROWB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const int z = blockIdx.z; // 0: dW_d from (a, dy); 1: dW_u from (du, x); 2: dW_g from (dg, x)
-    const int i0 = blockIdx.y * mt::TILE, n0 = blockIdx.x * mt::TILE;
+    // z = 0: dW_d from (a, dy); 1: dW_u from (du, x); 2: dW_g from (dg, x)
+    const int i0 = by * mt::TILE, n0 = bx * mt::TILE;
     const uint8_t *src = z == 0 ? dy : x;
     float *out = z == 0 ? dwd : (z == 1 ? dwu : dwg);
     const size_t rowbytes = (size_t)dm * esz;
@@ -551,6 +589,55 @@ __global__ __launch_bounds__(mt::NT, 2) void ovf_dw_kernel(
             }
 }
 
+// ------------------------------------------------------------ fused launches
+// Work that needs no ordering between its parts shares one launch: the ELL
+// masks with the backup rows' u/da GEMM, and the backup rows' dx GEMM with
+// their dW GEMM. Workgroup b < n_a does part A, the rest part B.
+template <int DT>
+__global__ __launch_bounds__(NT, 2) void mask_ud_kernel(
+    const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
+    const int16_t *__restrict__ ell_col, int T, int K, int dff, uint64_t *__restrict__ masks,
+    int32_t *__restrict__ cnt, int n_chunk, int n_mask, const uint8_t *__restrict__ x,
+    const uint8_t *__restrict__ dy, const int32_t *__restrict__ ovf_rows,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
+    const uint8_t *__restrict__ wd, int dm, const void *__restrict__ dense,
+    void *__restrict__ inter, size_t stride)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_LDS];
+    static_assert(CH * 8 + BR * 4 <= TILE_LDS, "mask chunk must fit the shared LDS");
+    const int b = blockIdx.x;
+    if (b < n_mask) {
+        ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk,
+                       b % n_chunk, (unsigned long long *)lds, (int *)(lds + CH * 8));
+        return;
+    }
+    const int u = b - n_mask, nx = dff / mt::TILE;
+    Tiles t = (Tiles)lds;
+    ovf_ud_tile<DT>(x, dy, ovf_rows, n_ovf_p, max_ovf, wu, wd, dm, dff, dense, inter, stride,
+                    u % nx, u / nx, t, t + 2);
+}
+
+template <int DT>
+__global__ __launch_bounds__(mt::NT, 2) void ovf_dxdw_kernel(
+    const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ x,
+    const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wg,
+    const uint8_t *__restrict__ wu, int dm, int dff, float *__restrict__ dx,
+    float *__restrict__ dwd, float *__restrict__ dwu, float *__restrict__ dwg, int n_dx)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_LDS];
+    Tiles t = (Tiles)lds;
+    const int b = blockIdx.x, nx = (dm + mt::TILE - 1) / mt::TILE;
+    if (b < n_dx) {
+        ovf_dx_tile<DT>(inter, stride, ovf_rows, n_ovf_p, max_ovf, wu, wg, dm, dff, dx, b % nx,
+                        b / nx, t, t + 2);
+        return;
+    }
+    const int u = b - n_dx, ny = dff / mt::TILE;
+    ovf_dw_tile<DT>(inter, stride, ovf_rows, n_ovf_p, max_ovf, x, dy, dm, dff, dwd, dwu, dwg,
+                    u % nx, (u / nx) % ny, u / (nx * ny), t, t + 2);
+}
+
 template <int DT, int NW>
 void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg, const void *wu,
                 const void *wd, int dm, float *dx, float *dwg, float *dwu, float *dwd, uint8_t *ws,
@@ -565,7 +652,7 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     void *inter = ws + L.inter;
     const size_t stride = (size_t)L.pad_ovf * dff;
     const uint8_t *xb = (const uint8_t *)x, *dyb = (const uint8_t *)dy;
-    const int rgroups = (T + NT / 64 - 1) / (NT / 64), ngroups = (dff + NT / 64 - 1) / (NT / 64);
+    const int rgroups = (T + NT / 64 - 1) / (NT / 64);
     constexpr int NWN = NW < 16 ? NW : 16;          // neuron pass: accumulated words per lane
     // entries in flight per wave (neuron pass, dx pass); waves sharing one
     // neuron's entries (narrow rows only: wide rows leave no registers for it)
@@ -575,12 +662,19 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     constexpr int NWP = NW < ACC_NW ? NW : ACC_NW; // dx pass: words per lane of one part
     const int parts = row_parts<DT>(dm, NWP);
 
+    const int mt_tiles = L.pad_ovf / mt::TILE, nt_dm = (dm + mt::TILE - 1) / mt::TILE;
+    const bool ovf = h->max_ovf > 0 && T > 0;
     if (T > 0) {
-        hipLaunchKernelGGL(ell_mask_kernel, dim3(L.nblk, (dff + CH - 1) / CH), dim3(NT), 0, s,
-                           h->row_nnz, h->row_slot, h->ell_col, T, K, dff, L.nblk, masks, cnt);
-        tm.mark("ell_mask_kernel");
+        const int n_chunk = (dff + CH - 1) / CH, n_mask = L.nblk * n_chunk;
+        const int n_ud = ovf ? (dff / mt::TILE) * mt_tiles : 0;
+        hipLaunchKernelGGL((mask_ud_kernel<DT>), dim3(n_mask + n_ud), dim3(NT), 0, s, h->row_nnz,
+                           h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk, n_mask, xb,
+                           dyb, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
+                           (const uint8_t *)wd, dm, h->dense, inter, stride);
+        tm.mark("mask_ud_kernel");
     }
-    hipLaunchKernelGGL(blk_prefix_kernel, dim3(ngroups), dim3(NT), 0, s, cnt, L.nblk, dff, colptr);
+    hipLaunchKernelGGL(blk_prefix_kernel, dim3((dff + 63) / 64), dim3(NT), 0, s, cnt, L.nblk, dff,
+                       colptr);
     tm.mark("blk_prefix_kernel");
     hipLaunchKernelGGL(colptr_kernel, dim3(1), dim3(SCAN_NT), 0, s, colptr, dff);
     tm.mark("colptr_kernel");
@@ -600,21 +694,13 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                            (const uint8_t *)wu, (const uint8_t *)wg, dm, dx);
         tm.mark("bwd_dx_kernel");
     }
-    if (h->max_ovf > 0 && T > 0) {
-        const int mt_tiles = L.pad_ovf / mt::TILE;
-        hipLaunchKernelGGL((ovf_ud_kernel<DT>), dim3(dff / mt::TILE, mt_tiles), dim3(mt::NT), 0, s,
-                           xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
-                           (const uint8_t *)wd, dm, dff, h->dense, inter, stride);
-        tm.mark("ovf_ud_kernel");
-        const int nt_dm = (dm + mt::TILE - 1) / mt::TILE;
-        hipLaunchKernelGGL((ovf_dx_kernel<DT>), dim3(nt_dm, mt_tiles), dim3(mt::NT), 0, s, inter,
-                           stride, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
-                           (const uint8_t *)wg, dm, dff, dx);
-        tm.mark("ovf_dx_kernel");
-        hipLaunchKernelGGL((ovf_dw_kernel<DT>), dim3(nt_dm, dff / mt::TILE, 3), dim3(mt::NT), 0, s,
-                           inter, stride, h->ovf_rows, h->n_ovf, h->max_ovf, xb, dyb, dm, dff, dwd,
-                           dwu, dwg);
-        tm.mark("ovf_dw_kernel");
+    if (ovf) {
+        const int n_dx = nt_dm * mt_tiles, n_dw = nt_dm * (dff / mt::TILE) * 3;
+        hipLaunchKernelGGL((ovf_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(mt::NT), 0, s, inter,
+                           stride, h->ovf_rows, h->n_ovf, h->max_ovf, xb, dyb,
+                           (const uint8_t *)wg, (const uint8_t *)wu, dm, dff, dx, dwd, dwu, dwg,
+                           n_dx);
+        tm.mark("ovf_dxdw_kernel");
     }
 }
 

@@ -41,7 +41,12 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // One 4-byte-per-lane load from global memory straight into LDS: lane l's word
 // lands at LDS byte lds + 4 l. Written as assembly so that the compiler, which
 // would otherwise make every LDS read and barrier wait for all such loads in
-// flight, leaves the waiting to the explicit vmcnt waits of the K loop.
+// flight, leaves the waiting to the explicit vmcnt waits of the K loop. M0
+// (the LDS base of the load) is written here; nothing else in this kernel
+// reads M0 on gfx950 (its LDS instructions do not use it), hence the
+// silenced warning about clobbering a reserved register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 DEVI void lds_dma4(const uint8_t *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -49,6 +54,7 @@ DEVI void lds_dma4(const uint8_t *g, uint32_t lds)
                  : "v"(g), "s"(lds)
                  : "m0");
 }
+#pragma clang diagnostic pop
 
 // Byte offset of 16-byte chunk c (0..3) of LDS row r (64-byte rows). Rows
 // r, r+4, r+8, r+12 start on the same bank; XOR-ing the chunk with (r / 4) % 4

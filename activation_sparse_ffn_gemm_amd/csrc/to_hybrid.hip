@@ -3,14 +3,16 @@
 // so rows with few nonzeros go to a compact ELL matrix and overflow rows are
 // redirected to a dense backup, through a dedicated conversion kernel).
 //
-// Three launches, all integer / copy work:
+// Two launches, all integer / copy work:
 //   1. rows:  one wave per row sums the tile counts (row_nnz) and, for a row
 //             with row_nnz <= K, concatenates its tiles into ELL row t; the
 //             tiles are in column order, so the ELL row is ascending.
-//   2. slots: one workgroup scans the overflow flags in row order, giving
-//             backup slots in ascending row order, ovf_rows and n_ovf.
-//   3. dense: one workgroup per used backup slot zero-fills the dense row
-//             and scatters the row's values into it.
+//   2. slots + dense: one workgroup per block of 64 rows counts the overflow
+//             rows before its block (a reduction over row_nnz), numbers its
+//             own overflow rows after them in row order (backup slots in
+//             ascending row order), writes row_slot, ovf_rows, and the dense
+//             backup rows (zero fill, then scatter); the last block writes
+//             n_ovf.
 #include "common.hpp"
 
 namespace {
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
     if (lane == 0)
         row_nnz[t] = total;
     if (total > K)
-        return; // overflow row: handled by the dense launch
+        return; // overflow row: goes to the dense backup
     int base = 0;
     for (int j0 = 0; j0 < nt; j0 += 64) {
         const int j = j0 + lane;
@@ -44,80 +46,121 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
         const int excl = base + incl - n;
         const size_t src = ((size_t)t * nt + j) * W;
         const size_t dst = (size_t)t * K + excl;
-        for (int s = 0; s < n; ++s) {
-            ell_col[dst + s] = col[src + s];
-            ((S *)ell_val)[dst + s] = ((const S *)val)[src + s];
+        // 8 slots at a time: loads unconditional (slot clamped to the tile),
+        // stores masked, so the loads of a lane are all in flight together
+        for (int s0 = 0; s0 < n; s0 += 8) {
+            int16_t c[8];
+            S v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const size_t q = src + min(s0 + u, W - 1);
+                c[u] = col[q];
+                v[u] = ((const S *)val)[q];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < n) {
+                    ell_col[dst + s0 + u] = c[u];
+                    ((S *)ell_val)[dst + s0 + u] = v[u];
+                }
         }
         base += __shfl(incl, 63, 64);
     }
 }
 
-constexpr int SCAN_NT = 1024;
+constexpr int BLK = 64;   // rows per workgroup of the slot/dense launch
+constexpr int DNT = 256;  // its threads
 
-__global__ __launch_bounds__(SCAN_NT) void hyb_slots_kernel(
-    const int32_t *__restrict__ row_nnz, int T, int K, int max_ovf, int32_t *__restrict__ row_slot,
-    int32_t *__restrict__ ovf_rows, int32_t *__restrict__ n_ovf, int32_t *__restrict__ status)
+template <int DT>
+__global__ __launch_bounds__(DNT) void hyb_dense_kernel(
+    const int32_t *__restrict__ count, const int16_t *__restrict__ col,
+    const void *__restrict__ val, const int32_t *__restrict__ row_nnz, int T, int nt, int W,
+    int K, int dff, int max_ovf, int32_t *__restrict__ row_slot, int32_t *__restrict__ ovf_rows,
+    int32_t *__restrict__ n_ovf, void *__restrict__ dense, int32_t *__restrict__ status)
 {
-    __shared__ int wsum[SCAN_NT / 64];
-    __shared__ int carry;
+    using S = typename elem<DT>::storage;
+    __shared__ int rows[BLK];
+    __shared__ int n_here, n_before;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r0 = blockIdx.x * BLK;
     if (tid == 0)
-        carry = 0;
+        n_before = 0;
     __syncthreads();
-    for (int t0 = 0; t0 < T; t0 += SCAN_NT) {
-        const int t = t0 + tid;
-        const int f = (t < T && row_nnz[t] > K) ? 1 : 0;
-        const int incl = wave_incl_scan(f, lane);
-        if (lane == 63)
-            wsum[wv] = incl;
-        __syncthreads();
-        int before = carry;
-        for (int w = 0; w < wv; ++w)
-            before += wsum[w];
-        const int slot = before + incl - f;
+    // overflow rows before this block: 8 loads per thread in flight (rows
+    // clamped, flags masked), per-thread counts summed in LDS
+    int mine = 0;
+    for (int t0 = 0; t0 < r0; t0 += 8 * DNT) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = row_nnz[min(t0 + u * DNT + tid, r0 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            mine += (t0 + u * DNT + tid < r0 && v[u] > K) ? 1 : 0;
+    }
+    if (mine)
+        atomicAdd(&n_before, mine);
+    __syncthreads();
+    const int before = n_before;
+    // this block's rows: wave 0 numbers them (64 rows = one ballot)
+    if (wv == 0) {
+        const int t = r0 + lane;
+        const bool f = t < T && row_nnz[t] > K;
+        const unsigned long long m = __ballot(f);
+        const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
         if (t < T) {
             row_slot[t] = f ? slot : -1;
             if (f && slot < max_ovf)
                 ovf_rows[slot] = t;
         }
-        __syncthreads();
-        if (tid == SCAN_NT - 1)
-            carry = slot + f;
-        __syncthreads();
-    }
-    if (tid == 0) {
-        *n_ovf = carry;
-        if (carry > max_ovf)
-            raise_status(status, TWELL_DEV_OVF_CAPACITY);
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(256) void hyb_dense_kernel(
-    const int32_t *__restrict__ count, const int16_t *__restrict__ col,
-    const void *__restrict__ val, int nt, int W, int dff, int max_ovf,
-    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf,
-    void *__restrict__ dense, int32_t *__restrict__ status)
-{
-    using S = typename elem<DT>::storage;
-    const int slot = blockIdx.x;
-    if (slot >= min(*n_ovf, max_ovf))
-        return;
-    const int t = ovf_rows[slot];
-    S *drow = (S *)dense + (size_t)slot * dff;
-    for (int i = threadIdx.x; i < dff; i += blockDim.x)
-        drow[i] = S(0);
-    __syncthreads();
-    for (int j = threadIdx.x; j < nt; j += blockDim.x) {
-        const int n = min(count[(size_t)t * nt + j], W);
-        const size_t src = ((size_t)t * nt + j) * W;
-        for (int s = 0; s < n; ++s) {
-            const int c = col[src + s];
-            if (c >= 0 && c < dff)
-                drow[c] = ((const S *)val)[src + s];
-            else
-                raise_status(status, TWELL_DEV_BAD_INDEX);
+        if (f)
+            rows[__popcll(m & ((1ull << lane) - 1ull))] = t;
+        if (lane == 0) {
+            n_here = __popcll(m);
+            if (r0 + BLK >= T) { // last block: the true total
+                *n_ovf = before + __popcll(m);
+                if (before + __popcll(m) > max_ovf)
+                    raise_status(status, TWELL_DEV_OVF_CAPACITY);
+            }
         }
+    }
+    __syncthreads();
+    // dense rows of this block's overflow rows (within capacity)
+    for (int k = 0; k < n_here; ++k) {
+        const int slot = before + k;
+        if (slot >= max_ovf)
+            break;
+        const int t = rows[k];
+        S *drow = (S *)dense + (size_t)slot * dff;
+        for (int i = tid; i < dff; i += DNT)
+            drow[i] = S(0);
+        __syncthreads();
+        // every slot of the row's TwELL tiles, 8 per thread at a time (loads
+        // unconditional, stores of the stored slots only)
+        const size_t src = (size_t)t * nt * W;
+        const int nslot = nt * W;
+        for (int q0 = 0; q0 < nslot; q0 += 8 * DNT) {
+            int c[8], n[8];
+            S v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int q = min(q0 + u * DNT + tid, nslot - 1);
+                n[u] = count[(size_t)t * nt + q / W];
+                c[u] = col[src + q];
+                v[u] = ((const S *)val)[src + q];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int q = q0 + u * DNT + tid;
+                if (q < nslot && q % W < min(n[u], W)) {
+                    if (c[u] >= 0 && c[u] < dff)
+                        drow[c[u]] = v[u];
+                    else
+                        raise_status(status, TWELL_DEV_BAD_INDEX);
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -125,19 +168,16 @@ template <int DT>
 hipError_t launch(const twell_t *h, const hybrid_t *o, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int nt = h->d_ff / TWELL_TILE_C;
-    if (h->T > 0)
+    if (h->T > 0) {
         hipLaunchKernelGGL(hyb_rows_kernel<DT>, dim3((h->T + 3) / 4), dim3(256), 0, s, h->count,
                            h->col, h->val, h->T, nt, h->width, o->K, o->row_nnz, o->ell_col,
                            o->ell_val);
-    tm.mark("hyb_rows_kernel");
-    hipLaunchKernelGGL(hyb_slots_kernel, dim3(1), dim3(SCAN_NT), 0, s, o->row_nnz, h->T, o->K,
-                       o->max_ovf, o->row_slot, o->ovf_rows, o->n_ovf, status);
-    tm.mark("hyb_slots_kernel");
-    const int nslots = min(o->max_ovf, h->T);
-    if (nslots > 0)
-        hipLaunchKernelGGL(hyb_dense_kernel<DT>, dim3(nslots), dim3(256), 0, s, h->count, h->col,
-                           h->val, nt, h->width, h->d_ff, o->max_ovf, o->ovf_rows, o->n_ovf,
-                           o->dense, status);
+        tm.mark("hyb_rows_kernel");
+    }
+    hipLaunchKernelGGL(hyb_dense_kernel<DT>, dim3(h->T > 0 ? (h->T + BLK - 1) / BLK : 1),
+                       dim3(DNT), 0, s, h->count, h->col, h->val, o->row_nnz, h->T, nt, h->width,
+                       o->K, h->d_ff, o->max_ovf, o->row_slot, o->ovf_rows, o->n_ovf, o->dense,
+                       status);
     tm.mark("hyb_dense_kernel");
     return hipGetLastError();
 }

@@ -194,18 +194,19 @@ def main():
                              "2 d_model d_ff flop per token (TwELL written in the epilogue)"),
         "ffn_fwd_kernel": ("hbm", nnz * 2 * row_b + T * row_b + T * dm * 4 + twell_b,
                            "per nonzero one wu_t row + one wd row; x, y, TwELL once"),
-        "hyb_rows_kernel": ("hbm", T * n_t * 4 + nnz * 4 + nnz_ell * 4 + 8 * T,
-                            "TwELL counts + entries read; ELL entries, row_nnz written"),
-        "hyb_dense_kernel": ("hbm", (nnz - nnz_ell) * 4 + n_ovf * dff * 2,
-                             "backup rows' entries read, dense backup written"),
+        "hyb_rows_kernel": ("hbm", T * n_t * 4 + nnz_ell * 8 + 4 * T,
+                            "TwELL counts + ELL rows' entries read; ELL entries, row_nnz written"),
+        "hyb_dense_kernel": ("hbm", n_ovf * n_t * (4 + 128 * 4) + n_ovf * dff * 2 + 8 * T,
+                             "backup rows' TwELL tiles read, dense backup, row_slot written"),
         "bwd_neuron_kernel": ("hbm", nnz_ell * (2 * row_b + 4 + 2 + 8) + dff * (2 * row_b + 3 * dm * 4),
                               "per ELL nonzero one x row + one dy row + CSC slot, h, du/dg; "
                               "per neuron wu_t + wd rows and three fp32 dW rows"),
         "bwd_dx_kernel": ("hbm", nnz_ell * (2 * row_b + 10) + 8 * T + T_ell * dm * 4,
                           "per ELL nonzero one wu_t row + one wg_t row + col, du, dg; dx rows"),
-        "ovf_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "u_O and da_O: 2 GEMMs"),
-        "ovf_dx_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "dx_O: 2 GEMMs"),
-        "ovf_dw_kernel": ("mfma", 3 * 2.0 * n_ovf * dm * dff, "dW_g, dW_u, dW_d += : 3 GEMMs"),
+        "mask_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff,
+                           "u_O and da_O: 2 GEMMs (beside the ELL transpose masks)"),
+        "ovf_dxdw_kernel": ("mfma", 5 * 2.0 * n_ovf * dm * dff,
+                            "dx_O (2 GEMMs) and dW_g, dW_u, dW_d += (3 GEMMs)"),
     }
     peak = {"mfma": BF16_PEAK_TFLOPS, "hbm": HBM_PEAK_GBS}
     unit = {"mfma": "TFLOP/s", "hbm": "GB/s"}
