@@ -8,7 +8,7 @@ hipError_t launch_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int
 hipError_t launch_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
                           const void *wd, int dm, float *y, void *ws, int32_t *status,
                           twell_timing_t *timing, hipStream_t s);
-size_t fwd_workspace(int T, int dff, int W);
+size_t fwd_workspace(int dt, int T, int dm, int dff, int W);
 hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status,
                             twell_timing_t *timing, hipStream_t s);
 hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
@@ -114,10 +114,9 @@ int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, 
 size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                  int32_t width)
 {
-    (void)d_model;
-    if (!dtype_ok(dt) || T < 0 || d_ff < TWELL_TILE_C || width < 1)
+    if (!dtype_ok(dt) || T < 0 || d_model < 1 || d_ff < TWELL_TILE_C || width < 1)
         return 0;
-    return fwd_workspace(T, d_ff, width);
+    return fwd_workspace(dt, T, d_model, d_ff, width);
 }
 
 int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,

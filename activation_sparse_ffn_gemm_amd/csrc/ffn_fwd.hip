@@ -1,33 +1,57 @@
-// Fused up and down projections over the TwELL nonzeros ("Sparser, Faster,
-// Lighter Transformer Language Models", summary page section 2.B.2: one kernel
-// applies the up and down projections to the nonzero gate entries only).
+// Up and down projections over the TwELL nonzeros only ("Sparser, Faster,
+// Lighter Transformer Language Models", summary page section 2.B.2: the up
+// and down projections applied to the nonzero gate entries, nothing else).
 //
 // y[t] = sum over stored (i, h) of row t of  a * wd[i],  a = h * (x[t] . wu_t[i]).
 //
-// One wave64 owns one token (and, for wide rows, one part of d_model for the
-// output): x[t] and the float32 accumulator of y[t] stay in registers, the
-// row's entries are staged in LDS in ascending column order, and per nonzero
-// the wave gathers one wu_t row (the up column) and one wd row (the down
-// row), each a contiguous d_model vector read with 4-byte lanes (rows.hpp),
-// several nonzeros in flight at once. a is never written to memory.
+// Every gathered row is a contiguous d_model vector (wu_t and wd rows are
+// both [d_ff][d_model]), read with 4-byte lanes through a per-row buffer
+// descriptor (rows.hpp). Two designs:
+//
+// Many tokens and large weights: two passes, each giving every XCD a working set
+// that stays in its own 4 MB L2 (workgroup b runs on XCD b % 8):
+//   up:   XCD k owns the neuron tiles [k nt / 8, (k+1) nt / 8). A wave per
+//         token holds x[t] in registers, gathers the wu_t rows of its
+//         entries in those tiles and writes a = h u for each, with the entry's
+//         column, into the token's compact entry list (entries of all tiles in
+//         column order, so each XCD's share is one contiguous run). Extra
+//         workgroups copy wd into a slice-major layout for the down pass.
+//   down: XCD k owns the k-th eighth of the d_model columns. A wave per token
+//         walks the token's compact list and gathers, per entry, only the
+//         slice of the wd row in that copy (slices are contiguous per XCD, so
+//         the gathers spread over all L2 channels), accumulating y[t]'s slice.
+// Otherwise: one fused pass, a wave per token doing both projections, a is
+// never written to memory.
 #include "rows.hpp"
 
 namespace {
 
-constexpr int NT = 256;   // 4 waves = 4 tokens per workgroup
-constexpr int LIST = 256; // entries staged in LDS per pass
+constexpr int NT = 256;       // 4 waves = 4 tokens per workgroup
+constexpr int LIST = 256;     // entries staged in LDS per pass
+// The two-pass design pays for its extra traffic (x read by every XCD, the
+// wd copy, the entry lists) only with many tokens and weights well beyond
+// one XCD's L2; otherwise the fused pass is faster.
+constexpr int SPLIT_T = 1024;                 // tokens
+constexpr size_t SPLIT_W = (size_t)16 << 20;  // bytes of one weight matrix
+
+inline bool use_split(int dt, int T, int dm, int dff)
+{
+    return T >= SPLIT_T && (size_t)dff * dm * (dt == TWELL_BF16 ? 2 : 4) >= SPLIT_W;
+}
+constexpr int RL_ROWS = 8;    // wd rows per workgroup of the slice-major copy
 
 // Stage the stored entries of row t, tiles [j0, j1), into LDS: element e of
-// the list is (slot within the row = j * W + s, column, value). Calls fn(ne)
-// after each pass of up to LIST entries, with the list visible to the wave.
-// A lane reads the slots of one tile, 8 independent loads at a time. With
-// VALS false only slots and columns are staged (val is not read).
+// the list is (column, value). Calls fn(p0, ne) after each pass of up to LIST
+// entries, p0 being the index of the pass's first entry among the range's
+// entries (in column order). A lane reads the slots of one tile, 8
+// independent loads at a time. With VALS false val is not read.
 template <int DT, bool VALS, class Fn>
 DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *val, int t,
-                          int nt, int W, int j0, int j1, int dff, int lane, int *lslot,
-                          int *lcol, float *lval, int32_t *status, Fn fn)
+                          int nt, int W, int j0, int j1, int dff, int lane, int *lcol, float *lval,
+                          int32_t *status, Fn fn)
 {
     using E = elem<DT>;
+    int done = 0; // entries of earlier 64-tile chunks
     for (int jb = j0; jb < j1; jb += 64) {
         const int j = jb + lane;
         const int n = j < j1 ? min(count[(size_t)t * nt + j], W) : 0;
@@ -48,10 +72,6 @@ DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *
                     v[u] = VALS ? E::load1(val, q) : 0.f;
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (s0 + u >= n)
-                        c[u] = 0, v[u] = 0.f;
-#pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int e = excl + s0 + u - p0;
                     if (s0 + u < n && e < LIST) {
@@ -60,7 +80,6 @@ DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *
                             c[u] = 0;
                             v[u] = 0.f;
                         }
-                        lslot[e] = j * W + s0 + u;
                         lcol[e] = c[u];
                         lval[e] = v[u];
                     }
@@ -69,10 +88,24 @@ DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            fn(min(LIST, tot - p0));
+            fn(done + p0, min(LIST, tot - p0));
             __builtin_amdgcn_wave_barrier();
         }
+        done += tot;
     }
+}
+
+// Stored entries of row t in tiles [0, j) (.x) and in all tiles (.y).
+DEVI int2 row_counts(const int32_t *count, int t, int nt, int W, int j, int lane)
+{
+    int below = 0, all = 0;
+    for (int jb = 0; jb < nt; jb += 64) {
+        const int jj = jb + lane;
+        const int n = jj < nt ? min(count[(size_t)t * nt + jj], W) : 0;
+        below += __shfl(wave_incl_scan(jj < j ? n : 0, lane), 63, 64);
+        all += __shfl(wave_incl_scan(n, lane), 63, 64);
+    }
+    return make_int2(below, all);
 }
 
 // ---------------------------------------------------------------- fused
@@ -85,7 +118,7 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
 {
     using R = Row<DT, NW>;   // whole row, for the up dot product
     using RP = Row<DT, NWP>; // this wave's part of the row, for the down projection
-    __shared__ int lslot[NT / 64][LIST], lcol[NT / 64][LIST];
+    __shared__ int lcol[NT / 64][LIST];
     __shared__ float lval[NT / 64][LIST];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int t = blockIdx.x * (NT / 64) + wv;
@@ -98,7 +131,7 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
     float acc[NWP][RP::EPW];
     part.zero_f(acc);
     for_row_entries<DT, true>(count, col, val, t, nt, W, 0, nt, nt * TWELL_TILE_C, lane,
-                              lslot[wv], lcol[wv], lval[wv], status, [&](int ne) {
+                              lcol[wv], lval[wv], status, [&](int, int ne) {
         // Stream the staged entries through G register buffers: the rows of
         // entry e + G are requested as soon as entry e has been used, so G
         // entries' gathers stay in flight while the wave computes. Requests
@@ -126,47 +159,264 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
     part.store_f(y, t, acc);
 }
 
+// ---------------------------------------------------------------- split
+// Geometry of the slice-major copy of wd: slice k holds words
+// [k sww, k sww + sww) of every row (fewer in the last slices), each row's
+// slice padded to swp words (a multiple of 32: whole 128-byte lines).
+struct Slices {
+    int ndw, sww, swp;
+    DEVI int valid(int k) const { return max(0, min(sww, ndw - k * sww)); }
+};
+
+inline Slices slices(int dt, int dm)
+{
+    Slices s;
+    s.ndw = dt == TWELL_BF16 ? dm / 2 : dm;
+    s.sww = (s.ndw + NXCD - 1) / NXCD;
+    s.swp = (s.sww + 31) / 32 * 32;
+    return s;
+}
+
+// Workspace of the two-pass design: slice-major wd, then the compact entry
+// lists (a as float32, columns as int16) and their lengths.
+struct FwdLayout {
+    size_t wds, ac, cc, rn, total;
+    int cap;
+};
+
+inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline FwdLayout fwd_layout(int dt, int T, int dm, int dff, int W)
+{
+    FwdLayout L;
+    const Slices sl = slices(dt, dm);
+    L.cap = dff / TWELL_TILE_C * W;
+    size_t o = 0;
+    L.wds = o; o += up256((size_t)NXCD * dff * sl.swp * 4);
+    L.ac = o;  o += up256((size_t)T * L.cap * 4);
+    L.cc = o;  o += up256((size_t)T * L.cap * 2);
+    L.rn = o;  o += up256((size_t)T * 4);
+    L.total = o;
+    return L;
+}
+
+template <int DT, int NW, int G>
+__global__ __launch_bounds__(NT) void fwd_up_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ count,
+    const int16_t *__restrict__ col, const void *__restrict__ val, int T, int nt, int W,
+    const uint8_t *__restrict__ wu, int dm, int n_copy, const uint32_t *__restrict__ wd,
+    uint32_t *__restrict__ wds, int dff, Slices sl, float *__restrict__ ac,
+    int16_t *__restrict__ cc, int32_t *__restrict__ rn, int cap, int32_t *__restrict__ status)
+{
+    using R = Row<DT, NW>;
+    __shared__ int lcol[NT / 64][LIST];
+    __shared__ float lval[NT / 64][LIST];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int b = blockIdx.x;
+    if (b < n_copy) {
+        // slice-major copy of RL_ROWS rows of wd (padding words set to 0)
+        const int per = NXCD * sl.swp;
+        for (int q = threadIdx.x; q < RL_ROWS * per; q += NT) {
+            const int i = b * RL_ROWS + q / per;
+            if (i >= dff)
+                break;
+            const int k = (q % per) / sl.swp, w = q % sl.swp, srcw = k * sl.sww + w;
+            const uint32_t v = wd[(size_t)i * sl.ndw + min(srcw, sl.ndw - 1)];
+            wds[((size_t)k * dff + i) * sl.swp + w] = (w < sl.sww && srcw < sl.ndw) ? v : 0u;
+        }
+        return;
+    }
+    b -= n_copy; // n_copy is a multiple of 8: b % 8 is still the XCD
+    const int k = b % NXCD;
+    const int t = (b / NXCD) * (NT / 64) + wv;
+    if (t >= T)
+        return;
+    const int j0 = k * nt / NXCD, j1 = (k + 1) * nt / NXCD;
+    const int2 cnt = row_counts(count, t, nt, W, j0, lane);
+    if (k == 0 && lane == 0)
+        rn[t] = cnt.y;
+    if (j0 >= j1)
+        return;
+    const R geo(dm, lane, 0);
+    uint32_t xw[NW];
+    geo.load_w(x, t, xw);
+    float *arow = ac + (size_t)t * cap + cnt.x;
+    int16_t *crow = cc + (size_t)t * cap + cnt.x;
+    for_row_entries<DT, true>(count, col, val, t, nt, W, j0, j1, dff, lane, lcol[wv], lval[wv],
+                              status, [&](int p0, int ne) {
+        for (int eb = 0; eb < ne; eb += 64) {
+            const int m = min(64, ne - eb);
+            // stream the m entries through G register buffers; lane e keeps
+            // entry e's a and writes it, with its column, at the end
+            uint32_t vu[G][NW];
+            auto fetch = [&](int e, uint32_t (&u)[NW]) {
+                geo.load_w(wu, lcol[wv][eb + min(e, m - 1)], u);
+            };
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                fetch(g, vu[g]);
+            float mine = 0.f;
+            for (int e0 = 0; e0 < m; e0 += G) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int e = e0 + g;
+                    const float u = wave_sum(geo.dotw(xw, vu[g]));
+                    if (lane == e && e < m)
+                        mine = lval[wv][eb + e] * u;
+                    fetch(e + G, vu[g]);
+                }
+            }
+            if (lane < m) {
+                arow[p0 + eb + lane] = mine;
+                crow[p0 + eb + lane] = (int16_t)lcol[wv][eb + lane];
+            }
+        }
+    });
+}
+
+template <int DT, int SPL, int G>
+__global__ __launch_bounds__(NT) void fwd_down_kernel(
+    const uint32_t *__restrict__ wds, int dff, Slices sl, const float *__restrict__ ac,
+    const int16_t *__restrict__ cc, const int32_t *__restrict__ rn, int cap, int T, int dm,
+    float *__restrict__ y)
+{
+    constexpr int EPW = DT == TWELL_BF16 ? 2 : 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int k = blockIdx.x % NXCD;
+    const int t = (blockIdx.x / NXCD) * (NT / 64) + wv;
+    const int nk = sl.valid(k);
+    if (t >= T || nk == 0)
+        return;
+    const int n = rn[t];
+    const float *arow = ac + (size_t)t * cap;
+    const int16_t *crow = cc + (size_t)t * cap;
+    const uint32_t *slice = wds + (size_t)k * dff * sl.swp;
+    float acc[SPL][EPW];
+#pragma unroll
+    for (int c = 0; c < SPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EPW; ++e)
+            acc[c][e] = 0.f;
+    for (int eb = 0; eb < n; eb += 64) {
+        const int m = min(64, n - eb);
+        const int ci = lane < m ? crow[eb + lane] : 0;
+        const float av = lane < m ? arow[eb + lane] : 0.f;
+        uint32_t v[G][SPL];
+        // the row's slice through a buffer descriptor: words past nk read 0
+        auto fetch = [&](int e, uint32_t (&w)[SPL]) {
+            const int c = bcast(ci, min(e, m - 1));
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(slice + (size_t)c * sl.swp), (short)0, nk * 4, BUF_DWORD3);
+#pragma unroll
+            for (int q = 0; q < SPL; ++q)
+                w[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (q * 64 + lane) * 4, 0, 0);
+        };
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            fetch(g, v[g]);
+        for (int e0 = 0; e0 < m; e0 += G) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int e = e0 + g;
+                if (e < m) { // uniform
+                    const float a = bcast(av, e);
+#pragma unroll
+                    for (int q = 0; q < SPL; ++q) {
+                        if constexpr (EPW == 2) {
+                            acc[q][0] += a * bf16_lo(v[g][q]);
+                            acc[q][1] += a * bf16_hi(v[g][q]);
+                        } else {
+                            acc[q][0] += a * __uint_as_float(v[g][q]);
+                        }
+                    }
+                }
+                fetch(e + G, v[g]);
+            }
+        }
+    }
+    float *yrow = y + (size_t)t * dm + (size_t)k * sl.sww * EPW;
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+        const int w = q * 64 + lane;
+        if (w < nk) {
+            if constexpr (EPW == 2)
+                *(float2 *)(yrow + 2 * w) = make_float2(acc[q][0], acc[q][1]);
+            else
+                yrow[w] = acc[q][0];
+        }
+    }
+}
+
 template <int DT, int NW>
 void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, int dm, float *y,
-               int32_t *status, hipStream_t s)
+               uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
-    constexpr int NWP = NW < 16 ? NW : 16; // whole rows up to d_model 2048 (bf16)
-    constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
-    const int parts = row_parts<DT>(dm, NWP);
-    const int groups = (h->T + NT / 64 - 1) / (NT / 64);
-    hipLaunchKernelGGL((ffn_fwd_kernel<DT, NW, NWP, G>), dim3(groups, parts), dim3(NT), 0, s,
-                       (const uint8_t *)x, h->count, h->col, h->val, h->T,
-                       h->d_ff / TWELL_TILE_C, h->width, (const uint8_t *)wu,
-                       (const uint8_t *)wd, dm, y, status);
+    const int T = h->T, nt = h->d_ff / TWELL_TILE_C, dff = h->d_ff;
+    const int groups = (T + NT / 64 - 1) / (NT / 64);
+    if (!use_split(DT, T, dm, dff)) {
+        constexpr int NWP = NW < 16 ? NW : 16; // whole rows up to d_model 2048 (bf16)
+        constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
+        const int parts = row_parts<DT>(dm, NWP);
+        hipLaunchKernelGGL((ffn_fwd_kernel<DT, NW, NWP, G>), dim3(groups, parts), dim3(NT), 0, s,
+                           (const uint8_t *)x, h->count, h->col, h->val, T, nt, h->width,
+                           (const uint8_t *)wu, (const uint8_t *)wd, dm, y, status);
+        tm.mark("ffn_fwd_kernel");
+        return;
+    }
+    const Slices sl = slices(DT, dm);
+    const FwdLayout L = fwd_layout(DT, T, dm, dff, h->width);
+    uint32_t *wds = (uint32_t *)(ws + L.wds);
+    float *ac = (float *)(ws + L.ac);
+    int16_t *cc = (int16_t *)(ws + L.cc);
+    int32_t *rn = (int32_t *)(ws + L.rn);
+    const int n_copy = ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD;
+    constexpr int GU = NW <= 16 ? 4 : 2; // entries in flight per wave (no accumulators here)
+    hipLaunchKernelGGL((fwd_up_kernel<DT, NW, GU>), dim3(n_copy + groups * NXCD), dim3(NT), 0, s,
+                       (const uint8_t *)x, h->count, h->col, h->val, T, nt, h->width,
+                       (const uint8_t *)wu, dm, n_copy, (const uint32_t *)wd, wds, dff, sl, ac,
+                       cc, rn, L.cap, status);
+    tm.mark("fwd_up_kernel");
+    const int spl = (sl.sww + 63) / 64;
+    if (spl <= 1)
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y);
+    else if (spl == 2)
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y);
+    else
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y);
+    tm.mark("fwd_down_kernel");
 }
 
 template <int DT>
 void launch_dt(const void *x, const twell_t *h, const void *wu, const void *wd, int dm, float *y,
-               int32_t *status, hipStream_t s)
+               uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
+#define TW_CASE(N) \
+    case N: launch_nw<DT, N>(x, h, wu, wd, dm, y, ws, status, tm, s); break;
     switch (row_nw<DT>(dm)) {
-    case 1: launch_nw<DT, 1>(x, h, wu, wd, dm, y, status, s); break;
-    case 2: launch_nw<DT, 2>(x, h, wu, wd, dm, y, status, s); break;
-    case 4: launch_nw<DT, 4>(x, h, wu, wd, dm, y, status, s); break;
-    case 8: launch_nw<DT, 8>(x, h, wu, wd, dm, y, status, s); break;
-    case 16: launch_nw<DT, 16>(x, h, wu, wd, dm, y, status, s); break;
-    default: launch_nw<DT, 32>(x, h, wu, wd, dm, y, status, s); break;
+        TW_CASE(1) TW_CASE(2) TW_CASE(4) TW_CASE(8) TW_CASE(16)
+    default: launch_nw<DT, 32>(x, h, wu, wd, dm, y, ws, status, tm, s); break;
     }
+#undef TW_CASE
 }
 
 } // namespace
 
-size_t fwd_workspace(int, int, int) { return 0; }
+size_t fwd_workspace(int dt, int T, int dm, int dff, int W)
+{
+    return use_split(dt, T, dm, dff) ? fwd_layout(dt, T, dm, dff, W).total : 0;
+}
 
 hipError_t launch_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
-                          const void *wd, int dm, float *y, void *, int32_t *status,
+                          const void *wd, int dm, float *y, void *ws, int32_t *status,
                           twell_timing_t *timing, hipStream_t s)
 {
     Timer tm(timing, s);
     if (dt == TWELL_BF16)
-        launch_dt<TWELL_BF16>(x, h, wu_t, wd, dm, y, status, s);
+        launch_dt<TWELL_BF16>(x, h, wu_t, wd, dm, y, (uint8_t *)ws, status, tm, s);
     else
-        launch_dt<TWELL_F32>(x, h, wu_t, wd, dm, y, status, s);
-    tm.mark("ffn_fwd_kernel");
+        launch_dt<TWELL_F32>(x, h, wu_t, wd, dm, y, (uint8_t *)ws, status, tm, s);
     return hipGetLastError();
 }

@@ -194,6 +194,11 @@ def main():
                              "2 d_model d_ff flop per token (TwELL written in the epilogue)"),
         "ffn_fwd_kernel": ("hbm", nnz * 2 * row_b + T * row_b + T * dm * 4 + twell_b,
                            "per nonzero one wu_t row + one wd row; x, y, TwELL once"),
+        "fwd_up_kernel": ("hbm", nnz * row_b + T * row_b + twell_b + 2 * dff * row_b + nnz * 6,
+                          "per nonzero one wu_t row; x, TwELL once; wd slice-major copy "
+                          "(read + write); a and column per nonzero written"),
+        "fwd_down_kernel": ("hbm", nnz * row_b + nnz * 6 + T * dm * 4,
+                            "per nonzero one wd row (as 8 slices); a and column per nonzero; y"),
         "hyb_rows_kernel": ("hbm", T * n_t * 4 + nnz_ell * 8 + 4 * T,
                             "TwELL counts + ELL rows' entries read; ELL entries, row_nnz written"),
         "hyb_dense_kernel": ("hbm", n_ovf * n_t * (4 + 128 * 4) + n_ovf * dff * 2 + 8 * T,
