@@ -41,6 +41,7 @@ WORKLOADS = {
 CSRC = os.path.join(ROOT, "activation_sparse_ffn_gemm_amd", "csrc")
 KERNEL_SOURCES = {
     "gate_pack_kernel": "gate_pack.hip", "ffn_fwd_kernel": "ffn_fwd.hip",
+    "fwd_up_kernel": "ffn_fwd.hip", "fwd_down_kernel": "ffn_fwd.hip",
     "hyb_rows_kernel": "to_hybrid.hip", "hyb_slots_kernel": "to_hybrid.hip",
     "hyb_dense_kernel": "to_hybrid.hip",
 }
