@@ -41,8 +41,9 @@ def load(path: str) -> ctypes.CDLL:
     L.orc_ffn_dense.argtypes = [P, P, P, P, I, I, I, P]
     L.orc_ffn_twell.argtypes = [P, P, P, P, I, I, I, P, P, I, P]
     L.orc_to_hybrid.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P]
-    L.orc_bwd_hybrid.argtypes = [P, P, I, I, I, P, P, P, P, I, P, P, P, P, P, P, P, P]
-    L.orc_bwd_dense.argtypes = [P, P, I, I, I, P, P, P, P, P, P, P]
+    D = ctypes.c_double
+    L.orc_bwd_hybrid.argtypes = [P, P, I, I, I, P, P, P, P, I, P, P, P, P, D, P, P, P, P]
+    L.orc_bwd_dense.argtypes = [P, P, I, I, I, P, P, P, D, P, P, P, P]
     L.orc_num_threads.argtypes = []
     _lib = L
     return L
@@ -132,8 +133,9 @@ def to_hybrid(tw: dict, K: int, max_ovf: int) -> dict:
             "capacity_exceeded": bool(cap), "K": K, "max_ovf": max_ovf, "d_ff": dff}
 
 
-def bwd_hybrid(x, dy, hy: dict, wg_t, wu_t, wd):
-    """Backward on the hybrid's pattern; returns (dx, dwg_t, dwu_t, dwd)."""
+def bwd_hybrid(x, dy, hy: dict, wg_t, wu_t, wd, l1: float = 0.0):
+    """Backward on the hybrid's pattern, with the gradient of an activation
+    penalty l1 * sum(h) added; returns (dx, dwg_t, dwu_t, dwd)."""
     x, dy, wg_t, wu_t, wd = map(_f64, (x, dy, wg_t, wu_t, wd))
     T, dm = x.shape
     dff = wg_t.shape[0]
@@ -146,20 +148,21 @@ def bwd_hybrid(x, dy, hy: dict, wg_t, wu_t, wd):
     dwg, dwu, dwd = (np.empty((dff, dm)) for _ in range(3))
     rc = lib().orc_bwd_hybrid(_p(x), _p(dy), T, dm, dff, _p(row_nnz), _p(row_slot), _p(ell_col),
                               _p(ell_val), K, _p(dense), _p(wg_t), _p(wu_t), _p(wd),
-                              _p(dx), _p(dwg), _p(dwu), _p(dwd))
+                              float(l1), _p(dx), _p(dwg), _p(dwu), _p(dwd))
     if rc:
         raise MemoryError("oracle backward ran out of memory")
     return dx, dwg, dwu, dwd
 
 
-def bwd_dense(x, dy, wg_t, wu_t, wd):
-    """Dense backward of the layer; returns (dx, dwg_t, dwu_t, dwd)."""
+def bwd_dense(x, dy, wg_t, wu_t, wd, l1: float = 0.0):
+    """Dense backward of the layer (with the gradient of the activation
+    penalty l1 * sum(ReLU(x W_g))); returns (dx, dwg_t, dwu_t, dwd)."""
     x, dy, wg_t, wu_t, wd = map(_f64, (x, dy, wg_t, wu_t, wd))
     T, dm = x.shape
     dff = wg_t.shape[0]
     dx = np.empty((T, dm))
     dwg, dwu, dwd = (np.empty((dff, dm)) for _ in range(3))
-    rc = lib().orc_bwd_dense(_p(x), _p(dy), T, dm, dff, _p(wg_t), _p(wu_t), _p(wd),
+    rc = lib().orc_bwd_dense(_p(x), _p(dy), T, dm, dff, _p(wg_t), _p(wu_t), _p(wd), float(l1),
                              _p(dx), _p(dwg), _p(dwu), _p(dwd))
     if rc:
         raise MemoryError("oracle backward ran out of memory")

@@ -264,6 +264,9 @@ static int hybrid_rows(int T, int dff, const int32_t *row_nnz, const int32_t *ro
  *   a = h u,  du = da h,  dg = da u                    (at P)
  *   dx = du W_u^T + dg W_g^T                          (sparse-to-dense)
  *   dW_d = a^T dy,  dW_u = x^T du,  dW_g = x^T dg      (sparse^T-to-dense)
+ * With an L1 activation penalty l1 * sum(h) added to the loss (the dothoosh
+ * article's training recipe: an L1 term on the FFN activations to induce
+ * sparsity), its gradient l1 * ReLU'(g) adds l1 to dg at every entry of P.
  * Outputs are overwritten; weight gradients are in the storage layouts
  * (dwg_t = dW_g^T, dwu_t = dW_u^T, dwd = dW_d). Overflow rows whose slot is
  * past max_ovf must not occur (the caller checks the capacity flag).
@@ -272,7 +275,7 @@ static int hybrid_rows(int T, int dff, const int32_t *row_nnz, const int32_t *ro
 int orc_bwd_hybrid(const double *x, const double *dy, int T, int dm, int dff,
                    const int32_t *row_nnz, const int32_t *row_slot,
                    const int32_t *ell_col, const double *ell_val, int K, const double *dense,
-                   const double *wg_t, const double *wu_t, const double *wd,
+                   const double *wg_t, const double *wu_t, const double *wd, double l1,
                    double *dx, double *dwg_t, double *dwu_t, double *dwd)
 {
     rows_t r;
@@ -303,7 +306,7 @@ int orc_bwd_hybrid(const double *x, const double *dy, int T, int dm, int dff,
                 double da = dot(dyt, wd + (i64)i * dm, dm);
                 ca[e] = r.h[e] * u;
                 cdu[e] = da * r.h[e];
-                cdg[e] = da * u;
+                cdg[e] = da * u + l1;
                 const double *wui = wu_t + (i64)i * dm, *wgi = wg_t + (i64)i * dm;
                 for (int k = 0; k < dm; ++k) {
                     su[k] += cdu[e] * wui[k];
@@ -353,10 +356,11 @@ int orc_bwd_hybrid(const double *x, const double *dy, int T, int dm, int dff,
 /*
  * Dense backward of the same layer over every (t, i), with ReLU'(g) = [g > 0]:
  * the plain gradient formulas of the dense layer, written without any
- * sparsity, used to check orc_bwd_hybrid on a lossless pattern.
+ * sparsity, used to check orc_bwd_hybrid on a lossless pattern. l1 is the
+ * weight of the activation penalty l1 * sum(ReLU(g)) in the loss.
  */
 int orc_bwd_dense(const double *x, const double *dy, int T, int dm, int dff,
-                  const double *wg_t, const double *wu_t, const double *wd,
+                  const double *wg_t, const double *wu_t, const double *wd, double l1,
                   double *dx, double *dwg_t, double *dwu_t, double *dwd)
 {
     i64 n = (i64)T * dff;
@@ -375,7 +379,7 @@ int orc_bwd_dense(const double *x, const double *dy, int T, int dm, int dff,
             double da = dot(dyt, wd + (i64)i * dm, dm);
             a[(i64)t * dff + i] = h * u;
             du[(i64)t * dff + i] = da * h;
-            dg[(i64)t * dff + i] = g > 0.0 ? da * u : 0.0;
+            dg[(i64)t * dff + i] = g > 0.0 ? da * u + l1 : 0.0;
         }
         double *su = dx + (i64)t * dm; /* first sum, in place */
         double *sg = (double *)malloc(sizeof(double) * dm);

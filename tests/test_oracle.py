@@ -33,16 +33,18 @@ def storage(ex):
     return np.array(ex["x"], np.float64), Wg.T.copy(), Wu.T.copy(), Wd.copy()
 
 
-def torch_layer(x, wg_t, wu_t, wd, dy=None):
-    """Dense layer by torch (float64); returns y and, given dy, the gradients."""
+def torch_layer(x, wg_t, wu_t, wd, dy=None, l1=0.0):
+    """Dense layer by torch (float64); returns y and, given dy, the gradients
+    of sum(y * dy) + l1 * sum(ReLU(x W_g))."""
     X = torch.tensor(x, requires_grad=dy is not None)
     G = torch.tensor(wg_t, requires_grad=dy is not None)
     U = torch.tensor(wu_t, requires_grad=dy is not None)
     D = torch.tensor(wd, requires_grad=dy is not None)
-    y = (torch.relu(X @ G.T) * (X @ U.T)) @ D
+    h = torch.relu(X @ G.T)
+    y = (h * (X @ U.T)) @ D
     if dy is None:
         return y.detach().numpy()
-    y.backward(torch.tensor(dy))
+    ((y * torch.tensor(dy)).sum() + l1 * h.sum()).backward()
     return y.detach().numpy(), X.grad.numpy(), G.grad.numpy(), U.grad.numpy(), D.grad.numpy()
 
 
@@ -207,8 +209,8 @@ def test_forward_matches_torch_row_subset_0p5b(orc):
     np.testing.assert_allclose(y, torch_layer(x, wg_t, wu_t, wd), rtol=1e-9, atol=1e-11)
 
 
-@pytest.mark.parametrize("skew", [0, 5])
-def test_backward_matches_autograd(orc, skew):
+@pytest.mark.parametrize("skew,l1", [(0, 0.0), (5, 0.0), (5, 0.375)])
+def test_backward_matches_autograd(orc, skew, l1):
     d = synth.make_inputs(synth.Workload("t", 40, 64, 256, "f32", 0.08), with_dy=True)
     if skew:
         d = synth.make_inputs(synth.Workload("t", 40, 64, 256, "f32", 0.08, skew_frac=0.125,
@@ -219,16 +221,18 @@ def test_backward_matches_autograd(orc, skew):
     K = int(np.median(nnz))
     hy = orc.to_hybrid(tw, K=K, max_ovf=40)
     assert 0 < hy["n_ovf"] < 40
-    _, gx, gg, gu, gd = torch_layer(x, wg_t, wu_t, wd, dy)
-    got = orc.bwd_hybrid(x, dy, hy, wg_t, wu_t, wd)
+    _, gx, gg, gu, gd = torch_layer(x, wg_t, wu_t, wd, dy, l1=l1)
+    got = orc.bwd_hybrid(x, dy, hy, wg_t, wu_t, wd, l1=l1)
     for a, b in zip(got, (gx, gg, gu, gd)):
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
     # the dense formulas agree with the sparse ones bit for bit (zeros are exact)
-    for a, b in zip(orc.bwd_dense(x, dy, wg_t, wu_t, wd), got):
+    for a, b in zip(orc.bwd_dense(x, dy, wg_t, wu_t, wd, l1=l1), got):
         assert np.array_equal(a, b)
 
 
-def test_backward_finite_differences(orc):
+@pytest.mark.parametrize("l1", [0.0, 0.25])
+def test_backward_finite_differences(orc, l1):
+    """Central differences of sum(y * dy) + l1 * sum(ReLU(x W_g))."""
     rng = np.random.default_rng(7)
     T, dm, dff = 3, 4, 128
     x = rng.standard_normal((T, dm))
@@ -238,10 +242,11 @@ def test_backward_finite_differences(orc):
     assert np.abs(g).min() > 1e-3  # no gate within reach of the kink
 
     def loss(x_, wg_, wu_, wd_):
-        return float((orc.ffn_dense(x_, wg_, wu_, wd_) * dy).sum())
+        penalty = float(np.maximum(x_ @ wg_.T, 0.0).sum())
+        return float((orc.ffn_dense(x_, wg_, wu_, wd_) * dy).sum()) + l1 * penalty
 
     hy = orc.to_hybrid(orc.twell_pack(g), K=128, max_ovf=1)
-    grads = orc.bwd_hybrid(x, dy, hy, wg_t, wu_t, wd)
+    grads = orc.bwd_hybrid(x, dy, hy, wg_t, wu_t, wd, l1=l1)
     params = [x, wg_t, wu_t, wd]
     eps = 1e-6
     for p_idx, grad in enumerate(grads):

@@ -23,7 +23,9 @@ MUTANTS = {
                                            "double u = dot(xt, wg_t + (i64)i * dm, dm);\n            double a = h * u;"),
     "hybrid tie goes to backup": ("if (nnz <= K) {", "if (nnz < K) {"),
     "hybrid backup row id": ("ovf_rows[n] = t;", "ovf_rows[n] = n;"),
-    "bwd dg uses h": ("cdg[e] = da * u;", "cdg[e] = da * r.h[e];"),
+    "bwd dg uses h": ("cdg[e] = da * u + l1;", "cdg[e] = da * r.h[e] + l1;"),
+    "bwd drops the L1 term": ("cdg[e] = da * u + l1;", "cdg[e] = da * u;"),
+    "bwd L1 term weighted by h": ("cdg[e] = da * u + l1;", "cdg[e] = da * u + l1 * r.h[e];"),
     "bwd da from up weights": ("double da = dot(dyt, wd + (i64)i * dm, dm);\n                ca[e]",
                                "double da = dot(dyt, wu_t + (i64)i * dm, dm);\n                ca[e]"),
     "bwd dx sign": ("dxt[k] = su[k] + sg[k];", "dxt[k] = su[k] - sg[k];"),
@@ -40,7 +42,8 @@ PIN_FUNCS = [
     lambda o: pins.test_twell_width_cap(o),
     lambda o: pins.test_hybrid_invariants(o),
     lambda o: pins.test_forward_matches_torch(o),
-    lambda o: pins.test_backward_matches_autograd(o, 5),
+    lambda o: pins.test_backward_matches_autograd(o, 5, 0.0),
+    lambda o: pins.test_backward_matches_autograd(o, 5, 0.375),
     lambda o: pins.test_brute_force_tiny_layer(o),
 ]
 
