@@ -102,7 +102,7 @@ def load() -> ctypes.CDLL:
     L.twell_fwd_workspace_bytes.restype = S
     L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P, P]
     L.hybrid_ffn_bwd.argtypes = [ctypes.c_int, P, P, ctypes.POINTER(HybridC), P, P, P, I,
-                                 P, P, P, P, P, S, P, P, P]
+                                 ctypes.c_float, P, P, P, P, P, S, P, P, P]
     L.hybrid_bwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I, I]
     L.hybrid_bwd_workspace_bytes.restype = S
     L.twell_status_str.argtypes = [ctypes.c_int]
@@ -262,8 +262,9 @@ def bwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf) -> int:
 
 
 def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=None,
-            timing: KernelTimer | None = None):
-    """Returns (dx, dwg_t, dwu_t, dwd), all float32."""
+            timing: KernelTimer | None = None, l1: float = 0.0):
+    """Returns (dx, dwg_t, dwu_t, dwd), all float32; l1 weights an activation
+    penalty l1 * sum(h) whose gradient is included."""
     T, dm = x.shape
     d_ff = wg_t.shape[0]
     if out is None:
@@ -277,7 +278,8 @@ def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=
     ch = hy.c()
     dx, dwg, dwu, dwd = out
     _check(load().hybrid_ffn_bwd(_dt(x), _ptr(x), _ptr(dy), ctypes.byref(ch), _ptr(wg_t),
-                                 _ptr(wu_t), _ptr(wd), dm, _ptr(dx), _ptr(dwg), _ptr(dwu),
+                                 _ptr(wu_t), _ptr(wd), dm, float(l1), _ptr(dx), _ptr(dwg),
+                                 _ptr(dwu),
                                  _ptr(dwd), _ptr(workspace), nbytes, _ptr(status),
                                  _timing(timing), _stream(x.device)), "hybrid_ffn_bwd")
     return out

@@ -12,7 +12,8 @@ size_t fwd_workspace(int dt, int T, int dm, int dff, int W);
 hipError_t launch_to_hybrid(const twell_t *h, const hybrid_t *o, int32_t *status,
                             twell_timing_t *timing, hipStream_t s);
 hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
-                      const void *wg_t, const void *wu_t, const void *wd, int dm, float *dx,
+                      const void *wg_t, const void *wu_t, const void *wd, int dm, float l1,
+                      float *dx,
                       float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
                       twell_timing_t *timing, hipStream_t s);
 size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *offsets);
@@ -173,7 +174,7 @@ size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, in
 
 int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
                    const void *wg_t, const void *wu_t, const void *wd, int32_t d_model,
-                   float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
+                   float l1, float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
                    size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
                    void *stream)
 {
@@ -193,7 +194,9 @@ int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t
     const size_t need = hybrid_bwd_workspace_bytes(dt, h->T, d_model, h->d_ff, h->K, h->max_ovf);
     if (workspace_bytes < need || (need && !workspace))
         return TWELL_E_WORKSPACE;
-    return hip_rc(launch_bwd(dt, x, dy, h, wg_t, wu_t, wd, d_model, dx, dwg_t, dwu_t, dwd,
+    if (!(l1 == l1) || l1 > 3.4e38f || l1 < -3.4e38f) // NaN or infinite
+        return TWELL_E_SHAPE;
+    return hip_rc(launch_bwd(dt, x, dy, h, wg_t, wu_t, wd, d_model, l1, dx, dwg_t, dwu_t, dwd,
                              workspace, dev_status, timing, (hipStream_t)stream));
 }
 

@@ -3,7 +3,9 @@
 // section 2.B.3: sparse-to-dense and dense-to-sparse products in the backward,
 // no dense work on zeros; overflow rows live in a dense backup).
 //
-// With u = x W_u and da = dy W_d^T sampled on P, a = h u, du = da h, dg = da u:
+// With u = x W_u and da = dy W_d^T sampled on P, a = h u, du = da h and
+// dg = da u + l1 (l1: weight of an activation penalty l1 * sum(h) in the
+// loss, whose gradient is l1 on P):
 //   dx = du W_u^T + dg W_g^T,  dW_d = a^T dy,  dW_u = x^T du,  dW_g = x^T dg.
 //
 // ELL rows (gathers, fp32 accumulation, no atomics, deterministic):
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
     const int32_t *__restrict__ colptr, const int32_t *__restrict__ csc,
     const void *__restrict__ ell_val, int T, int K, int dff, const uint8_t *__restrict__ x,
     const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd,
-    int dm, float *__restrict__ coef, float *__restrict__ dwg, float *__restrict__ dwu,
+    int dm, float l1, float *__restrict__ coef, float *__restrict__ dwg, float *__restrict__ dwu,
     float *__restrict__ dwd)
 {
     using E = elem<DT>;
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
                 const float da = wave_sum(geo.dotw(vd[g], wdw));
                 if (e < m) { // uniform
                     const float hh = bcast(h, e);
-                    const float a = hh * u, du = da * hh, dg = hh != 0.f ? da * u : 0.f;
+                    const float a = hh * u, du = da * hh, dg = hh != 0.f ? da * u + l1 : 0.f;
                     // the lane that owns this entry keeps du, dg for the dx pass
                     if (lane == e && idx >= 0) {
                         coef[idx] = du;
@@ -424,8 +426,8 @@ DEVI void ovf_ud_tile(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff,
-    const void *__restrict__ dense, void *__restrict__ inter, size_t stride, int bx, int by,
-    Tiles As, Tiles Bs)
+    const void *__restrict__ dense, float l1, void *__restrict__ inter, size_t stride, int bx,
+    int by, Tiles As, Tiles Bs)
 {
     using E = elem<DT>;
     const int n_ovf = min(*n_ovf_p, max_ovf);
@@ -476,7 +478,7 @@ DEVI void ovf_ud_tile(
                 const float h = E::load1(dense, o), u = au[mi][ni][e], da = ad[mi][ni][e];
                 put_inter<DT>(inter, stride, 0, o, h * u);
                 put_inter<DT>(inter, stride, 1, o, da * h);
-                put_inter<DT>(inter, stride, 2, o, h != 0.f ? da * u : 0.f);
+                put_inter<DT>(inter, stride, 2, o, h != 0.f ? da * u + l1 : 0.f);
             }
 }
 
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(NT, 2) void mask_ud_kernel(
     int32_t *__restrict__ cnt, int n_chunk, int n_mask, const uint8_t *__restrict__ x,
     const uint8_t *__restrict__ dy, const int32_t *__restrict__ ovf_rows,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
-    const uint8_t *__restrict__ wd, int dm, const void *__restrict__ dense,
+    const uint8_t *__restrict__ wd, int dm, const void *__restrict__ dense, float l1,
     void *__restrict__ inter, size_t stride)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_LDS];
@@ -613,7 +615,7 @@ __global__ __launch_bounds__(NT, 2) void mask_ud_kernel(
     }
     const int u = b - n_mask, nx = dff / mt::TILE;
     Tiles t = (Tiles)lds;
-    ovf_ud_tile<DT>(x, dy, ovf_rows, n_ovf_p, max_ovf, wu, wd, dm, dff, dense, inter, stride,
+    ovf_ud_tile<DT>(x, dy, ovf_rows, n_ovf_p, max_ovf, wu, wd, dm, dff, dense, l1, inter, stride,
                     u % nx, u / nx, t, t + 2);
 }
 
@@ -640,8 +642,8 @@ __global__ __launch_bounds__(mt::NT, 2) void ovf_dxdw_kernel(
 
 template <int DT, int NW>
 void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg, const void *wu,
-                const void *wd, int dm, float *dx, float *dwg, float *dwu, float *dwd, uint8_t *ws,
-                int32_t *status, Timer &tm, hipStream_t s)
+                const void *wd, int dm, float l1, float *dx, float *dwg, float *dwu, float *dwd,
+                uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int T = h->T, K = h->K, dff = h->d_ff;
     const Layout L = layout(T, dff, K, h->max_ovf);
@@ -670,7 +672,7 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
         hipLaunchKernelGGL((mask_ud_kernel<DT>), dim3(n_mask + n_ud), dim3(NT), 0, s, h->row_nnz,
                            h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk, n_mask, xb,
                            dyb, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
-                           (const uint8_t *)wd, dm, h->dense, inter, stride);
+                           (const uint8_t *)wd, dm, h->dense, l1, inter, stride);
         tm.mark("mask_ud_kernel");
     }
     hipLaunchKernelGGL(blk_prefix_kernel, dim3((dff + 63) / 64), dim3(NT), 0, s, cnt, L.nblk, dff,
@@ -686,7 +688,7 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     }
     hipLaunchKernelGGL((bwd_neuron_kernel<DT, NW, NWN, GN, NSPLIT>), dim3(dff, NW / NWN),
                        dim3(64 * NSPLIT), 0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
-                       (const uint8_t *)wd, dm, coef, dwg, dwu, dwd);
+                       (const uint8_t *)wd, dm, l1, coef, dwg, dwu, dwd);
     tm.mark("bwd_neuron_kernel");
     if (T > 0) {
         hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, GD>), dim3(rgroups, parts), dim3(NT), 0, s,
@@ -706,14 +708,14 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
 
 template <int DT>
 void launch_dt(const void *x, const void *dy, const hybrid_t *h, const void *wg, const void *wu,
-               const void *wd, int dm, float *dx, float *dwg, float *dwu, float *dwd, uint8_t *ws,
-               int32_t *status, Timer &tm, hipStream_t s)
+               const void *wd, int dm, float l1, float *dx, float *dwg, float *dwu, float *dwd,
+               uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
 #define TW_CASE(N) \
-    case N: launch_all<DT, N>(x, dy, h, wg, wu, wd, dm, dx, dwg, dwu, dwd, ws, status, tm, s); break;
+    case N: launch_all<DT, N>(x, dy, h, wg, wu, wd, dm, l1, dx, dwg, dwu, dwd, ws, status, tm, s); break;
     switch (row_nw<DT>(dm)) {
         TW_CASE(1) TW_CASE(2) TW_CASE(4) TW_CASE(8) TW_CASE(16)
-    default: launch_all<DT, 32>(x, dy, h, wg, wu, wd, dm, dx, dwg, dwu, dwd, ws, status, tm, s);
+    default: launch_all<DT, 32>(x, dy, h, wg, wu, wd, dm, l1, dx, dwg, dwu, dwd, ws, status, tm, s);
     }
 #undef TW_CASE
 }
@@ -736,16 +738,16 @@ size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *
 }
 
 hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
-                      const void *wg_t, const void *wu_t, const void *wd, int dm, float *dx,
-                      float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
-                      twell_timing_t *timing, hipStream_t s)
+                      const void *wg_t, const void *wu_t, const void *wd, int dm, float l1,
+                      float *dx, float *dwg_t, float *dwu_t, float *dwd, void *ws,
+                      int32_t *status, twell_timing_t *timing, hipStream_t s)
 {
     Timer tm(timing, s);
     if (dt == TWELL_BF16)
-        launch_dt<TWELL_BF16>(x, dy, h, wg_t, wu_t, wd, dm, dx, dwg_t, dwu_t, dwd,
+        launch_dt<TWELL_BF16>(x, dy, h, wg_t, wu_t, wd, dm, l1, dx, dwg_t, dwu_t, dwd,
                               (uint8_t *)ws, status, tm, s);
     else
-        launch_dt<TWELL_F32>(x, dy, h, wg_t, wu_t, wd, dm, dx, dwg_t, dwu_t, dwd,
+        launch_dt<TWELL_F32>(x, dy, h, wg_t, wu_t, wd, dm, l1, dx, dwg_t, dwu_t, dwd,
                              (uint8_t *)ws, status, tm, s);
     return hipGetLastError();
 }

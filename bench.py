@@ -87,6 +87,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="0.5b-1pct", choices=sorted(WORKLOADS))
+    p.add_argument("--l1", type=float, default=2e-5,
+                   help="weight of the L1 activation penalty in the backward (training recipe)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--no-dense", action="store_true", help="skip the dense torch leg")
     p.add_argument("--copy-calib", action="store_true",
@@ -147,7 +149,7 @@ def main():
         tw.ffn_fwd(x, twl, wu, wd, y=y, workspace=fws, status=st, timing=tm["ffn_fwd"])
         tw.to_hybrid(twl, w.K, w.max_ovf, out=hy, status=st, timing=tm["to_hybrid"])
         tw.ffn_bwd(x, dy, hy, wg, wu, wd, out=grads, workspace=bws, status=st,
-                   timing=tm["bwd"])
+                   timing=tm["bwd"], l1=a.l1)
 
     for _ in range(a.warmup):
         step()
@@ -291,7 +293,7 @@ def main():
             tws["val"] = f64(torch.from_numpy(tws["val"]).to(torch.bfloat16))
             orc.ffn_twell(X[:Ts], tws, WU, WD)
             hys = orc.to_hybrid(tws, w.K, w.max_ovf)
-            orc.bwd_hybrid(X[:Ts], DY[:Ts], hys, WG, WU, WD)
+            orc.bwd_hybrid(X[:Ts], DY[:Ts], hys, WG, WU, WD, l1=a.l1)
             el += time.perf_counter() - t1
             toks += Ts
             reps += 1
@@ -313,7 +315,7 @@ def main():
                    "TwELL->hybrid, hybrid backward (dx, dW_g, dW_u, dW_d)", "T": T, "d_model": dm, "d_ff": dff,
                    "density": w.density, "measured_density": round(nnz / (T * dff), 5),
                    "nnz": nnz, "nnz_ell": nnz_ell, "n_ovf": n_ovf, "twell_width": w.width,
-                   "K": w.K, "max_ovf": w.max_ovf},
+                   "K": w.K, "max_ovf": w.max_ovf, "l1": a.l1},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "fwd_tokens_per_s": round(T / ((stage_ms["gate_pack"] + stage_ms["ffn_fwd"]) * 1e-3), 1),
         "roofline": roofline,

@@ -183,8 +183,12 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
  * (section 2.B.3 of the summary page: sparse-to-dense and dense-to-sparse
  * products, no dense work on zeros). An entry is in P iff it is stored with a
  * nonzero value; ReLU' = 1 on P. With u = x W_u and da = dy W_d^T sampled on
- * P, a = h u, du = da h and dg = da u:
+ * P, a = h u, du = da h and dg = da u + l1:
  *   dx = du W_u^T + dg W_g^T,  dW_d = a^T dy,  dW_u = x^T du,  dW_g = x^T dg.
+ * l1 is the weight of an L1 activation penalty l1 * sum(h) in the loss (the
+ * training recipe of the dothoosh.com article: an L1 term on the FFN
+ * activations); its gradient adds l1 to dg on P. Pass 0 for none; any scaling
+ * (e.g. by the token count) is the caller's.
  * ELL rows use gathers; backup rows use dense MFMA products.
  *   dy [T][d_model] dtype dt; dx [T][d_model] float32; dwg_t, dwu_t, dwd
  *   [d_ff][d_model] float32 (storage layouts: dwg_t = dW_g^T, dwu_t = dW_u^T,
@@ -194,7 +198,7 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
  * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
  */
 int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
-                   const void *wg_t, const void *wu_t, const void *wd, int32_t d_model,
+                   const void *wg_t, const void *wu_t, const void *wd, int32_t d_model, float l1,
                    float *dx, float *dwg_t, float *dwu_t, float *dwd, void *workspace,
                    size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
                    void *stream);

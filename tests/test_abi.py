@@ -105,10 +105,12 @@ def test_bwd_validation(L):
     need = L.hybrid_bwd_workspace_bytes(tw.TWELL_BF16, 4, 64, 256, 16, 4)
     assert need > 0
 
-    def f(ws=FAKE, nbytes=None, dm=64, dx=FAKE, hh=h, dt=tw.TWELL_BF16):
-        return L.hybrid_ffn_bwd(dt, FAKE, FAKE, ctypes.byref(hh), FAKE, FAKE, FAKE, dm, dx,
+    def f(ws=FAKE, nbytes=None, dm=64, dx=FAKE, hh=h, dt=tw.TWELL_BF16, l1=0.0):
+        return L.hybrid_ffn_bwd(dt, FAKE, FAKE, ctypes.byref(hh), FAKE, FAKE, FAKE, dm, l1, dx,
                                 FAKE, FAKE, FAKE, ws, need if nbytes is None else nbytes,
                                 None, None, None)
+    assert f(l1=float("nan")) == -2
+    assert f(l1=float("inf")) == -2
     assert f(nbytes=need - 1) == -5
     assert f(ws=0) == -5
     assert f(dx=0) == -1

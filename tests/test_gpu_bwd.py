@@ -44,32 +44,36 @@ def upload_hybrid(ref: dict, dtype: str) -> tw.Hybrid:
         torch.tensor([ref["n_ovf"]], dtype=torch.int32, device=DEV))
 
 
-def run_bwd(d, hy, dtype):
+def run_bwd(d, hy, dtype, l1=0.0):
     x, dy, wg, wu, wd = (d[k].to(DEV) for k in ("x", "dy", "wg_t", "wu_t", "wd"))
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = tw.ffn_bwd(x, dy, hy, wg, wu, wd, status=st)
+    out = tw.ffn_bwd(x, dy, hy, wg, wu, wd, status=st, l1=l1)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     return out
 
 
-def oracle_bwd(orc, d, ref):
+def oracle_bwd(orc, d, ref, l1=0.0):
     return orc.bwd_hybrid(f64(d["x"]), f64(d["dy"]), ref, f64(d["wg_t"]), f64(d["wu_t"]),
-                          f64(d["wd"]))
+                          f64(d["wd"]), l1=l1)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T,dm,dff,K,skew", [(1, 64, 128, 8, 0), (150, 192, 384, 12, 9),
-                                             (300, 512, 1024, 40, 21), (77, 320, 256, 128, 0)])
-def test_bwd_integer_exact(orc, dtype, T, dm, dff, K, skew):
-    """Integer inputs: ELL gathers and the backup rows' hi/lo MFMA products are
-    exact, so every gradient matches the oracle bit for bit."""
-    announce("bwd int", dtype, T, dm, dff, K, skew)
+@pytest.mark.parametrize("T,dm,dff,K,skew,l1", [(1, 64, 128, 8, 0, 0.0),
+                                                (150, 192, 384, 12, 9, 0.0),
+                                                (300, 512, 1024, 40, 21, 0.0),
+                                                (77, 320, 256, 128, 0, 0.0),
+                                                (150, 192, 384, 12, 9, 0.5)])
+def test_bwd_integer_exact(orc, dtype, T, dm, dff, K, skew, l1):
+    """Integer inputs (and an L1 weight of 0.5): ELL gathers and the backup
+    rows' hi/lo MFMA products are exact, so every gradient matches the oracle
+    bit for bit."""
+    announce("bwd int", dtype, T, dm, dff, K, skew, l1)
     d = synth.make_integer_inputs(T, dm, dff, dtype, 0.03, with_dy=True, skew_rows=skew)
     ref = oracle_hybrid(orc, d, dtype, K, 64)
     assert (ref["n_ovf"] > 0) == (skew > 0)
-    got = run_bwd(d, upload_hybrid(ref, dtype), dtype)
-    want = oracle_bwd(orc, d, ref)
+    got = run_bwd(d, upload_hybrid(ref, dtype), dtype, l1=l1)
+    want = oracle_bwd(orc, d, ref, l1=l1)
     for n, a, b in zip(NAMES, got, want):
         assert np.array_equal(f64(a), b), n
 
@@ -92,15 +96,16 @@ def test_bwd_gaussian(orc, w):
 
 
 def test_bwd_training_layer_full(orc):
-    """The skewed 1.5B training layer at full size (T = 8192, 410 backup rows):
-    every gradient element against the oracle on the same hybrid."""
+    """The skewed 1.5B training layer at full size (T = 8192, 410 backup rows),
+    with the recipe's L1 weight 2e-5: every gradient element against the
+    oracle on the same hybrid."""
     w = synth.TRAIN_1P5B
     announce("bwd training layer full")
     d = synth.make_inputs(w, with_dy=True)
     ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
     assert ref["n_ovf"] == 410
-    got = run_bwd(d, upload_hybrid(ref, w.dtype), w.dtype)
-    want = oracle_bwd(orc, d, ref)
+    got = run_bwd(d, upload_hybrid(ref, w.dtype), w.dtype, l1=2e-5)
+    want = oracle_bwd(orc, d, ref, l1=2e-5)
     for n, a, b in zip(NAMES, got, want):
         assert_close(a, b, w.dtype, n)
 
