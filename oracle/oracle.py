@@ -42,6 +42,7 @@ def load(path: str) -> ctypes.CDLL:
     L.orc_ffn_twell.argtypes = [P, P, P, P, I, I, I, P, P, I, P]
     L.orc_to_hybrid.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, P]
     D = ctypes.c_double
+    L.orc_ffn_hybrid.argtypes = [P, I, I, I, P, P, P, P, I, P, P, P, P]
     L.orc_bwd_hybrid.argtypes = [P, P, I, I, I, P, P, P, P, I, P, P, P, P, D, P, P, P, P]
     L.orc_bwd_dense.argtypes = [P, P, I, I, I, P, P, P, D, P, P, P, P]
     L.orc_num_threads.argtypes = []
@@ -131,6 +132,23 @@ def to_hybrid(tw: dict, K: int, max_ovf: int) -> dict:
     return {"row_nnz": row_nnz, "row_slot": row_slot, "ell_col": ell_col, "ell_val": ell_val,
             "ovf_rows": ovf_rows[:max_ovf], "dense": dense[:max_ovf], "n_ovf": int(n_ovf[0]),
             "capacity_exceeded": bool(cap), "K": K, "max_ovf": max_ovf, "d_ff": dff}
+
+
+def ffn_hybrid(x, hy: dict, wu_t, wd):
+    """Forward over a hybrid's entries (ELL rows and dense backup rows)."""
+    x, wu_t, wd = map(_f64, (x, wu_t, wd))
+    T, dm = x.shape
+    dff = hy["d_ff"]
+    row_nnz, row_slot, ell_col = _i32(hy["row_nnz"]), _i32(hy["row_slot"]), _i32(hy["ell_col"])
+    ell_val = _f64(hy["ell_val"])
+    dense = _f64(hy["dense"]) if hy["dense"].size else np.zeros((1, dff))
+    assert not hy.get("capacity_exceeded", False)
+    y = np.empty((T, dm))
+    rc = lib().orc_ffn_hybrid(_p(x), T, dm, dff, _p(row_nnz), _p(row_slot), _p(ell_col),
+                              _p(ell_val), hy["K"], _p(dense), _p(wu_t), _p(wd), _p(y))
+    if rc:
+        raise MemoryError("oracle forward ran out of memory")
+    return y
 
 
 def bwd_hybrid(x, dy, hy: dict, wg_t, wu_t, wd, l1: float = 0.0):

@@ -258,6 +258,41 @@ static int hybrid_rows(int T, int dff, const int32_t *row_nnz, const int32_t *ro
 }
 
 /*
+ * Forward over a hybrid (section 2.B.3: the hybrid layout serves the training
+ * forward as well as the backward): y[t] = sum over the row's entries, in
+ * ascending column order, of h * (x[t] . wu_t[i]) * wd[i], the row's entries
+ * being its ELL entries or the nonzeros of its dense backup row. On a
+ * lossless hybrid this is orc_ffn_twell's sum term for term (zero values
+ * contribute exact zeros). Returns 0, or -1 if memory ran out.
+ */
+int orc_ffn_hybrid(const double *x, int T, int dm, int dff, const int32_t *row_nnz,
+                   const int32_t *row_slot, const int32_t *ell_col, const double *ell_val, int K,
+                   const double *dense, const double *wu_t, const double *wd, double *y)
+{
+    rows_t r;
+    if (hybrid_rows(T, dff, row_nnz, row_slot, ell_col, ell_val, K, dense, &r))
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const double *xt = x + (i64)t * dm;
+        double *yt = y + (i64)t * dm;
+        for (int k = 0; k < dm; ++k)
+            yt[k] = 0.0;
+        for (i64 e = r.off[t]; e < r.off[t + 1]; ++e) {
+            int i = r.col[e];
+            double a = r.h[e] * dot(xt, wu_t + (i64)i * dm, dm);
+            const double *wdi = wd + (i64)i * dm;
+            for (int k = 0; k < dm; ++k)
+                yt[k] += a * wdi[k];
+        }
+    }
+    free(r.off);
+    free(r.col);
+    free(r.h);
+    return 0;
+}
+
+/*
  * Backward of y = (h (.) u) W_d, u = x W_u, h = ReLU(x W_g), on the pattern
  * P of a hybrid (section 2.B.3), with ReLU' = 1 on P and 0 off it:
  *   u = x W_u and da = dy W_d^T sampled at P          (dense-to-sparse)

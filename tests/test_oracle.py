@@ -113,10 +113,11 @@ def test_worked_example_hybrid_and_backward(orc):
     assert h1["dense"][:2].tolist() == r["dense"]
     want = [np.array(ex[k], np.float64) for k in ("dx", "dW_g", "dW_u", "dW_d")]
     want[1], want[2] = want[1].T, want[2].T  # storage layouts of dW_g, dW_u
-    for hy in (h2, h1):  # all-ELL and all-backup give the same gradients
+    for hy in (h2, h1):  # all-ELL and all-backup give the same gradients and y
         got = orc.bwd_hybrid(x, dy, hy, wg_t, wu_t, wd)
         for a, b in zip(got, want):
             assert np.array_equal(a, b)
+        assert np.array_equal(orc.ffn_hybrid(x, hy, wu_t, wd), np.array(ex["y"], np.float64))
     for a, b in zip(orc.bwd_dense(x, dy, wg_t, wu_t, wd), want):
         assert np.array_equal(a, b)
 
@@ -192,6 +193,23 @@ def test_hybrid_invariants(orc):
     assert small["capacity_exceeded"] and small["n_ovf"] == len(ovf)
 
 
+@pytest.mark.parametrize("kind", ["gauss", "int"])
+def test_hybrid_forward_equals_twell_forward(orc, kind):
+    """The hybrid-routed forward (ELL rows + dense backup rows) sums the same
+    terms in the same order as the TwELL forward: bitwise equal."""
+    if kind == "int":
+        d = synth.make_integer_inputs(96, 128, 512, "f32", 0.03, skew_rows=9)
+    else:
+        d = synth.make_inputs(synth.Workload("t", 80, 96, 384, "f32", 0.05, skew_frac=0.1,
+                                             skew_density=0.4))
+    x, wg_t, wu_t, wd = (f64(d[k]) for k in ("x", "wg_t", "wu_t", "wd"))
+    tw = orc.twell_pack(orc.gate(x, wg_t))
+    K = int(np.median(tw["count"].sum(1)))
+    hy = orc.to_hybrid(tw, K=K, max_ovf=64)
+    assert 0 < hy["n_ovf"] < 64
+    assert np.array_equal(orc.ffn_hybrid(x, hy, wu_t, wd), orc.ffn_twell(x, tw, wu_t, wd))
+
+
 # ---------------------------------------------------------------- library routines
 def test_forward_matches_torch(orc):
     d = synth.make_inputs(synth.TINY_F32)
@@ -207,6 +225,17 @@ def test_forward_matches_torch_row_subset_0p5b(orc):
     wg_t, wu_t, wd = (f64(d[k]) for k in ("wg_t", "wu_t", "wd"))
     y = orc.ffn_twell(x, orc.twell_pack(orc.gate(x, wg_t), W=128), wu_t, wd)
     np.testing.assert_allclose(y, torch_layer(x, wg_t, wu_t, wd), rtol=1e-9, atol=1e-11)
+
+
+def test_hybrid_forward_matches_torch(orc):
+    d = synth.make_inputs(synth.Workload("t", 40, 64, 256, "f32", 0.08, skew_frac=0.125,
+                                         skew_density=0.5))
+    x, wg_t, wu_t, wd = (f64(d[k]) for k in ("x", "wg_t", "wu_t", "wd"))
+    tw = orc.twell_pack(orc.gate(x, wg_t))
+    hy = orc.to_hybrid(tw, K=int(np.median(tw["count"].sum(1))), max_ovf=40)
+    assert hy["n_ovf"] > 0
+    np.testing.assert_allclose(orc.ffn_hybrid(x, hy, wu_t, wd), torch_layer(x, wg_t, wu_t, wd),
+                               rtol=1e-10, atol=1e-12)
 
 
 @pytest.mark.parametrize("skew,l1", [(0, 0.0), (5, 0.0), (5, 0.375)])

@@ -28,6 +28,10 @@ MUTANTS = {
     "bwd L1 term weighted by h": ("cdg[e] = da * u + l1;", "cdg[e] = da * u + l1 * r.h[e];"),
     "bwd da from up weights": ("double da = dot(dyt, wd + (i64)i * dm, dm);\n                ca[e]",
                                "double da = dot(dyt, wu_t + (i64)i * dm, dm);\n                ca[e]"),
+    "hybrid fwd drops up projection": ("double a = r.h[e] * dot(xt, wu_t + (i64)i * dm, dm);",
+                                       "double a = r.h[e];"),
+    "hybrid fwd down row from up weights": ("const double *wdi = wd + (i64)i * dm;\n            for (int k = 0; k < dm; ++k)\n                yt[k] += a * wdi[k];\n        }\n    }\n    free(r.off);",
+                                            "const double *wdi = wu_t + (i64)i * dm;\n            for (int k = 0; k < dm; ++k)\n                yt[k] += a * wdi[k];\n        }\n    }\n    free(r.off);"),
     "bwd dx sign": ("dxt[k] = su[k] + sg[k];", "dxt[k] = su[k] - sg[k];"),
     "bwd dW_u from dy": ("dwu_t[o + k] += cdu[e] * xt[k];", "dwu_t[o + k] += cdu[e] * dyt[k];"),
     "bwd dW_d from x": ("dwd[o + k] += ca[e] * dyt[k];", "dwd[o + k] += ca[e] * xt[k];"),
@@ -45,6 +49,8 @@ PIN_FUNCS = [
     lambda o: pins.test_backward_matches_autograd(o, 5, 0.0),
     lambda o: pins.test_backward_matches_autograd(o, 5, 0.375),
     lambda o: pins.test_brute_force_tiny_layer(o),
+    lambda o: pins.test_hybrid_forward_equals_twell_forward(o, "int"),
+    lambda o: pins.test_hybrid_forward_matches_torch(o),
 ]
 
 
