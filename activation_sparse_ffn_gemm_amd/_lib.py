@@ -22,7 +22,8 @@ DEV_TILE_OVERFLOW, DEV_OVF_CAPACITY, DEV_BAD_INDEX = 1, 2, 4
 
 # every extern "C" symbol include/twell.h declares
 EXPORTS = ("twell_gate_pack", "twell_ffn_fwd", "twell_fwd_workspace_bytes", "twell_to_hybrid",
-           "hybrid_ffn_bwd", "hybrid_bwd_workspace_bytes", "twell_status_str")
+           "hybrid_ffn_fwd", "hybrid_fwd_workspace_bytes", "hybrid_ffn_bwd",
+           "hybrid_bwd_workspace_bytes", "twell_status_str")
 
 c_i32, c_sz, c_p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
 
@@ -103,11 +104,16 @@ def load() -> ctypes.CDLL:
     L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P, P]
     L.hybrid_ffn_bwd.argtypes = [ctypes.c_int, P, P, ctypes.POINTER(HybridC), P, P, P, I,
                                  ctypes.c_float, P, P, P, P, P, S, P, P, P]
+    L.hybrid_ffn_fwd.argtypes = [ctypes.c_int, P, ctypes.POINTER(HybridC), P, P, I, P, P, S, P,
+                                 P, P]
+    L.hybrid_fwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I, I]
+    L.hybrid_fwd_workspace_bytes.restype = S
     L.hybrid_bwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I, I]
     L.hybrid_bwd_workspace_bytes.restype = S
     L.twell_status_str.argtypes = [ctypes.c_int]
     L.twell_status_str.restype = ctypes.c_char_p
-    for f in ("twell_gate_pack", "twell_ffn_fwd", "twell_to_hybrid", "hybrid_ffn_bwd"):
+    for f in ("twell_gate_pack", "twell_ffn_fwd", "twell_to_hybrid", "hybrid_ffn_fwd",
+              "hybrid_ffn_bwd"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -255,6 +261,27 @@ def to_hybrid(tw: Twell, K, max_ovf, out: Hybrid | None = None, status=None,
     _check(load().twell_to_hybrid(ctypes.byref(ct), ctypes.byref(ch), _ptr(status),
                                   _timing(timing), _stream(tw.val.device)), "twell_to_hybrid")
     return out
+
+
+def hybrid_fwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf) -> int:
+    return int(load().hybrid_fwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf))
+
+
+def hybrid_fwd(x, hy: Hybrid, wu_t, wd, y=None, workspace=None, status=None,
+               timing: KernelTimer | None = None):
+    """Training forward over a hybrid; returns y (float32)."""
+    T, dm = x.shape
+    if y is None:
+        y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
+    need = hybrid_fwd_workspace_bytes(_dt(x), T, dm, hy.d_ff, hy.K, hy.max_ovf)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel()
+    ch = hy.c()
+    _check(load().hybrid_ffn_fwd(_dt(x), _ptr(x), ctypes.byref(ch), _ptr(wu_t), _ptr(wd), dm,
+                                 _ptr(y), _ptr(workspace), nbytes, _ptr(status), _timing(timing),
+                                 _stream(x.device)), "hybrid_ffn_fwd")
+    return y
 
 
 def bwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf) -> int:

@@ -17,6 +17,10 @@ hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybri
                       float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
                       twell_timing_t *timing, hipStream_t s);
 size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *offsets);
+hipError_t launch_hyb_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
+                          const void *wd, int dm, float *y, void *ws, int32_t *status,
+                          twell_timing_t *timing, hipStream_t s);
+size_t hyb_fwd_workspace(int max_ovf, int dff);
 
 namespace {
 
@@ -162,6 +166,40 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
     if (out->T != h->T || out->d_ff != h->d_ff)
         return TWELL_E_SHAPE;
     return hip_rc(launch_to_hybrid(h, out, dev_status, timing, (hipStream_t)stream));
+}
+
+size_t hybrid_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                  int32_t K, int32_t max_ovf)
+{
+    if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
+        return 0;
+    return hyb_fwd_workspace(max_ovf, d_ff);
+}
+
+int hybrid_ffn_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
+                   const void *wd, int32_t d_model, float *y, void *workspace,
+                   size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
+                   void *stream)
+{
+    if (!dtype_ok(dt))
+        return TWELL_E_DTYPE;
+    if (!h || !wu_t || !wd)
+        return TWELL_E_NULL;
+    if (int rc = check_hybrid(h, dt))
+        return rc;
+    if (h->T > 0 && (!x || !y))
+        return TWELL_E_NULL;
+    if (int rc = check_dm(dt, d_model))
+        return rc;
+    if (!a16(x) || !a16(wu_t) || !a16(wd) || !a16(y) || !a16(workspace))
+        return TWELL_E_ALIGN;
+    const size_t need = hybrid_fwd_workspace_bytes(dt, h->T, d_model, h->d_ff, h->K, h->max_ovf);
+    if (workspace_bytes < need || (need && !workspace))
+        return TWELL_E_WORKSPACE;
+    if (h->T == 0)
+        return TWELL_OK;
+    return hip_rc(launch_hyb_fwd(dt, x, h, wu_t, wd, d_model, y, workspace, dev_status, timing,
+                                 (hipStream_t)stream));
 }
 
 size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,

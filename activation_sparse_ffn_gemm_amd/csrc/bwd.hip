@@ -403,23 +403,10 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 
 // ------------------------------------------------------------ 4-6. backup rows
 // Intermediate arrays, each [pad_ovf][dff]: bf16 -> a_hi, a_lo, du_hi, du_lo,
-// dg_hi, dg_lo; f32 -> a, du, dg.
-template <int DT> DEVI void put_inter(void *inter, size_t stride, int q, size_t o, float v);
-template <> DEVI void put_inter<TWELL_BF16>(void *inter, size_t stride, int q, size_t o, float v)
-{
-    uint16_t *p = (uint16_t *)inter;
-    const uint16_t hi = f32_to_bf16(v);
-    p[(2 * q) * stride + o] = hi;
-    p[(2 * q + 1) * stride + o] = f32_to_bf16(v - bf16_to_f32(hi));
-}
-template <> DEVI void put_inter<TWELL_F32>(void *inter, size_t stride, int q, size_t o, float v)
-{
-    ((float *)inter)[q * stride + o] = v;
-}
-
-// LDS of the backup-row GEMM tiles: two double-buffered 128 x 128-byte stages
-typedef uint8_t (*Tiles)[mt::TILE * mt::ROWB];
-constexpr int TILE_LDS = 4 * mt::TILE * mt::ROWB; // As[2] + Bs[2]: 64 KB
+// dg_hi, dg_lo; f32 -> a, du, dg (mt::put_inter).
+using mt::put_inter;
+using mt::Tiles;
+using mt::TILE_LDS;
 
 template <int DT>
 DEVI void ovf_ud_tile(

@@ -173,6 +173,28 @@ DEVI void gemm(Acc &acc, uint8_t (*As)[TILE * ROWB], uint8_t (*Bs)[TILE * ROWB],
     }
 }
 
+// LDS of a 128 x 128 tile GEMM: two double-buffered 128 x 128-byte stages
+typedef uint8_t (*Tiles)[TILE * ROWB];
+constexpr int TILE_LDS = 4 * TILE * ROWB; // As[2] + Bs[2]: 64 KB
+
+// Float32 intermediates of the backup rows' products, array q of [rows][cols]
+// arrays `stride` elements apart. For bf16 inputs each value v is stored as
+// two bf16, hi = bf16(v) and lo = bf16(v - hi) (arrays 2q and 2q + 1), so a
+// bf16 MFMA product over both keeps about 16 significant bits; float32
+// inputs store v as is.
+template <int DT> DEVI void put_inter(void *inter, size_t stride, int q, size_t o, float v);
+template <> DEVI void put_inter<TWELL_BF16>(void *inter, size_t stride, int q, size_t o, float v)
+{
+    uint16_t *p = (uint16_t *)inter;
+    const uint16_t hi = f32_to_bf16(v);
+    p[(2 * q) * stride + o] = hi;
+    p[(2 * q + 1) * stride + o] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+template <> DEVI void put_inter<TWELL_F32>(void *inter, size_t stride, int q, size_t o, float v)
+{
+    ((float *)inter)[q * stride + o] = v;
+}
+
 // Tile coordinates of accumulator element e of block (mi, ni) of this lane.
 DEVI int acc_row(int wm, int mi, int e, int lane) { return wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
 DEVI int acc_col(int wn, int ni, int lane) { return wn * 64 + ni * 32 + (lane & 31); }

@@ -237,6 +237,20 @@ def main():
                 "traffic_note": traffic_note, "launch_ms": round(kern_ms[dom], 4),
                 "work_per_launch": wk, "work_unit": desc}
 
+    # ---- layer memory: what the sparse path keeps between forward and backward
+    # (the hybrid; the TwELL is dropped once converted) and what it needs at
+    # its peak (TwELL + hybrid + workspaces), against the dense layer's below
+    nbytes = lambda *ts: sum(t.numel() * t.element_size() for t in ts)
+    hy_b = nbytes(hy.row_nnz, hy.row_slot, hy.ell_col, hy.ell_val, hy.ovf_rows, hy.dense,
+                  hy.n_ovf)
+    tw_b = nbytes(twl.count, twl.col, twl.val)
+    memory = {"hybrid_bytes": hy_b, "twell_bytes": tw_b, "fwd_workspace_bytes": fws_n,
+              "bwd_workspace_bytes": bws.numel(),
+              "sparse_saved_activation_bytes": hy_b,
+              "sparse_step_peak_bytes": tw_b + hy_b + max(fws_n, bws.numel()),
+              "note": "activation memory only; x, dy, weights, y and gradients are the same "
+                      "for both layers"}
+
     # ---- dense bf16 layer, same shapes, torch (hipBLASLt) as a timed black box
     dense = None
     if not a.no_dense:
@@ -271,10 +285,24 @@ def main():
         with torch.no_grad():
             fwd_ms = timeit(lambda: dense_fwd(x), a.steps)
         train_ms = timeit(dense_train, a.steps)
+        # activation memory of the dense layer: what autograd keeps between
+        # forward and backward, and the step's peak above the resident inputs
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        gu = xr @ p_gu
+        yy = (torch.relu(gu[:, :dff]) * gu[:, dff:]) @ p_d
+        torch.cuda.synchronize()
+        dense_saved = torch.cuda.memory_allocated() - base - yy.numel() * yy.element_size()
+        yy.backward(dy)
+        torch.cuda.synchronize()
+        dense_peak = torch.cuda.max_memory_allocated() - base
+        del gu, yy
         dense = {"fwd_tokens_per_s": round(T / (fwd_ms * 1e-3), 1), "fwd_ms": round(fwd_ms, 4),
                  "train_tokens_per_s": round(T / (train_ms * 1e-3), 1),
                  "train_ms": round(train_ms, 4),
-                 "train_tflops": round(9 * 2.0 * T * dm * dff / (train_ms * 1e-3) / 1e12, 1)}
+                 "train_tflops": round(9 * 2.0 * T * dm * dff / (train_ms * 1e-3) / 1e12, 1),
+                 "saved_activation_bytes": int(dense_saved), "step_peak_bytes": int(dense_peak)}
         del p_gu, p_d, xr
 
     # ---- CPU oracle on this host (bounded sample of the same workload)
@@ -321,6 +349,7 @@ def main():
         "roofline": roofline,
         "kernels": per_kernel,
         "dense_bf16": dense,
+        "memory": memory,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

@@ -9,9 +9,10 @@
  *                  epilogue                                -> twell_gate_pack
  *   section 2.B.2  one fused stage applying the up and down projections to
  *                  the TwELL nonzeros only                  -> twell_ffn_fwd
- *   section 2.B.3  TwELL -> hybrid (ELL rows + dense backup) conversion and
- *                  the sparse<->dense products of the backward
- *                                                   -> twell_to_hybrid,
+ *   section 2.B.3  TwELL -> hybrid (ELL rows + dense backup) conversion, the
+ *                  training forward over the hybrid and the sparse<->dense
+ *                  products of the backward          -> twell_to_hybrid,
+ *                                                      hybrid_ffn_fwd,
  *                                                      hybrid_ffn_bwd
  *
  * Conventions shared by every entry point
@@ -177,6 +178,27 @@ size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int
  */
 int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
                     twell_timing_t *timing, void *stream);
+
+/*
+ * Training forward over a hybrid (section 2.B.3 of the summary page: the
+ * hybrid layout carries the training forward as well as the backward):
+ * y[t] = sum over row t's stored nonzeros (i, h) of h * (x[t] . wu_t[i]) * wd[i],
+ * float32 accumulation. ELL rows use gathers; backup rows use two dense MFMA
+ * products, A = h (.) (x_O W_u) then y_O = A W_d (A kept as a float32
+ * intermediate in the workspace, for bf16 inputs as a hi/lo bf16 pair).
+ *   x [T][d_model] dtype dt; y [T][d_model] float32, every row written.
+ *   workspace: at least hybrid_fwd_workspace_bytes(...) bytes.
+ * Undefined if the hybrid's OVF_CAPACITY bit was raised.
+ * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
+ */
+int hybrid_ffn_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
+                   const void *wd, int32_t d_model, float *y, void *workspace,
+                   size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
+                   void *stream);
+
+/* Workspace bytes hybrid_ffn_fwd needs (0 on invalid arguments). */
+size_t hybrid_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                  int32_t K, int32_t max_ovf);
 
 /*
  * Backward of y = (h (.) x W_u) W_d on the pattern P held by a hybrid

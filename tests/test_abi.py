@@ -118,3 +118,22 @@ def test_bwd_validation(L):
     assert f(dx=FAKE + 8) == -4
     assert f(dt=tw.TWELL_F32) == -3
     assert f(hh=hybrid_c(max_ovf=-2)) == -2
+
+
+def test_hybrid_fwd_validation(L):
+    h = hybrid_c()
+    need = L.hybrid_fwd_workspace_bytes(tw.TWELL_BF16, 4, 64, 256, 16, 4)
+    assert need > 0
+    assert L.hybrid_fwd_workspace_bytes(tw.TWELL_BF16, 4, 64, 256, 16, 0) == 0  # no backup rows
+
+    def f(ws=FAKE, nbytes=None, dm=64, y=FAKE, hh=h, dt=tw.TWELL_BF16, x=FAKE):
+        return L.hybrid_ffn_fwd(dt, x, ctypes.byref(hh), FAKE, FAKE, dm, y, ws,
+                                need if nbytes is None else nbytes, None, None, None)
+    assert f(nbytes=need - 1) == -5
+    assert f(ws=0) == -5
+    assert f(y=0) == -1
+    assert f(x=0) == -1
+    assert f(dm=32) == -2
+    assert f(dt=tw.TWELL_F32) == -3
+    assert f(hh=hybrid_c(K=0)) == -2
+    assert f(y=FAKE + 8) == -4

@@ -1,0 +1,104 @@
+"""GPU parity of hybrid_ffn_fwd (the training forward over the hybrid layout)
+against the oracle's forward over the same hybrid, through the C-ABI.
+
+As for the backward, the hybrid fed to the GPU is the oracle's (values rounded
+to the storage dtype): inputs flow oracle -> GPU only.
+"""
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_ffn_gemm_amd import _lib as tw
+from activation_sparse_ffn_gemm_amd import synth
+from helpers import assert_close, f64
+from test_gpu_bwd import oracle_hybrid, upload_hybrid
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def run_fwd(d, hy):
+    x, wu, wd = (d[k].to(DEV) for k in ("x", "wu_t", "wd"))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = tw.hybrid_fwd(x, hy, wu, wd, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,dm,dff,K,skew", [(1, 64, 128, 8, 0), (150, 192, 384, 12, 9),
+                                             (300, 512, 1024, 40, 21), (77, 320, 256, 128, 0)])
+def test_hybrid_fwd_integer_exact(orc, dtype, T, dm, dff, K, skew):
+    """Integer inputs: the ELL gathers and the backup rows' hi/lo MFMA products
+    are exact, so y matches the oracle bit for bit."""
+    announce("hyb fwd int", dtype, T, dm, dff, K, skew)
+    d = synth.make_integer_inputs(T, dm, dff, dtype, 0.03, skew_rows=skew)
+    ref = oracle_hybrid(orc, d, dtype, K, 64)
+    assert (ref["n_ovf"] > 0) == (skew > 0)
+    y = run_fwd(d, upload_hybrid(ref, dtype))
+    want = orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"]))
+    assert np.array_equal(f64(y), want)
+
+
+@pytest.mark.parametrize("w", [
+    synth.Workload("small-f32", 96, 256, 512, "f32", 0.03, skew_frac=0.1, skew_density=0.4,
+                   K=40, max_ovf=16),
+    synth.Workload("small-bf16", 200, 384, 640, "bf16", 0.02, skew_frac=0.05, skew_density=0.3,
+                   K=48, max_ovf=16),
+    synth.Workload("all-ell-bf16", 256, 1024, 2816, "bf16", 0.01, K=128, max_ovf=8),
+], ids=lambda w: w.name)
+def test_hybrid_fwd_gaussian(orc, w):
+    announce("hyb fwd gauss", w.name)
+    d = synth.make_inputs(w)
+    ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
+    y = run_fwd(d, upload_hybrid(ref, w.dtype))
+    assert_close(y, orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"])), w.dtype, "y")
+
+
+def test_hybrid_fwd_training_layer_full(orc):
+    """The skewed 1.5B training layer at full size (T = 8192, 410 backup rows
+    holding most of the nonzeros): every y element against the oracle."""
+    w = synth.TRAIN_1P5B
+    announce("hyb fwd training layer full")
+    d = synth.make_inputs(w)
+    ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
+    assert ref["n_ovf"] == 410
+    y = run_fwd(d, upload_hybrid(ref, w.dtype))
+    assert_close(y, orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"])), w.dtype, "y")
+
+
+def test_hybrid_fwd_agrees_with_twell_fwd():
+    """On one TwELL, the forward over its hybrid and the TwELL forward are the
+    same sums (GPU against GPU; each is checked against the oracle above)."""
+    w = synth.Workload("e2e", 512, 256, 768, "bf16", 0.02, skew_frac=0.05, skew_density=0.3,
+                       K=40, max_ovf=64, width=128)
+    announce("hyb fwd vs twell fwd")
+    d = synth.make_inputs(w)
+    x, wg, wu, wd = (d[k].to(DEV) for k in ("x", "wg_t", "wu_t", "wd"))
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    t = tw.gate_pack(x, wg, width=w.width, status=st)
+    y_tw = tw.ffn_fwd(x, t, wu, wd, status=st)
+    hy = tw.to_hybrid(t, w.K, w.max_ovf, status=st)
+    y_hy = tw.hybrid_fwd(x, hy, wu, wd, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(hy.n_ovf.item()) > 0
+    np.testing.assert_allclose(f64(y_hy), f64(y_tw), rtol=2e-5, atol=2e-5 * float(y_tw.abs().max()))
+
+
+def test_hybrid_fwd_empty_and_no_backup(orc):
+    announce("hyb fwd empty")
+    hy0 = tw.empty_hybrid(0, 256, 16, 4, torch.bfloat16, DEV)
+    hy0.n_ovf.zero_()
+    x0 = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    wu = torch.zeros((256, 64), dtype=torch.bfloat16, device=DEV)
+    assert tw.hybrid_fwd(x0, hy0, wu, wu).shape == (0, 64)
+    d = synth.make_integer_inputs(40, 128, 256, "bf16", 0.03)
+    ref = oracle_hybrid(orc, d, "bf16", 128, 0)
+    assert ref["n_ovf"] == 0
+    y = run_fwd(d, upload_hybrid(ref, "bf16"))
+    assert np.array_equal(f64(y), orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"])))
