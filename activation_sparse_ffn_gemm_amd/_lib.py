@@ -21,9 +21,11 @@ TILE_C = 128
 DEV_TILE_OVERFLOW, DEV_OVF_CAPACITY, DEV_BAD_INDEX = 1, 2, 4
 
 # every extern "C" symbol include/twell.h declares
-EXPORTS = ("twell_gate_pack", "twell_ffn_fwd", "twell_fwd_workspace_bytes", "twell_to_hybrid",
-           "hybrid_ffn_fwd", "hybrid_fwd_workspace_bytes", "hybrid_ffn_bwd",
-           "hybrid_bwd_workspace_bytes", "twell_status_str")
+EXPORTS = ("twell_gate_pack", "twell_gate_workspace_bytes", "twell_ffn_fwd", "twell_fwd_workspace_bytes", "twell_decode_fwd",
+           "twell_decode_workspace_bytes", "twell_to_hybrid", "hybrid_ffn_fwd",
+           "hybrid_fwd_workspace_bytes", "hybrid_ffn_bwd", "hybrid_bwd_workspace_bytes",
+           "twell_status_str")
+DECODE_T = 64  # most tokens twell_decode_fwd takes (few-token kernels up to here)
 
 c_i32, c_sz, c_p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
 
@@ -96,11 +98,18 @@ def load() -> ctypes.CDLL:
                          "(the HIP library is the only implementation; there is no fallback)")
     L = ctypes.CDLL(LIB_PATH)
     P, I, S = c_p, c_i32, c_sz
-    L.twell_gate_pack.argtypes = [ctypes.c_int, P, P, I, I, ctypes.POINTER(TwellC), P, P, P]
+    L.twell_gate_pack.argtypes = [ctypes.c_int, P, P, I, I, ctypes.POINTER(TwellC), P, S, P, P,
+                                  P]
+    L.twell_gate_workspace_bytes.argtypes = [ctypes.c_int, I, I, I]
+    L.twell_gate_workspace_bytes.restype = S
     L.twell_ffn_fwd.argtypes = [ctypes.c_int, P, ctypes.POINTER(TwellC), P, P, I, P, P, S, P, P,
                                 P]
     L.twell_fwd_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I]
     L.twell_fwd_workspace_bytes.restype = S
+    L.twell_decode_fwd.argtypes = [ctypes.c_int, P, P, P, P, I, ctypes.POINTER(TwellC), P, P,
+                                   S, P, P, P]
+    L.twell_decode_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I]
+    L.twell_decode_workspace_bytes.restype = S
     L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P, P]
     L.hybrid_ffn_bwd.argtypes = [ctypes.c_int, P, P, ctypes.POINTER(HybridC), P, P, P, I,
                                  ctypes.c_float, P, P, P, P, P, S, P, P, P]
@@ -112,8 +121,8 @@ def load() -> ctypes.CDLL:
     L.hybrid_bwd_workspace_bytes.restype = S
     L.twell_status_str.argtypes = [ctypes.c_int]
     L.twell_status_str.restype = ctypes.c_char_p
-    for f in ("twell_gate_pack", "twell_ffn_fwd", "twell_to_hybrid", "hybrid_ffn_fwd",
-              "hybrid_ffn_bwd"):
+    for f in ("twell_gate_pack", "twell_ffn_fwd", "twell_decode_fwd", "twell_to_hybrid",
+              "hybrid_ffn_fwd", "hybrid_ffn_bwd"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -221,15 +230,23 @@ def _timing(t):
     return None if t is None else t.arg()
 
 
+def gate_workspace_bytes(dtype, T, d_model, d_ff) -> int:
+    return int(load().twell_gate_workspace_bytes(dtype, T, d_model, d_ff))
+
+
 def gate_pack(x, wg_t, width=TILE_C, out: Twell | None = None, status=None,
-              timing: KernelTimer | None = None) -> Twell:
+              timing: KernelTimer | None = None, workspace=None) -> Twell:
     T, dm = x.shape
     if out is None:
         out = empty_twell(T, wg_t.shape[0], width, x.dtype, x.device)
+    need = gate_workspace_bytes(_dt(x), T, dm, wg_t.shape[0])
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     c = out.c()
     _check(load().twell_gate_pack(_dt(x), _ptr(x), _ptr(wg_t), T, dm, ctypes.byref(c),
-                                  _ptr(status), _timing(timing), _stream(x.device)),
-           "twell_gate_pack")
+                                  _ptr(workspace), nbytes, _ptr(status), _timing(timing),
+                                  _stream(x.device)), "twell_gate_pack")
     return out
 
 
@@ -251,6 +268,32 @@ def ffn_fwd(x, tw: Twell, wu_t, wd, y=None, workspace=None, status=None,
                                 _ptr(y), _ptr(workspace), nbytes, _ptr(status),
                                 _timing(timing), _stream(x.device)), "twell_ffn_fwd")
     return y
+
+
+def decode_workspace_bytes(dtype, T, d_model, d_ff, width) -> int:
+    return int(load().twell_decode_workspace_bytes(dtype, T, d_model, d_ff, width))
+
+
+def decode_fwd(x, wg_t, wu_t, wd, width=TILE_C, out: Twell | None = None, y=None,
+               workspace=None, status=None, timing: KernelTimer | None = None):
+    """The whole layer for T <= DECODE_T tokens in one launch; returns
+    (TwELL of h, y float32)."""
+    T, dm = x.shape
+    d_ff = wg_t.shape[0]
+    if out is None:
+        out = empty_twell(T, d_ff, width, x.dtype, x.device)
+    if y is None:
+        y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
+    need = decode_workspace_bytes(_dt(x), T, dm, d_ff, out.width)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel()
+    c = out.c()
+    _check(load().twell_decode_fwd(_dt(x), _ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), dm,
+                                   ctypes.byref(c), _ptr(y), _ptr(workspace), nbytes,
+                                   _ptr(status), _timing(timing), _stream(x.device)),
+           "twell_decode_fwd")
+    return out, y
 
 
 def to_hybrid(tw: Twell, K, max_ovf, out: Hybrid | None = None, status=None,

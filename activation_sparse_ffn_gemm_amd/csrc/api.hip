@@ -3,8 +3,9 @@
 #include "common.hpp"
 
 hipError_t launch_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int T, int dm,
-                            const twell_t *o, int32_t *status, twell_timing_t *timing,
+                            const twell_t *o, void *ws, int32_t *status, twell_timing_t *timing,
                             hipStream_t s);
+size_t dec_gate_workspace(int dt, int T, int dm, int dff);
 hipError_t launch_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
                           const void *wd, int dm, float *y, void *ws, int32_t *status,
                           twell_timing_t *timing, hipStream_t s);
@@ -21,6 +22,10 @@ hipError_t launch_hyb_fwd(twell_dtype dt, const void *x, const hybrid_t *h, cons
                           const void *wd, int dm, float *y, void *ws, int32_t *status,
                           twell_timing_t *timing, hipStream_t s);
 size_t hyb_fwd_workspace(int max_ovf, int dff);
+size_t dec_layer_workspace(int dt, int T, int dm, int dff, int W);
+hipError_t launch_dec_layer(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
+                            const void *wd, int dm, const twell_t *o, float *y, void *ws,
+                            int32_t *status, twell_timing_t *timing, hipStream_t s);
 
 namespace {
 
@@ -94,9 +99,16 @@ const char *twell_status_str(int code)
     }
 }
 
+size_t twell_gate_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff)
+{
+    if (!dtype_ok(dt) || T < 0 || check_dm(dt, d_model) || check_dff(d_ff))
+        return 0;
+    return T <= TWELL_DECODE_T ? dec_gate_workspace(dt, T, d_model, d_ff) : 0;
+}
+
 int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, int32_t d_model,
-                    const twell_t *out, int32_t *dev_status, twell_timing_t *timing,
-                    void *stream)
+                    const twell_t *out, void *workspace, size_t workspace_bytes,
+                    int32_t *dev_status, twell_timing_t *timing, void *stream)
 {
     if (!dtype_ok(dt))
         return TWELL_E_DTYPE;
@@ -110,9 +122,14 @@ int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, 
         return TWELL_E_SHAPE;
     if (!a16(x) || !a16(wg_t))
         return TWELL_E_ALIGN;
+    const size_t need = twell_gate_workspace_bytes(dt, T, d_model, out->d_ff);
+    if (workspace_bytes < need || (need && !workspace))
+        return TWELL_E_WORKSPACE;
+    if (!a16(workspace))
+        return TWELL_E_ALIGN;
     if (T == 0)
         return TWELL_OK;
-    return hip_rc(launch_gate_pack(dt, x, wg_t, T, d_model, out, dev_status, timing,
+    return hip_rc(launch_gate_pack(dt, x, wg_t, T, d_model, out, workspace, dev_status, timing,
                                    (hipStream_t)stream));
 }
 
@@ -150,6 +167,46 @@ int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *w
         return TWELL_OK;
     return hip_rc(launch_ffn_fwd(dt, x, h, wu_t, wd, d_model, y, workspace, dev_status, timing,
                                  (hipStream_t)stream));
+}
+
+size_t twell_decode_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                    int32_t width)
+{
+    if (!dtype_ok(dt) || T < 0 || T > TWELL_DECODE_T || check_dm(dt, d_model) ||
+        check_dff(d_ff) || width < 1 || width > TWELL_TILE_C)
+        return 0;
+    return dec_layer_workspace(dt, T, d_model, d_ff, width);
+}
+
+int twell_decode_fwd(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
+                     const void *wd, int32_t d_model, const twell_t *out, float *y,
+                     void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                     twell_timing_t *timing, void *stream)
+{
+    if (!dtype_ok(dt))
+        return TWELL_E_DTYPE;
+    if (!wg_t || !wu_t || !wd || !out)
+        return TWELL_E_NULL;
+    if (int rc = check_twell(out, dt))
+        return rc;
+    if (out->T > 0 && (!x || !y))
+        return TWELL_E_NULL;
+    if (int rc = check_dm(dt, d_model))
+        return rc;
+    if (out->T > TWELL_DECODE_T)
+        return TWELL_E_SHAPE;
+    if (!a16(x) || !a16(wg_t) || !a16(wu_t) || !a16(wd) || !a16(y))
+        return TWELL_E_ALIGN;
+    const size_t need =
+        twell_decode_workspace_bytes(dt, out->T, d_model, out->d_ff, out->width);
+    if (workspace_bytes < need || (need && !workspace))
+        return TWELL_E_WORKSPACE;
+    if (!a16(workspace))
+        return TWELL_E_ALIGN;
+    if (out->T == 0)
+        return TWELL_OK;
+    return hip_rc(launch_dec_layer(dt, x, wg_t, wu_t, wd, d_model, out, y, workspace,
+                                   dev_status, timing, (hipStream_t)stream));
 }
 
 int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,

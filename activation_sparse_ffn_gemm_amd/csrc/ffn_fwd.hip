@@ -404,8 +404,15 @@ void launch_dt(const void *x, const twell_t *h, const void *wu, const void *wd, 
 
 } // namespace
 
+size_t dec_ffn_workspace(int dt, int T, int dm, int dff, int W);
+hipError_t launch_dec_ffn(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,
+                          const void *wd, int dm, float *y, void *ws, int32_t *status, Timer &tm,
+                          hipStream_t s);
+
 size_t fwd_workspace(int dt, int T, int dm, int dff, int W)
 {
+    if (T <= TWELL_DECODE_T)
+        return dec_ffn_workspace(dt, T, dm, dff, W);
     return use_split(dt, T, dm, dff) ? fwd_layout(dt, T, dm, dff, W).total : 0;
 }
 
@@ -414,6 +421,8 @@ hipError_t launch_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const
                           twell_timing_t *timing, hipStream_t s)
 {
     Timer tm(timing, s);
+    if (h->T <= TWELL_DECODE_T) // few tokens: up and down over the whole chip
+        return launch_dec_ffn(dt, x, h, wu_t, wd, dm, y, ws, status, tm, s);
     if (dt == TWELL_BF16)
         launch_dt<TWELL_BF16>(x, h, wu_t, wd, dm, y, (uint8_t *)ws, status, tm, s);
     else

@@ -352,11 +352,16 @@ __global__ __launch_bounds__(NT, MINB) void gate_pack_kernel(
 
 } // namespace
 
+hipError_t launch_dec_gate(twell_dtype dt, const void *x, const void *wg_t, int T, int dm,
+                           const twell_t *o, void *ws, int32_t *status, Timer &tm, hipStream_t s);
+
 hipError_t launch_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int T, int dm,
-                            const twell_t *o, int32_t *status, twell_timing_t *timing,
+                            const twell_t *o, void *ws, int32_t *status, twell_timing_t *timing,
                             hipStream_t s)
 {
     Timer tm(timing, s);
+    if (T <= TWELL_DECODE_T) // few tokens: the tile grid would leave the chip idle
+        return launch_dec_gate(dt, x, wg_t, T, dm, o, ws, status, tm, s);
     const int total = ((o->d_ff + BN - 1) / BN) * ((T + BM - 1) / BM);
     dim3 grid((total + NXCD - 1) / NXCD * NXCD);
     if (dt == TWELL_BF16)

@@ -10,11 +10,11 @@
 
 #include "common.hpp"
 
-constexpr int ACC_NW = 8;
+constexpr int ACC_NW = 8; // words per lane in kernels that hold a row of accumulators
 
 // Fourth word of a raw buffer descriptor on gfx9-family parts: 32-bit data
 // format (needed for the range check of untyped loads), everything else 0.
-constexpr int BUF_DWORD3 = 0x00020000; // words per lane in kernels that hold a row of accumulators
+constexpr int BUF_DWORD3 = 0x00020000;
 
 template <int DT, int NW> struct Row {
     static constexpr int EPW = DT == TWELL_BF16 ? 2 : 1; // elements per word

@@ -71,6 +71,8 @@ enum {
 };
 
 #define TWELL_TILE_C 128 /* columns per TwELL tile: the gate kernel's N tile */
+#define TWELL_DECODE_T 64 /* calls with at most this many tokens take the
+                             few-token (decode) kernels; twell_decode_fwd's limit */
 
 /*
  * Optional per-call kernel timing (host struct, caller-owned; pass NULL for
@@ -146,11 +148,18 @@ typedef struct {
  *   x [T][d_model], wg_t [d_ff][d_model] (dtype dt); out (host struct with
  *   device arrays) sized as documented at twell_t, out->T == T,
  *   out->dtype == dt. Every count of every row < T is written.
- * Errors: NULL / SHAPE / DTYPE / ALIGN / HIP.
+ *   workspace: at least twell_gate_workspace_bytes(...) bytes; that is 0
+ *   (workspace may be NULL) unless T <= TWELL_DECODE_T, where d_model is
+ *   split across workgroups and the partial products of g (float32) pass
+ *   through the workspace before the pack.
+ * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
  */
 int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, int32_t d_model,
-                    const twell_t *out, int32_t *dev_status, twell_timing_t *timing,
-                    void *stream);
+                    const twell_t *out, void *workspace, size_t workspace_bytes,
+                    int32_t *dev_status, twell_timing_t *timing, void *stream);
+
+/* Workspace bytes twell_gate_pack needs (0 on invalid arguments). */
+size_t twell_gate_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff);
 
 /*
  * Fused up and down projections over the TwELL nonzeros (section 2.B.2 of the
@@ -167,6 +176,32 @@ int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *w
 
 size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                  int32_t width);
+
+/*
+ * The whole layer for few tokens in one call: the matrix-vector regime of
+ * decoding (the summary page, section 2.B.1, speaks of the gate product as a
+ * dense matrix-vector kernel whose epilogue packs TwELL; the dothoosh.com
+ * article notes that unstructured sparsity was long thought to pay off only
+ * there). Three launches: gate partials over slices of d_model; per (token,
+ * tile) the partials summed, the tile packed and a = h (x . wu_t[i]) formed
+ * for its nonzeros; y by gathering slices of the wd rows. Nothing is
+ * allocated or synchronised, so a caller may capture the call in a graph.
+ *   out->T = T with 0 <= T <= TWELL_DECODE_T (T == 0: nothing is done);
+ *   x [T][d_model], wg_t, wu_t, wd [d_ff][d_model] (dtype dt).
+ *   out receives the TwELL of h as twell_gate_pack writes it (same counts,
+ *   columns and values); y [T][d_model] float32 is overwritten with
+ *   sum over stored (i, h) of h (x[t] . wu_t[i]) wd[i], float32 accumulation.
+ *   workspace: at least twell_decode_workspace_bytes(...) bytes.
+ * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
+ */
+int twell_decode_fwd(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
+                     const void *wd, int32_t d_model, const twell_t *out, float *y,
+                     void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                     twell_timing_t *timing, void *stream);
+
+/* Workspace bytes twell_decode_fwd needs (0 on invalid arguments). */
+size_t twell_decode_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
+                                    int32_t width);
 
 /*
  * TwELL -> hybrid conversion (section 2.B.3 of the summary page: a dedicated

@@ -48,9 +48,9 @@ def hybrid_c(T=4, d_ff=256, K=16, max_ovf=4, dtype=tw.TWELL_BF16, ptr=FAKE):
     return tw.HybridC(T, d_ff, K, max_ovf, dtype, *([ptr] * 7))
 
 
-def gate(L, dt=tw.TWELL_BF16, x=FAKE, w=FAKE, T=4, dm=64, out=None):
+def gate(L, dt=tw.TWELL_BF16, x=FAKE, w=FAKE, T=4, dm=64, out=None, ws=FAKE, nb=1 << 30):
     out = out or twell_c(T=T)
-    return L.twell_gate_pack(dt, x, w, T, dm, ctypes.byref(out), None, None, None)
+    return L.twell_gate_pack(dt, x, w, T, dm, ctypes.byref(out), ws, nb, None, None, None)
 
 
 def test_gate_pack_validation(L):
@@ -69,6 +69,14 @@ def test_gate_pack_validation(L):
     assert gate(L, x=FAKE + 2) == -4                              # misaligned
     assert gate(L, out=twell_c(ptr=0)) == -1                      # NULL arrays
     assert gate(L, T=0, out=twell_c(T=0, ptr=0)) == 0             # T == 0: no-op
+    need = L.twell_gate_workspace_bytes(tw.TWELL_BF16, 4, 64, 256)
+    assert need >= 4 * 256 * 4                                    # few tokens: partials of g
+    assert gate(L, nb=need - 1) == -5
+    assert gate(L, ws=0, nb=0) == -5
+    assert gate(L, ws=FAKE + 4) == -4
+    assert L.twell_gate_workspace_bytes(tw.TWELL_BF16, 65, 64, 256) == 0  # tiled kernel: none
+    big = twell_c(T=100)
+    assert gate(L, T=100, out=big, ws=0, nb=0, x=FAKE + 2) == -4  # no workspace needed
 
 
 def test_ffn_fwd_validation(L):
@@ -137,3 +145,36 @@ def test_hybrid_fwd_validation(L):
     assert f(dt=tw.TWELL_F32) == -3
     assert f(hh=hybrid_c(K=0)) == -2
     assert f(y=FAKE + 8) == -4
+
+
+def test_decode_fwd_validation(L):
+    t = twell_c()
+    need = L.twell_decode_workspace_bytes(tw.TWELL_BF16, 4, 64, 256, 128)
+    # at least the gate partials (one slice or more) and one float per TwELL slot
+    assert need >= 4 * 256 * 4 + 4 * 2 * 128 * 4
+    assert L.twell_decode_workspace_bytes(tw.TWELL_BF16, 65, 64, 256, 128) == 0   # T limit
+    assert L.twell_decode_workspace_bytes(tw.TWELL_BF16, 4, 96, 256, 128) == 0    # d_model % 64
+    assert L.twell_decode_workspace_bytes(tw.TWELL_BF16, 4, 64, 200, 128) == 0    # d_ff % 128
+    assert L.twell_decode_workspace_bytes(tw.TWELL_F32, 4, 4096, 256, 128) == 0   # fp32 limit
+
+    def f(dt=tw.TWELL_BF16, x=FAKE, w=FAKE, dm=64, tt=t, y=FAKE, ws=FAKE, nb=None):
+        return L.twell_decode_fwd(dt, x, w, w, w, dm, ctypes.byref(tt), y, ws,
+                                  need if nb is None else nb, None, None, None)
+    assert f(dt=9) == -3
+    assert f(w=0) == -1
+    assert f(y=0) == -1
+    assert f(x=0) == -1
+    assert f(dm=100) == -2
+    assert f(tt=twell_c(T=65)) == -2
+    assert f(tt=twell_c(dtype=tw.TWELL_F32)) == -3
+    assert f(y=FAKE + 4) == -4
+    assert f(nb=need - 1) == -5
+    assert f(ws=0) == -5
+    assert f(ws=FAKE + 4) == -4
+    assert f(tt=twell_c(T=0, ptr=0), x=0, y=0, nb=0, ws=0) == 0   # T == 0: no-op
+
+
+def test_few_token_ffn_workspace(L):
+    """twell_ffn_fwd on few tokens keeps one float per TwELL slot."""
+    for T, dff, W in ((1, 6144, 32), (64, 256, 128), (7, 1024, 8)):
+        assert L.twell_fwd_workspace_bytes(tw.TWELL_BF16, T, 2304, dff, W) == T * (dff // 128) * W * 4

@@ -27,10 +27,14 @@ def status_word():
 
 # ------------------------------------------------------------ gate + TwELL
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (200, 256, 384), (333, 512, 1024)])
+@pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (33, 192, 640), (64, 4096, 256),
+                                      (65, 128, 384), (200, 256, 384), (333, 512, 1024)])
 def test_gate_pack_integer_exact(orc, dtype, T, dm, dff):
     """Integer inputs: every sum is exact, so count, col and val match bit for
-    bit, including exact g == 0 ties (not stored)."""
+    bit, including exact g == 0 ties (not stored). T <= 64 runs the few-token
+    kernel (T = 33: a second, one-token chunk), T > 64 the tiled one."""
+    if dtype == "f32" and dm > 2048:
+        pytest.skip("fp32 limit is d_model <= 2048")
     announce("gate_pack int", dtype, T, dm, dff)
     d = synth.make_integer_inputs(T, dm, dff, dtype, 0.03)
     g = orc.gate(f64(d["x"]), f64(d["wg_t"]))
@@ -73,11 +77,13 @@ def test_gate_pack_1p5b_sampled_rows(orc):
     assert_twell_matches(sub, g, w.dtype, w.width)
 
 
-def test_gate_pack_width_overflow(orc):
+@pytest.mark.parametrize("T", [40, 70])
+def test_gate_pack_width_overflow(orc, T):
     """A dense tile (x[:,0] = 0 removes the offset, ~50% positive) with W = 8:
-    true count kept, first 8 columns stored, device flag raised."""
-    announce("gate_pack width overflow")
-    d = synth.make_integer_inputs(70, 128, 256, "bf16", 0.02, skew_rows=70)
+    true count kept, first 8 columns stored, device flag raised (few-token and
+    tiled kernels)."""
+    announce("gate_pack width overflow", T)
+    d = synth.make_integer_inputs(T, 128, 256, "bf16", 0.02, skew_rows=T)
     g = orc.gate(f64(d["x"]), f64(d["wg_t"]))
     ref = orc.twell_pack(g, W=8)
     assert ref["overflow"]
@@ -91,7 +97,7 @@ def test_gate_pack_width_overflow(orc):
     col = out.col.cpu().numpy()
     val = f64(out.val)
     rv = f64(to_storage(ref["val"], "bf16"))
-    for t in range(70):
+    for t in range(T):
         for j in range(2):
             k = n[t, j]
             assert np.array_equal(col[t, j, :k], ref["col"][t, j, :k])
@@ -110,9 +116,10 @@ def test_gate_pack_all_zero_and_empty(orc):
     assert empty.count.shape == (0, 2)
 
 
-def test_gate_pack_deterministic():
-    announce("gate_pack determinism")
-    d = synth.make_inputs(synth.SCALE_0P5B.with_(T=1000))
+@pytest.mark.parametrize("T", [64, 1000])
+def test_gate_pack_deterministic(T):
+    announce("gate_pack determinism", T)
+    d = synth.make_inputs(synth.SCALE_0P5B.with_(T=T))
     x, wg = upload(d, ("x", "wg_t"))
     a = tw.gate_pack(x, wg, width=32)
     b = tw.gate_pack(x, wg, width=32)
@@ -138,7 +145,8 @@ def _fwd_on_oracle_twell(orc, d, dtype, W):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (77, 320, 384), (130, 1024, 512),
-                                      (40, 2304, 768)])
+                                      (40, 2304, 768), (33, 2048, 384), (64, 4096, 256),
+                                      (65, 896, 640)])
 def test_ffn_fwd_integer_exact(orc, dtype, T, dm, dff):
     if dtype == "f32" and dm > 2048:
         pytest.skip("fp32 limit is d_model <= 2048")
@@ -155,6 +163,19 @@ def test_ffn_fwd_on_oracle_twell(orc, w):
     d = synth.make_inputs(w)
     y, y_ref, _ = _fwd_on_oracle_twell(orc, d, w.dtype, w.width)
     assert_close(y, y_ref, w.dtype, "y")
+
+
+@pytest.mark.parametrize("T", [8, 300])
+def test_ffn_fwd_deterministic(T):
+    """Fixed summation order: two calls give the same bits."""
+    announce("ffn_fwd determinism", T)
+    w = synth.DECODE_2B.with_(T=T)
+    x, wg, wu, wd = upload(synth.make_inputs(w))
+    t = tw.gate_pack(x, wg, width=w.width)
+    a = tw.ffn_fwd(x, t, wu, wd)
+    b = tw.ffn_fwd(x, t, wu, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("w", [synth.TINY_F32, synth.SCALE_0P5B] +
