@@ -17,11 +17,11 @@ hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybri
                       float *dx,
                       float *dwg_t, float *dwu_t, float *dwd, void *ws, int32_t *status,
                       twell_timing_t *timing, hipStream_t s);
-size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *offsets);
+size_t bwd_workspace_layout(int dt, int T, int dm, int dff, int K, int max_ovf);
 hipError_t launch_hyb_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
                           const void *wd, int dm, float *y, void *ws, int32_t *status,
                           twell_timing_t *timing, hipStream_t s);
-size_t hyb_fwd_workspace(int max_ovf, int dff);
+size_t hyb_fwd_workspace(int dt, int dm, int max_ovf, int dff);
 size_t dec_layer_workspace(int dt, int T, int dm, int dff, int W);
 hipError_t launch_dec_layer(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
                             const void *wd, int dm, const twell_t *o, float *y, void *ws,
@@ -230,7 +230,7 @@ size_t hybrid_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, in
 {
     if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
         return 0;
-    return hyb_fwd_workspace(max_ovf, d_ff);
+    return hyb_fwd_workspace(dt, d_model, max_ovf, d_ff);
 }
 
 int hybrid_ffn_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
@@ -264,7 +264,7 @@ size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, in
 {
     if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
         return 0;
-    return bwd_workspace_layout(T, d_model, d_ff, K, max_ovf, nullptr);
+    return bwd_workspace_layout(dt, T, d_model, d_ff, K, max_ovf);
 }
 
 int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,

@@ -1,0 +1,588 @@
+// Dense products over the hybrid's backup rows ("Sparser, Faster, Lighter
+// Transformer Language Models", summary page section 2.B.3: rows with many
+// nonzeros go to a dense backup, whose products run densely).
+//
+// O = the backup rows (n_ovf of them, ovf_rows[m] their token rows), h_O
+// their stored h (the backup's dense array), x_O / dy_O their x / dy rows.
+// Forward:
+//   A = h_O (.) (x_O W_u)                        [n_ovf x d_ff]
+//   y_O = A W_d                                  [n_ovf x d_model]
+// Backward, with u = x_O W_u and da = dy_O W_d^T:
+//   a = h_O u,  du = da h_O,  dg = da u + l1 where h_O != 0, else 0
+//   dx_O = du W_u^T + dg W_g^T
+//   dW_d += a^T dy_O,  dW_u += du^T x_O,  dW_g += dg^T x_O
+//
+// Every product runs on the NT main loop (both operands K-contiguous), so
+// operands whose contraction index is their row index get a transposed copy
+// first: W_u, W_g and W_d as [d_model][d_ff], x_O and dy_O as
+// [d_model][rows], and the intermediates a, du, dg are written by the u/da
+// epilogue both as [rows][d_ff] (for dx) and as [d_ff][rows] (for dW). For
+// bf16 inputs a float32 intermediate v is stored as two bf16, hi = bf16(v)
+// and lo = bf16(v - hi), and a product over it runs over both halves (about
+// 16 significant bits); float32 inputs keep one float32 array.
+//
+// y_O and dx_O have few rows and a long K (d_ff, or 2-4 segments of it): K is
+// split over S workgroups per tile, each writing a float32 partial, and a
+// reduction pass adds the S partials in order and stores the rows.
+// Row counts are device values: workgroups whose rows all lie past n_ovf
+// return at once, and the grids are sized for the capacity max_ovf. Work
+// without an ordering between its parts shares a launch (the u/da tiles with
+// the transposes; the dx tiles with the dW tiles), so that a layer without
+// backup rows pays few launches.
+#include "ntgemm.hpp"
+
+namespace {
+
+using C1 = ng::Cfg<128, 128, 2, 2>; // 4 waves, 64 x 64 each
+constexpr int TILE = 128;
+constexpr int TT = 64;              // transpose tile (elements per side)
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+int pad_rows(int max_ovf) { return (max_ovf + TILE - 1) / TILE * TILE; }
+
+// K split of the y_O / dx_O products: a tile of 128 rows gives one
+// workgroup of four waves per CU far too little to overlap (about a third of
+// the MFMA rate, measured); aim at 2048 workgroups over the capacity's tiles
+// (several per CU when about half the capacity is used), at most 16 splits,
+// at least 16 K steps each.
+int split_k(int R, int dm, int nk)
+{
+    const int tiles = (R / TILE) * ((dm + TILE - 1) / TILE);
+    int S = std::max(1, 2048 / std::max(tiles, 1));
+    S = std::min(S, 16);
+    S = std::min(S, std::max(1, nk / 16));
+    return S;
+}
+
+// ---------------------------------------------------------------- transposes
+template <int DT> using Store = typename elem<DT>::storage;
+
+// One TT x TT tile of out[c][r] = in[src(r)][c] for c < cols and r < rows_out,
+// src(r) = r, or gather[r] for r < n_valid and a zero row past it (gather
+// non-null). 256 threads; lds: TT x (TT + 8) elements.
+template <typename T>
+DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols, int rows_out,
+                         const int32_t *__restrict__ gather, int n_valid, int bx, int by,
+                         uint8_t *lds)
+{
+    constexpr int V = 16 / sizeof(T), TP = TT + 8; // elements per 16-byte chunk, LDS pitch
+    T(*tile)[TP] = (T(*)[TP])lds;
+    const int c0 = bx * TT, r0 = by * TT, tid = threadIdx.x;
+    if (gather && r0 >= (n_valid + TT - 1) / TT * TT)
+        return; // never read: the products stop at the padded row count
+    constexpr int CPR = TT / V; // chunks per tile row
+    for (int q = tid; q < TT * CPR; q += 256) {
+        const int r = q / CPR, cc = q % CPR, gr = r0 + r, gc = c0 + cc * V;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (gr < n_valid && gc < cols) {
+            const int sr = gather ? gather[gr] : gr;
+            v = *(const uint4 *)(in + (size_t)sr * cols + gc);
+        }
+        const T *e = (const T *)&v;
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            tile[r][cc * V + k] = e[k];
+    }
+    __syncthreads();
+    for (int q = tid; q < TT * CPR; q += 256) {
+        const int c = q / CPR, rc = q % CPR, gc = c0 + c, gr = r0 + rc * V;
+        if (gc >= cols || gr >= rows_out)
+            continue;
+        T e[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            e[k] = tile[rc * V + k][c];
+        *(uint4 *)(out + (size_t)gc * rows_out + gr) = *(const uint4 *)e;
+    }
+    __syncthreads(); // lds is reused by the workgroup's next tile
+}
+
+// Tiles of a weight transpose [dff][dm] -> [dm][dff]
+DEVI int wt_tiles(int dm, int dff) { return (dm / TT) * (dff / TT); }
+template <int DT>
+DEVI void weight_t_tile(const void *w, void *wt, int dm, int dff, int b, uint8_t *lds)
+{
+    const int nx = dm / TT;
+    transpose_tile<Store<DT>>((const Store<DT> *)w, (Store<DT> *)wt, dm, dff, nullptr, dff, b % nx,
+                              b / nx, lds);
+}
+
+// ---------------------------------------------------------------- products
+DEVI int n_rows(const int32_t *n_ovf_p, int max_ovf) { return min(*n_ovf_p, max_ovf); }
+
+// hi/lo (bf16) or plain (f32) store of an intermediate value
+template <int DT> DEVI void put2(void *base, size_t lo_off, size_t o, float v)
+{
+    if constexpr (DT == TWELL_BF16) {
+        uint16_t *p = (uint16_t *)base;
+        const uint16_t hi = f32_to_bf16(v);
+        p[o] = hi;
+        p[lo_off + o] = f32_to_bf16(v - bf16_to_f32(hi));
+    } else {
+        ((float *)base)[o] = v;
+    }
+}
+
+// u (and da) of one tile of backup rows x neurons; the epilogue writes
+//   fwd (BWD = false): A = h u            -> a [R][dff] (hi, lo)
+//   bwd (BWD = true):  du, dg             -> [R][dff] (hi, lo each)
+//                      a, du, dg          -> [dff][R] (hi, lo each)
+template <int DT, bool BWD>
+DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
+                  const int32_t *__restrict__ ovf_rows, int n, const uint8_t *__restrict__ wu,
+                  const uint8_t *__restrict__ wd, int dm, int dff, int R,
+                  const void *__restrict__ dense, float l1, void *__restrict__ inter,
+                  void *__restrict__ inter_t, int bx, int by, uint8_t *L)
+{
+    using E = elem<DT>;
+    constexpr int esz = sizeof(typename E::storage);
+    constexpr int NH = DT == TWELL_BF16 ? 2 : 1; // arrays per intermediate
+    constexpr int P = TILE * esz + 16;          // row pitch (bytes) of the transposed tile in LDS
+    const int m0 = by * TILE, i0 = bx * TILE;
+    if (m0 >= n)
+        return;
+    const size_t rowbytes = (size_t)dm * esz;
+    const int nk = (int)(rowbytes / ng::ROWB);
+    auto off = [](int kt) { return ng::StepOff{(size_t)kt * ng::ROWB, (size_t)kt * ng::ROWB}; };
+    auto rows_of = [&](const uint8_t *src) {
+        return [=](int r) { return src + (size_t)ovf_rows[min(m0 + r, n - 1)] * rowbytes; };
+    };
+    auto wrows_of = [&](const uint8_t *w) {
+        return [=](int r) { return w + (size_t)(i0 + r) * rowbytes; };
+    };
+    ng::Acc<C1> au;
+    ng::mainloop<C1, DT>(L, rows_of(x), wrows_of(wu), off, 0, nk, au);
+    ng::Acc<C1> ad;
+    if constexpr (BWD)
+        ng::mainloop<C1, DT>(L, rows_of(dy), wrows_of(wd), off, 0, nk, ad);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<C1>(), wn = ng::wave_n<C1>();
+    const size_t plane = (size_t)R * dff; // elements per intermediate array
+    // every h of this lane's elements first: the loads all go out before any
+    // store, instead of one load-wait-store chain per element
+    float hv[C1::MI][C1::NI][16];
+#pragma unroll
+    for (int mi = 0; mi < C1::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C1::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + ng::acc_row<C1>(wm, mi, e, lane);
+                const int i = i0 + ng::acc_col<C1>(wn, ni, lane);
+                hv[mi][ni][e] = m < n ? E::load1(dense, (size_t)m * dff + i) : 0.f;
+            }
+    // a, du, dg of this lane's elements: u's accumulators become a, da's du
+    float dgv[C1::MI][C1::NI][16];
+#pragma unroll
+    for (int mi = 0; mi < C1::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C1::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + ng::acc_row<C1>(wm, mi, e, lane);
+                const int i = i0 + ng::acc_col<C1>(wn, ni, lane);
+                const size_t o = (size_t)m * dff + i;
+                const float h = hv[mi][ni][e], u = au.v[mi][ni][e];
+                au.v[mi][ni][e] = h * u;
+                if constexpr (!BWD) {
+                    put2<DT>(inter, plane, o, h * u);
+                } else {
+                    const float da = ad.v[mi][ni][e];
+                    const float du = da * h, dg = h != 0.f ? da * u + l1 : 0.f;
+                    ad.v[mi][ni][e] = du;
+                    dgv[mi][ni][e] = dg;
+                    put2<DT>(inter, plane, o, du);
+                    put2<DT>((uint8_t *)inter + NH * plane * esz, plane, o, dg);
+                }
+            }
+    if constexpr (BWD) {
+        // Transposed copies [dff][R] of a, du, dg (hi and lo halves for bf16):
+        // each half goes through LDS as [i][m] so that the global stores run
+        // along m, 16 bytes per lane.
+        for (int q = 0; q < 3 * NH; ++q) { // (a, du, dg) x (hi, lo)
+            const int which = q / NH, part = q % NH;
+#pragma unroll
+            for (int mi = 0; mi < C1::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C1::NI; ++ni)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
+                        const int r = ng::acc_row<C1>(wm, mi, 4 * g, lane);
+                        const int c = ng::acc_col<C1>(wn, ni, lane);
+                        uint8_t *dst = L + c * P + r * esz;
+                        float v[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int e = 4 * g + k;
+                            v[k] = which == 0 ? au.v[mi][ni][e]
+                                              : (which == 1 ? ad.v[mi][ni][e] : dgv[mi][ni][e]);
+                        }
+                        if constexpr (DT == TWELL_BF16) {
+                            uint16_t hw[4];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                const uint16_t hi = f32_to_bf16(v[k]);
+                                hw[k] = part == 0 ? hi : f32_to_bf16(v[k] - bf16_to_f32(hi));
+                            }
+                            *(uint2 *)dst = make_uint2(hw[0] | ((uint32_t)hw[1] << 16),
+                                                       hw[2] | ((uint32_t)hw[3] << 16));
+                        } else {
+                            *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                        }
+                    }
+            __syncthreads();
+            uint8_t *tbase = (uint8_t *)inter_t + (size_t)q * plane * esz;
+            constexpr int CPR = TILE * esz / 16; // 16-byte chunks per row
+            for (int t = threadIdx.x; t < TILE * CPR; t += C1::NT) {
+                const int c = t / CPR, ch = t % CPR;
+                *(uint4 *)(tbase + ((size_t)(i0 + c) * R + m0) * esz + ch * 16) =
+                    *(const uint4 *)(L + c * P + ch * 16);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// One tile of partial rows x weights^T over a K split: part[sp][m][d] = sum
+// over the split's K steps of a_q[m][.] . w_q[d][.], for NSEG segments of d_ff
+// each. Segment q reads A array q (arrays `R dff` elements apart) and B array
+// q >> BSHIFT (arrays `dm dff` elements apart).
+template <int DT, int NSEG, int BSHIFT>
+DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ wt, int n, int dm,
+                     int dff, int R, int S, float *__restrict__ part, int bx, int by, int sp,
+                     uint8_t *L)
+{
+    using E = elem<DT>;
+    constexpr int esz = sizeof(typename E::storage);
+    const int m0 = by * TILE, d0 = bx * TILE;
+    if (m0 >= n)
+        return;
+    const size_t rowbytes = (size_t)dff * esz, plane = (size_t)R * dff * esz,
+                 wplane = (size_t)dm * dff * esz;
+    const int spseg = (int)(rowbytes / ng::ROWB), nk = NSEG * spseg;
+    const int kt0 = (int)((long)nk * sp / S), kt1 = (int)((long)nk * (sp + 1) / S);
+    auto off = [&](int kt) {
+        const int q = kt / spseg, kk = kt % spseg;
+        return ng::StepOff{q * plane + (size_t)kk * ng::ROWB,
+                           (q >> BSHIFT) * wplane + (size_t)kk * ng::ROWB};
+    };
+    auto rowa = [&](int r) { return a + (size_t)(m0 + r) * rowbytes; };
+    auto rowb = [&](int r) { return wt + (size_t)min(d0 + r, dm - 1) * rowbytes; };
+    ng::Acc<C1> acc;
+    ng::mainloop<C1, DT>(L, rowa, rowb, off, kt0, kt1, acc);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<C1>(), wn = ng::wave_n<C1>();
+    float *p = part + (size_t)sp * R * dm;
+#pragma unroll
+    for (int mi = 0; mi < C1::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C1::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + ng::acc_row<C1>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<C1>(wn, ni, lane);
+                if (m < n && d < dm)
+                    p[(size_t)m * dm + d] = acc.v[mi][ni][e];
+            }
+}
+
+// One tile of dW[i][d] += sum_m it[i][m] xt[d][m] over the backup rows, z = 0,
+// 1, 2: (dW_d, a, dy), (dW_u, du, x), (dW_g, dg, x); hi and lo segments for bf16.
+template <int DT>
+DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt, int n, int dm,
+                  int dff, int R, float *__restrict__ dwd, float *__restrict__ dwu,
+                  float *__restrict__ dwg, int bx, int by, int z, uint8_t *L)
+{
+    using E = elem<DT>;
+    constexpr int esz = sizeof(typename E::storage);
+    constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
+    constexpr int KE = ng::ROWB / esz; // rows per K step
+    if (n <= 0)
+        return;
+    const int d0 = bx * TILE, i0 = by * TILE;
+    const size_t rowbytes = (size_t)R * esz, plane = (size_t)dff * R * esz;
+    const uint8_t *ta = it + (size_t)z * NH * plane;                  // a / du / dg, hi first
+    const uint8_t *tx = xt + (size_t)(z == 0 ? 1 : 0) * dm * rowbytes; // dy or x
+    float *out = z == 0 ? dwd : (z == 1 ? dwu : dwg);
+    const int spseg = (n + KE - 1) / KE, nk = NH * spseg;
+    auto off = [&](int kt) {
+        const int q = kt / spseg, kk = kt % spseg;
+        return ng::StepOff{q * plane + (size_t)kk * ng::ROWB, (size_t)kk * ng::ROWB};
+    };
+    auto rowa = [&](int r) { return ta + (size_t)(i0 + r) * rowbytes; };
+    auto rowb = [&](int r) { return tx + (size_t)min(d0 + r, dm - 1) * rowbytes; };
+    ng::Acc<C1> acc;
+    ng::mainloop<C1, DT>(L, rowa, rowb, off, 0, nk, acc);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<C1>(), wn = ng::wave_n<C1>();
+    // all of this lane's current dW values first (loads in flight together),
+    // then the sums
+    float cur[C1::MI][C1::NI][16];
+#pragma unroll
+    for (int mi = 0; mi < C1::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C1::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int i = i0 + ng::acc_row<C1>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<C1>(wn, ni, lane);
+                cur[mi][ni][e] = d < dm ? out[(size_t)i * dm + d] : 0.f;
+            }
+#pragma unroll
+    for (int mi = 0; mi < C1::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C1::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int i = i0 + ng::acc_row<C1>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<C1>(wn, ni, lane);
+                if (d < dm)
+                    out[(size_t)i * dm + d] = cur[mi][ni][e] + acc.v[mi][ni][e];
+            }
+}
+
+// ---------------------------------------------------------------- kernels
+constexpr int UD_LDS = C1::LDS > TILE * (4 * TILE + 16) ? C1::LDS : TILE * (4 * TILE + 16);
+
+// forward: the A tiles, then (other workgroups) the W_d transpose
+template <int DT>
+__global__ __launch_bounds__(C1::NT, 2) void bk_a_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ ovf_rows,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
+    const uint8_t *__restrict__ wd, int dm, int dff, int R, const void *__restrict__ dense,
+    void *__restrict__ inter, void *__restrict__ wdt, int n_a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t L[C1::LDS];
+    const int n = n_rows(n_ovf_p, max_ovf);
+    if (n <= 0)
+        return;
+    const int b = blockIdx.x, nx = dff / TILE;
+    if (b < n_a)
+        ud_tile<DT, false>(x, nullptr, ovf_rows, n, wu, nullptr, dm, dff, R, dense, 0.f, inter,
+                           nullptr, b % nx, b / nx, L);
+    else
+        weight_t_tile<DT>(wd, wdt, dm, dff, b - n_a, L);
+}
+
+// backward: the u/da tiles, then the transposes of W_u, W_g, x_O and dy_O
+template <int DT>
+__global__ __launch_bounds__(C1::NT, 1) void bk_ud_kernel(
+    const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
+    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
+    const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wg,
+    const uint8_t *__restrict__ wd, int dm, int dff, int R, const void *__restrict__ dense,
+    float l1, void *__restrict__ inter, void *__restrict__ inter_t, void *__restrict__ wt,
+    void *__restrict__ xt, int n_ud)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t L[UD_LDS];
+    const int n = n_rows(n_ovf_p, max_ovf);
+    if (n <= 0)
+        return;
+    int b = blockIdx.x;
+    const int nx = dff / TILE;
+    if (b < n_ud) {
+        ud_tile<DT, true>(x, dy, ovf_rows, n, wu, wd, dm, dff, R, dense, l1, inter, inter_t,
+                          b % nx, b / nx, L);
+        return;
+    }
+    b -= n_ud;
+    using T = Store<DT>;
+    const int nw = wt_tiles(dm, dff);
+    if (b < 2 * nw) { // W_u^T, W_g^T
+        const int z = b / nw;
+        weight_t_tile<DT>(z ? wg : wu, (T *)wt + (size_t)z * dm * dff, dm, dff, b % nw, L);
+        return;
+    }
+    b -= 2 * nw; // x_O^T, dy_O^T: [dm][R]
+    const int ng_ = (dm / TT) * (R / TT), z = b / ng_, q = b % ng_, gx = dm / TT;
+    transpose_tile<T>((const T *)(z ? dy : x), (T *)xt + (size_t)z * dm * R, dm, R, ovf_rows, n,
+                      q % gx, q / gx, L);
+}
+
+template <int DT, int NH>
+__global__ __launch_bounds__(C1::NT, 2) void bk_y_kernel(
+    const uint8_t *__restrict__ a, const uint8_t *__restrict__ wdt,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
+    float *__restrict__ part)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t L[C1::LDS];
+    rowsw_tile<DT, NH, 4>(a, wdt, n_rows(n_ovf_p, max_ovf), dm, dff, R, S, part, blockIdx.x,
+                          blockIdx.y, blockIdx.z, L);
+}
+
+// backward: the dx_O tiles (K split), then the dW tiles
+template <int DT>
+__global__ __launch_bounds__(C1::NT, 2) void bk_dxdw_kernel(
+    const uint8_t *__restrict__ inter, const uint8_t *__restrict__ wt,
+    const uint8_t *__restrict__ inter_t, const uint8_t *__restrict__ xt,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
+    float *__restrict__ part, float *__restrict__ dwd, float *__restrict__ dwu,
+    float *__restrict__ dwg, int n_dx)
+{
+    constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint8_t L[C1::LDS];
+    const int n = n_rows(n_ovf_p, max_ovf);
+    if (n <= 0)
+        return;
+    int b = blockIdx.x;
+    const int nd = (dm + TILE - 1) / TILE;
+    if (b < n_dx) {
+        // segments (du hi, du lo, dg hi, dg lo) against (W_u^T, W_u^T, W_g^T,
+        // W_g^T), or (du, dg) against (W_u^T, W_g^T)
+        const int mt = R / TILE;
+        rowsw_tile<DT, 2 * NH, NH == 2 ? 1 : 0>(inter, wt, n, dm, dff, R, S, part, b % nd,
+                                                 (b / nd) % mt, b / (nd * mt), L);
+        return;
+    }
+    b -= n_dx;
+    const int ni = dff / TILE;
+    dw_tile<DT>(inter_t, xt, n, dm, dff, R, dwd, dwu, dwg, b % nd, (b / nd) % ni, b / (nd * ni),
+                L);
+}
+
+// out[ovf_rows[m]][d] = sum over s, in order, of part[s][m][d] (m < n_ovf)
+__global__ __launch_bounds__(256) void bk_reduce_kernel(
+    const float *__restrict__ part, int S, const int32_t *__restrict__ ovf_rows,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int R, float *__restrict__ out)
+{
+    const int n = n_rows(n_ovf_p, max_ovf);
+    const int q4 = dm / 4; // float4 per row
+    for (size_t q = blockIdx.x * 256 + threadIdx.x; q < (size_t)n * q4;
+         q += (size_t)gridDim.x * 256) {
+        const int m = (int)(q / q4), c = (int)(q % q4) * 4;
+        float4 v = *(const float4 *)(part + (size_t)m * dm + c);
+        for (int sp = 1; sp < S; ++sp) {
+            const float4 w = *(const float4 *)(part + ((size_t)sp * R + m) * dm + c);
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        *(float4 *)(out + (size_t)ovf_rows[m] * dm + c) = v;
+    }
+}
+
+} // namespace
+
+// ---------------------------------------------------------------- host side
+struct BkLayout {
+    size_t inter, inter_t, xt, wt, part, total;
+    int R, S;
+};
+
+// Workspace of the backup products, bytes from `base`:
+//   inter   [NI][R][dff]  fwd: a (hi, lo); bwd: du, dg (hi, lo each)
+//   inter_t [3][NH][dff][R] bwd only: a, du, dg transposed
+//   xt      [2][dm][R]      bwd only: x_O, dy_O transposed
+//   wt      fwd: W_d^T; bwd: W_u^T, W_g^T ([dm][dff] each)
+//   part    [S][R][dm] float32 partials of y_O / dx_O
+BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
+{
+    BkLayout L{};
+    const size_t esz = dt == TWELL_BF16 ? 2 : 4, nh = dt == TWELL_BF16 ? 2 : 1;
+    L.R = pad_rows(max_ovf);
+    const int nseg = (int)(bwd ? 2 * nh : nh);
+    L.S = split_k(L.R, dm, nseg * (int)(dff * esz / ng::ROWB));
+    size_t o = 0;
+    L.inter = o;   o += up256((bwd ? 2 : 1) * nh * L.R * dff * esz);
+    L.inter_t = o; o += bwd ? up256(3 * nh * L.R * dff * esz) : 0;
+    L.xt = o;      o += bwd ? up256(2 * (size_t)dm * L.R * esz) : 0;
+    L.wt = o;      o += up256((bwd ? 2 : 1) * (size_t)dm * dff * esz);
+    L.part = o;    o += up256((size_t)L.S * L.R * dm * 4);
+    L.total = max_ovf > 0 ? o : 0;
+    return L;
+}
+
+template <int DT>
+void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd, int dm, float *y,
+               uint8_t *ws, Timer &tm, hipStream_t s)
+{
+    const int dff = h->d_ff;
+    const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, false);
+    const int n_a = (dff / TILE) * (L.R / TILE);
+    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a + (dm / TT) * (dff / TT)), dim3(C1::NT), 0, s,
+                       (const uint8_t *)x, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
+                       (const uint8_t *)wd, dm, dff, L.R, h->dense, (void *)(ws + L.inter),
+                       (void *)(ws + L.wt), n_a);
+    tm.mark("bk_a_kernel");
+    constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
+    hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + TILE - 1) / TILE, L.R / TILE, L.S),
+                       dim3(C1::NT), 0, s, (const uint8_t *)(ws + L.inter),
+                       (const uint8_t *)(ws + L.wt), h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
+                       (float *)(ws + L.part));
+    tm.mark("bk_y_kernel");
+    hipLaunchKernelGGL(bk_reduce_kernel, dim3(256), dim3(256), 0, s, (const float *)(ws + L.part),
+                       L.S, h->ovf_rows, h->n_ovf, h->max_ovf, dm, L.R, y);
+    tm.mark("bk_y_reduce_kernel");
+}
+
+template <int DT>
+void bk_ud_dt(const void *x, const void *dy, const hybrid_t *h, const void *wu, const void *wg,
+              const void *wd, int dm, float l1, uint8_t *ws, Timer &tm, hipStream_t s)
+{
+    const int dff = h->d_ff;
+    const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
+    const int n_ud = (dff / TILE) * (L.R / TILE);
+    const int n_t = 2 * (dm / TT) * (dff / TT) + 2 * (dm / TT) * (L.R / TT);
+    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud + n_t), dim3(C1::NT), 0, s,
+                       (const uint8_t *)x, (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
+                       (const uint8_t *)wu, (const uint8_t *)wg, (const uint8_t *)wd, dm, dff, L.R,
+                       h->dense, l1, (void *)(ws + L.inter), (void *)(ws + L.inter_t),
+                       (void *)(ws + L.wt), (void *)(ws + L.xt), n_ud);
+    tm.mark("bk_ud_kernel");
+}
+
+template <int DT>
+void bk_dxdw_dt(const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu, float *dwg,
+                uint8_t *ws, Timer &tm, hipStream_t s)
+{
+    const int dff = h->d_ff;
+    const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
+    const int nd = (dm + TILE - 1) / TILE;
+    const int n_dx = nd * (L.R / TILE) * L.S, n_dw = nd * (dff / TILE) * 3;
+    hipLaunchKernelGGL((bk_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(C1::NT), 0, s,
+                       (const uint8_t *)(ws + L.inter), (const uint8_t *)(ws + L.wt),
+                       (const uint8_t *)(ws + L.inter_t), (const uint8_t *)(ws + L.xt), h->n_ovf,
+                       h->max_ovf, dm, dff, L.R, L.S, (float *)(ws + L.part), dwd, dwu, dwg,
+                       n_dx);
+    tm.mark("bk_dxdw_kernel");
+    hipLaunchKernelGGL(bk_reduce_kernel, dim3(256), dim3(256), 0, s, (const float *)(ws + L.part),
+                       L.S, h->ovf_rows, h->n_ovf, h->max_ovf, dm, L.R, dx);
+    tm.mark("bk_dx_reduce_kernel");
+}
+
+size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd)
+{
+    return bk_layout(dt, dm, dff, max_ovf, bwd).total;
+}
+
+void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
+                   const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s)
+{
+    if (h->max_ovf <= 0 || h->T <= 0)
+        return;
+    if (dt == TWELL_BF16)
+        bk_fwd_dt<TWELL_BF16>(x, h, wu, wd, dm, y, (uint8_t *)ws, tm, s);
+    else
+        bk_fwd_dt<TWELL_F32>(x, h, wu, wd, dm, y, (uint8_t *)ws, tm, s);
+}
+
+void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
+                  const void *wu, const void *wg, const void *wd, int dm, float l1, void *ws,
+                  Timer &tm, hipStream_t s)
+{
+    if (h->max_ovf <= 0 || h->T <= 0)
+        return;
+    if (dt == TWELL_BF16)
+        bk_ud_dt<TWELL_BF16>(x, dy, h, wu, wg, wd, dm, l1, (uint8_t *)ws, tm, s);
+    else
+        bk_ud_dt<TWELL_F32>(x, dy, h, wu, wg, wd, dm, l1, (uint8_t *)ws, tm, s);
+}
+
+void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
+                    float *dwg, void *ws, Timer &tm, hipStream_t s)
+{
+    if (h->max_ovf <= 0 || h->T <= 0)
+        return;
+    if (dt == TWELL_BF16)
+        bk_dxdw_dt<TWELL_BF16>(h, dm, dx, dwd, dwu, dwg, (uint8_t *)ws, tm, s);
+    else
+        bk_dxdw_dt<TWELL_F32>(h, dm, dx, dwd, dwu, dwg, (uint8_t *)ws, tm, s);
+}

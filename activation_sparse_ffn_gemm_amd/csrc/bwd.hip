@@ -25,16 +25,22 @@
 //   5. dx (sparse-to-dense): a wave per (row, part of d_model) sums
 //      du wu_t[i] + dg wg_t[i] over the row's entries.
 // Rows are gathered with 4-byte lanes (rows.hpp).
-// Backup rows (dense MFMA, fp32 accumulation):
-//   6. U/DA: u and da of every backup row and neuron (two 128x128-tile GEMMs
-//      over d_model), then a, du, dg (dg zero where h is zero);
-//   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T, scattered to their rows;
-//   8. DW:   dW += [a | du | dg]^T [dy | x | x] over the backup rows.
-// For bf16 inputs, the fp32 intermediates a, du, dg enter the MFMA as a pair
-// of bf16 (hi + lo, 16 significant bits), so products 7 and 8 run over a K
-// twice as long; fp32 inputs use fp32 MFMA directly.
+// Backup rows (dense MFMA, fp32 accumulation; the products live in
+// backup.hip):
+//   6. U/DA: u and da of every backup row and neuron, then a, du, dg (dg zero
+//      where h is zero), launched before the ELL passes;
+//   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T, stored to their rows;
+//   8. DW:   dW += [a | du | dg]^T [dy | x | x] over the backup rows, after the
+//      neuron pass has written every dW row.
 #include "mfma_tile.hpp"
 #include "rows.hpp"
+
+size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
+void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
+                  const void *wu, const void *wg, const void *wd, int dm, float l1, void *ws,
+                  Timer &tm, hipStream_t s);
+void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
+                    float *dwg, void *ws, Timer &tm, hipStream_t s);
 
 namespace {
 
@@ -45,22 +51,21 @@ constexpr int CH = 1024;  // neurons per workgroup of the mask launch (8 KB of L
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t coef, masks, cnt, colptr, csc, inter, total;
-    int nblk, pad_ovf;
+    size_t coef, masks, cnt, colptr, csc, backup, total;
+    int nblk;
 };
 
-Layout layout(int T, int dff, int K, int max_ovf)
+Layout layout(int dt, int T, int dm, int dff, int K, int max_ovf)
 {
     Layout L;
     L.nblk = (T + BR - 1) / BR;
-    L.pad_ovf = (max_ovf + mt::TILE - 1) / mt::TILE * mt::TILE;
     size_t o = 0;
     L.coef = o;   o += up256((size_t)2 * T * K * 4); // du, dg per ELL slot
     L.masks = o;  o += up256((size_t)L.nblk * dff * 8);
     L.cnt = o;    o += up256((size_t)L.nblk * dff * 4);
     L.colptr = o; o += up256((size_t)(dff + 1) * 4);
     L.csc = o;    o += up256((size_t)T * K * 4);
-    L.inter = o;  o += up256((size_t)12 * L.pad_ovf * dff); // 6 bf16 or 3 f32 arrays
+    L.backup = o; o += up256(bk_workspace(dt, dm, dff, max_ovf, true));
     L.total = o;
     return L;
 }
@@ -401,230 +406,17 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
     geo.store_f(dx, t, acc);
 }
 
-// ------------------------------------------------------------ 4-6. backup rows
-// Intermediate arrays, each [pad_ovf][dff]: bf16 -> a_hi, a_lo, du_hi, du_lo,
-// dg_hi, dg_lo; f32 -> a, du, dg (mt::put_inter).
-using mt::put_inter;
-using mt::Tiles;
-using mt::TILE_LDS;
-
-template <int DT>
-DEVI void ovf_ud_tile(
-    const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
-    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
-    const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff,
-    const void *__restrict__ dense, float l1, void *__restrict__ inter, size_t stride, int bx,
-    int by, Tiles As, Tiles Bs)
-{
-    using E = elem<DT>;
-    const int n_ovf = min(*n_ovf_p, max_ovf);
-    const int m0 = by * mt::TILE, n0 = bx * mt::TILE;
-    if (m0 >= n_ovf)
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const size_t rowbytes = (size_t)dm * sizeof(typename E::storage);
-    const int nk = (int)(rowbytes / mt::ROWB);
-    int src[4]; // source row of each staged A row (-1 past n_ovf)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid + mt::NT * i) >> 3;
-        src[i] = m0 + r < n_ovf ? ovf_rows[m0 + r] : -1;
-    }
-    auto gather_rows = [&](const uint8_t *base) {
-        return [=](mt::Stage &st, int kt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = (tid + mt::NT * i) & 7;
-                st.v[i] = src[i] >= 0 ? ldg16(base + (size_t)src[i] * rowbytes + (size_t)kt * mt::ROWB + c * 16)
-                                      : make_uint4(0, 0, 0, 0);
-            }
-        };
-    };
-    auto weight_rows = [&](const uint8_t *base) {
-        return [=](mt::Stage &st, int kt) {
-            mt::load_k(st, [&](int r) { return base + (size_t)(n0 + r) * rowbytes + (size_t)kt * mt::ROWB; }, tid);
-        };
-    };
-    auto put = [&](uint8_t *S, const mt::Stage &st) { mt::store_k(S, st, tid); };
-    mt::Acc au, ad;
-    mt::zero(au);
-    mt::zero(ad);
-    mt::gemm<DT>(au, As, Bs, nk, gather_rows(x), put, weight_rows(wu), put, wm, wn, lane);
-    mt::gemm<DT>(ad, As, Bs, nk, gather_rows(dy), put, weight_rows(wd), put, wm, wn, lane);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + mt::acc_row(wm, mi, e, lane);
-                if (m >= n_ovf)
-                    continue;
-                const int i = n0 + mt::acc_col(wn, ni, lane);
-                const size_t o = (size_t)m * dff + i;
-                const float h = E::load1(dense, o), u = au[mi][ni][e], da = ad[mi][ni][e];
-                put_inter<DT>(inter, stride, 0, o, h * u);
-                put_inter<DT>(inter, stride, 1, o, da * h);
-                put_inter<DT>(inter, stride, 2, o, h != 0.f ? da * u + l1 : 0.f);
-            }
-}
-
-template <int DT>
-DEVI void ovf_dx_tile(
-    const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
-    const uint8_t *__restrict__ wg, int dm, int dff, float *__restrict__ dx, int bx, int by,
-    Tiles As, Tiles Bs)
-{
-    using E = elem<DT>;
-    constexpr int esz = sizeof(typename E::storage);
-    constexpr int KE = mt::ROWB / esz;
-    constexpr int NSEG = DT == TWELL_BF16 ? 4 : 2; // (du hi, du lo, dg hi, dg lo) or (du, dg)
-    const int n_ovf = min(*n_ovf_p, max_ovf);
-    const int m0 = by * mt::TILE, n0 = bx * mt::TILE;
-    if (m0 >= n_ovf)
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const size_t rowbytes = (size_t)dm * esz;
-    const int spseg = dff / KE; // K steps per segment
-    const uint8_t *ibase = (const uint8_t *)inter;
-    auto load_a = [&](mt::Stage &st, int kt) {
-        const int seg = kt / spseg, k0 = (kt % spseg) * KE;
-        const uint8_t *arr = ibase + (size_t)(NSEG == 4 ? 2 + seg : 1 + seg) * stride * esz;
-        mt::load_k(st, [&](int r) {
-            return m0 + r < n_ovf ? arr + ((size_t)(m0 + r) * dff + k0) * esz : (const uint8_t *)nullptr;
-        }, tid);
-    };
-    auto load_b = [&](mt::Stage &st, int kt) {
-        const int seg = kt / spseg, k0 = (kt % spseg) * KE;
-        const uint8_t *w = seg < NSEG / 2 ? wu : wg;
-        mt::load_mn<DT>(st, [&](int kk) { return w + (size_t)(k0 + kk) * rowbytes + (size_t)n0 * esz; },
-                        [&](int r0) { return n0 + r0 < dm; }, tid);
-    };
-    auto put_a = [&](uint8_t *S, const mt::Stage &st) { mt::store_k(S, st, tid); };
-    auto put_b = [&](uint8_t *S, const mt::Stage &st) { mt::store_mn<DT>(S, st, tid); };
-    mt::Acc acc;
-    mt::zero(acc);
-    mt::gemm<DT>(acc, As, Bs, NSEG * spseg, load_a, put_a, load_b, put_b, wm, wn, lane);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = m0 + mt::acc_row(wm, mi, e, lane);
-            if (m >= n_ovf)
-                continue;
-            const size_t drow = (size_t)ovf_rows[m] * dm;
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int n = n0 + mt::acc_col(wn, ni, lane);
-                if (n < dm)
-                    dx[drow + n] = acc[mi][ni][e];
-            }
-        }
-}
-
-template <int DT>
-DEVI void ovf_dw_tile(
-    const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ x,
-    const uint8_t *__restrict__ dy, int dm, int dff, float *__restrict__ dwd,
-    float *__restrict__ dwu, float *__restrict__ dwg, int bx, int by, int z, Tiles As, Tiles Bs)
-{
-    using E = elem<DT>;
-    constexpr int esz = sizeof(typename E::storage);
-    constexpr int KE = mt::ROWB / esz;
-    constexpr int NSEG = DT == TWELL_BF16 ? 2 : 1; // hi, lo
-    const int n_ovf = min(*n_ovf_p, max_ovf);
-    if (n_ovf <= 0)
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    // z = 0: dW_d from (a, dy); 1: dW_u from (du, x); 2: dW_g from (dg, x)
-    const int i0 = by * mt::TILE, n0 = bx * mt::TILE;
-    const uint8_t *src = z == 0 ? dy : x;
-    float *out = z == 0 ? dwd : (z == 1 ? dwu : dwg);
-    const size_t rowbytes = (size_t)dm * esz;
-    const int spseg = (n_ovf + KE - 1) / KE;
-    const uint8_t *ibase = (const uint8_t *)inter;
-    auto load_a = [&](mt::Stage &st, int kt) {
-        const int seg = kt / spseg, k0 = (kt % spseg) * KE;
-        const uint8_t *arr = ibase + (size_t)(NSEG * z + seg) * stride * esz;
-        mt::load_mn<DT>(st, [&](int kk) {
-            const int m = k0 + kk;
-            return m < n_ovf ? arr + ((size_t)m * dff + i0) * esz : (const uint8_t *)nullptr;
-        }, [&](int) { return true; }, tid);
-    };
-    auto load_b = [&](mt::Stage &st, int kt) {
-        const int k0 = (kt % spseg) * KE;
-        mt::load_mn<DT>(st, [&](int kk) {
-            const int m = k0 + kk;
-            return m < n_ovf ? src + (size_t)ovf_rows[m] * rowbytes + (size_t)n0 * esz
-                             : (const uint8_t *)nullptr;
-        }, [&](int r0) { return n0 + r0 < dm; }, tid);
-    };
-    auto put = [&](uint8_t *S, const mt::Stage &st) { mt::store_mn<DT>(S, st, tid); };
-    mt::Acc acc;
-    mt::zero(acc);
-    mt::gemm<DT>(acc, As, Bs, NSEG * spseg, load_a, put, load_b, put, wm, wn, lane);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = i0 + mt::acc_row(wm, mi, e, lane);
-                const int n = n0 + mt::acc_col(wn, ni, lane);
-                if (n < dm)
-                    out[(size_t)i * dm + n] += acc[mi][ni][e];
-            }
-}
-
-// ------------------------------------------------------------ fused launches
-// Work that needs no ordering between its parts shares one launch: the ELL
-// masks with the backup rows' u/da GEMM, and the backup rows' dx GEMM with
-// their dW GEMM. Workgroup b < n_a does part A, the rest part B.
-template <int DT>
-__global__ __launch_bounds__(NT, 2) void mask_ud_kernel(
+// ------------------------------------------------------------ masks launch
+__global__ __launch_bounds__(NT) void mask_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, int T, int K, int dff, uint64_t *__restrict__ masks,
-    int32_t *__restrict__ cnt, int n_chunk, int n_mask, const uint8_t *__restrict__ x,
-    const uint8_t *__restrict__ dy, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
-    const uint8_t *__restrict__ wd, int dm, const void *__restrict__ dense, float l1,
-    void *__restrict__ inter, size_t stride)
+    int32_t *__restrict__ cnt, int n_chunk)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_LDS];
-    static_assert(CH * 8 + BR * 4 <= TILE_LDS, "mask chunk must fit the shared LDS");
+    __shared__ unsigned long long m[CH];
+    __shared__ int rn[BR];
     const int b = blockIdx.x;
-    if (b < n_mask) {
-        ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk,
-                       b % n_chunk, (unsigned long long *)lds, (int *)(lds + CH * 8));
-        return;
-    }
-    const int u = b - n_mask, nx = dff / mt::TILE;
-    Tiles t = (Tiles)lds;
-    ovf_ud_tile<DT>(x, dy, ovf_rows, n_ovf_p, max_ovf, wu, wd, dm, dff, dense, l1, inter, stride,
-                    u % nx, u / nx, t, t + 2);
-}
-
-template <int DT>
-__global__ __launch_bounds__(mt::NT, 2) void ovf_dxdw_kernel(
-    const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ x,
-    const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wg,
-    const uint8_t *__restrict__ wu, int dm, int dff, float *__restrict__ dx,
-    float *__restrict__ dwd, float *__restrict__ dwu, float *__restrict__ dwg, int n_dx)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TILE_LDS];
-    Tiles t = (Tiles)lds;
-    const int b = blockIdx.x, nx = (dm + mt::TILE - 1) / mt::TILE;
-    if (b < n_dx) {
-        ovf_dx_tile<DT>(inter, stride, ovf_rows, n_ovf_p, max_ovf, wu, wg, dm, dff, dx, b % nx,
-                        b / nx, t, t + 2);
-        return;
-    }
-    const int u = b - n_dx, ny = dff / mt::TILE;
-    ovf_dw_tile<DT>(inter, stride, ovf_rows, n_ovf_p, max_ovf, x, dy, dm, dff, dwd, dwu, dwg,
-                    u % nx, (u / nx) % ny, u / (nx * ny), t, t + 2);
+    ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk, b % n_chunk,
+                   m, rn);
 }
 
 template <int DT, int NW>
@@ -633,13 +425,11 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                 uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int T = h->T, K = h->K, dff = h->d_ff;
-    const Layout L = layout(T, dff, K, h->max_ovf);
+    const Layout L = layout(DT, T, dm, dff, K, h->max_ovf);
     float *coef = (float *)(ws + L.coef);
     uint64_t *masks = (uint64_t *)(ws + L.masks);
     int32_t *cnt = (int32_t *)(ws + L.cnt), *colptr = (int32_t *)(ws + L.colptr);
     int32_t *csc = (int32_t *)(ws + L.csc);
-    void *inter = ws + L.inter;
-    const size_t stride = (size_t)L.pad_ovf * dff;
     const uint8_t *xb = (const uint8_t *)x, *dyb = (const uint8_t *)dy;
     const int rgroups = (T + NT / 64 - 1) / (NT / 64);
     constexpr int NWN = NW < 16 ? NW : 16;          // neuron pass: accumulated words per lane
@@ -651,17 +441,13 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     constexpr int NWP = NW < ACC_NW ? NW : ACC_NW; // dx pass: words per lane of one part
     const int parts = row_parts<DT>(dm, NWP);
 
-    const int mt_tiles = L.pad_ovf / mt::TILE, nt_dm = (dm + mt::TILE - 1) / mt::TILE;
-    const bool ovf = h->max_ovf > 0 && T > 0;
     if (T > 0) {
-        const int n_chunk = (dff + CH - 1) / CH, n_mask = L.nblk * n_chunk;
-        const int n_ud = ovf ? (dff / mt::TILE) * mt_tiles : 0;
-        hipLaunchKernelGGL((mask_ud_kernel<DT>), dim3(n_mask + n_ud), dim3(NT), 0, s, h->row_nnz,
-                           h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk, n_mask, xb,
-                           dyb, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
-                           (const uint8_t *)wd, dm, h->dense, l1, inter, stride);
-        tm.mark("mask_ud_kernel");
+        const int n_chunk = (dff + CH - 1) / CH;
+        hipLaunchKernelGGL(mask_kernel, dim3(L.nblk * n_chunk), dim3(NT), 0, s, h->row_nnz,
+                           h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk);
+        tm.mark("mask_kernel");
     }
+    launch_bk_ud((twell_dtype)DT, x, dy, h, wu, wg, wd, dm, l1, ws + L.backup, tm, s);
     hipLaunchKernelGGL(blk_prefix_kernel, dim3((dff + 63) / 64), dim3(NT), 0, s, cnt, L.nblk, dff,
                        colptr);
     tm.mark("blk_prefix_kernel");
@@ -683,14 +469,7 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                            (const uint8_t *)wu, (const uint8_t *)wg, dm, dx);
         tm.mark("bwd_dx_kernel");
     }
-    if (ovf) {
-        const int n_dx = nt_dm * mt_tiles, n_dw = nt_dm * (dff / mt::TILE) * 3;
-        hipLaunchKernelGGL((ovf_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(mt::NT), 0, s, inter,
-                           stride, h->ovf_rows, h->n_ovf, h->max_ovf, xb, dyb,
-                           (const uint8_t *)wg, (const uint8_t *)wu, dm, dff, dx, dwd, dwu, dwg,
-                           n_dx);
-        tm.mark("ovf_dxdw_kernel");
-    }
+    launch_bk_dxdw((twell_dtype)DT, h, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
 }
 
 template <int DT>
@@ -709,19 +488,9 @@ void launch_dt(const void *x, const void *dy, const hybrid_t *h, const void *wg,
 
 } // namespace
 
-size_t bwd_workspace_layout(int T, int dm, int dff, int K, int max_ovf, size_t *offsets)
+size_t bwd_workspace_layout(int dt, int T, int dm, int dff, int K, int max_ovf)
 {
-    (void)dm;
-    const Layout L = layout(T, dff, K, max_ovf);
-    if (offsets) {
-        offsets[0] = L.coef;
-        offsets[1] = L.masks;
-        offsets[2] = L.cnt;
-        offsets[3] = L.colptr;
-        offsets[4] = L.csc;
-        offsets[5] = L.inter;
-    }
-    return L.total;
+    return layout(dt, T, dm, dff, K, max_ovf).total;
 }
 
 hipError_t launch_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,

@@ -37,7 +37,6 @@ namespace {
 constexpr int DW = 8;          // waves per workgroup
 constexpr int DNT = 64 * DW;
 constexpr int TC = 32;         // tokens per MFMA chunk of the gate
-constexpr int SB = 4;          // K steps of loads in flight per wave in the gate
 constexpr int LP = TWELL_TILE_C + 8; // LDS pitch of a partial row (floats): rows 4
                                      // apart (the two lane halves) land 32 banks apart
 constexpr int LISTD = 2048;    // entries staged per pass of the down phase
@@ -65,10 +64,10 @@ DecPlan dec_plan(int dt, int T, int dm, int dff, int W, bool with_gate)
     P.W = W;
     P.nsteps = dm * esz / 32;
     // about one item per compute unit, at least one K step per wave, and the
-    // partials (ks T dff floats) at most a quarter of W_g's bytes
+    // partials (ks T dff floats) at most half of W_g's bytes
     int ks = std::max(1, GATE_ITEMS / P.nt);
     ks = std::min(ks, std::max(1, P.nsteps / DW));
-    ks = std::min(ks, std::max(1, 2 * P.nsteps / std::max(T, 1)));
+    ks = std::min(ks, std::max(1, 4 * P.nsteps / std::max(T, 1)));
     P.spw = (P.nsteps + ks * DW - 1) / (ks * DW);
     P.ks = (P.nsteps + P.spw * DW - 1) / (P.spw * DW);
     P.tcm = std::min(T, TC);
@@ -119,38 +118,44 @@ DEVI void pack_tile(float g0, float g1, size_t tj, int n0, int W, int lane, int3
     }
 }
 
-// MFMA partial of one tile's 128 columns over K steps [s0, s1) (4 blocks of
-// 32 columns; accumulator element e of lane l in a block holds row
-// 8(e/4) + 4(l/32) + e%4, column l%32).
-// Rows of x past the last token repeat a valid row: they only feed output rows
-// that are never stored.
-template <int DT>
-DEVI void gate_steps(const uint8_t *xrow, const uint8_t *const (&wrow)[4], int s0, int s1,
-                     floatx16_t (&acc)[4])
+// MFMA partial of one tile's 128 columns for NC chunks of 32 tokens over K
+// steps [s0, s1) (4 blocks of 32 columns; accumulator element e of lane l in
+// a block holds row 8(e/4) + 4(l/32) + e%4, column l%32). Each W_g fragment
+// is loaded once for all chunks. Rows of x past the last token repeat a valid
+// row: they only feed output rows that are never stored.
+template <int DT, int NC>
+DEVI void gate_steps(const uint8_t *const (&xrow)[NC], const uint8_t *const (&wrow)[4], int s0,
+                     int s1, floatx16_t (&acc)[NC][4])
 {
+    constexpr int NSB = NC == 1 ? 4 : 2; // K steps of loads in flight
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            acc[b][e] = 0.f;
-    for (int s = s0; s < s1; s += SB) {
-        // SB steps of loads in flight before their MFMAs (steps past the
-        // range re-read its last step and are not used)
-        uint4 a[SB], b[SB][4];
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int i = 0; i < SB; ++i) {
+            for (int e = 0; e < 16; ++e)
+                acc[c][b][e] = 0.f;
+    for (int s = s0; s < s1; s += NSB) {
+        // steps past the range re-read its last step and are not used
+        uint4 a[NSB][NC], b[NSB][4];
+#pragma unroll
+        for (int i = 0; i < NSB; ++i) {
             const size_t o = (size_t)min(s + i, s1 - 1) * 32;
-            a[i] = ldg16(xrow + o);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                b[i][c] = ldg16(wrow[c] + o);
+            for (int c = 0; c < NC; ++c)
+                a[i][c] = ldg16(xrow[c] + o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                b[i][q] = ldg16(wrow[q] + o);
         }
 #pragma unroll
-        for (int i = 0; i < SB; ++i)
+        for (int i = 0; i < NSB; ++i)
             if (s + i < s1) // uniform
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    mt::mma_group<DT>(acc[c], a[i], b[i][c]);
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        mt::mma_group<DT>(acc[c][q], a[i][c], b[i][q]);
     }
 }
 
@@ -171,7 +176,7 @@ DEVI void park_partial(const floatx16_t (&acc)[4], float *lds, int wave, int tcm
 }
 
 // ---------------------------------------------------------------- phase 1
-template <int DT>
+template <int DT, int NC>
 DEVI void gate_part_item(const DecPlan &P, const uint8_t *__restrict__ x,
                          const uint8_t *__restrict__ wg, int item, float *__restrict__ part,
                          float *lds)
@@ -184,22 +189,28 @@ DEVI void gate_part_item(const DecPlan &P, const uint8_t *__restrict__ x,
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         wrow[b] = wg + (size_t)(n0 + b * 32 + l32) * rowbytes + half * 16;
-    for (int tc = 0; tc < P.T; tc += TC) {
-        const int tn = min(TC, P.T - tc);
-        const uint8_t *xrow = x + (size_t)(tc + min(l32, tn - 1)) * rowbytes + half * 16;
-        floatx16_t acc[4];
-        gate_steps<DT>(xrow, wrow, s0, s1, acc);
-        park_partial(acc, lds, wave, P.tcm, tn, half, l32);
+    const uint8_t *xrow[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int tn = min(TC, P.T - c * TC); // >= 1: NC chunks cover T
+        xrow[c] = x + (size_t)(c * TC + min(l32, tn - 1)) * rowbytes + half * 16;
+    }
+    floatx16_t acc[NC][4];
+    gate_steps<DT, NC>(xrow, wrow, s0, s1, acc);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int tc = c * TC, tn = min(TC, P.T - tc);
+        park_partial(acc[c], lds, wave, P.tcm, tn, half, l32);
         __syncthreads();
         for (int i = threadIdx.x; i < tn * TWELL_TILE_C; i += DNT) {
-            const int r = i / TWELL_TILE_C, c = i % TWELL_TILE_C;
-            float g = lds[r * LP + c];
+            const int r = i / TWELL_TILE_C, q = i % TWELL_TILE_C;
+            float g = lds[r * LP + q];
 #pragma unroll
             for (int w = 1; w < DW; ++w)
-                g += lds[(w * P.tcm + r) * LP + c];
-            part[((size_t)k * P.T + tc + r) * P.dff + n0 + c] = g;
+                g += lds[(w * P.tcm + r) * LP + q];
+            part[((size_t)k * P.T + tc + r) * P.dff + n0 + q] = g;
         }
-        __syncthreads(); // lds is rewritten by the next chunk or item
+        __syncthreads(); // lds is rewritten by the next chunk
     }
 }
 
@@ -446,12 +457,12 @@ size_t down_lds() { return (2 * LISTD + 260 + DW * 512) * 4; }
 size_t gate_lds(const DecPlan &P) { return (size_t)DW * P.tcm * LP * 4; }
 
 // ---------------------------------------------------------------- kernels
-template <int DT>
+template <int DT, int NC>
 __global__ __launch_bounds__(DNT) void dec_gate_part_kernel(
     DecPlan P, const uint8_t *__restrict__ x, const uint8_t *__restrict__ wg, float *part)
 {
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    gate_part_item<DT>(P, x, wg, blockIdx.x, part, smem);
+    gate_part_item<DT, NC>(P, x, wg, blockIdx.x, part, smem);
 }
 
 template <int DT, int NW, int G, bool UP>
@@ -504,8 +515,12 @@ template <int DT>
 void launch_gate_part(const DecPlan &P, const void *x, const void *wg, float *part, Timer &tm,
                       hipStream_t s)
 {
-    hipLaunchKernelGGL(dec_gate_part_kernel<DT>, dim3(P.nt * P.ks), dim3(DNT), gate_lds(P), s, P,
-                       (const uint8_t *)x, (const uint8_t *)wg, part);
+    if (P.T > TC)
+        hipLaunchKernelGGL((dec_gate_part_kernel<DT, 2>), dim3(P.nt * P.ks), dim3(DNT),
+                           gate_lds(P), s, P, (const uint8_t *)x, (const uint8_t *)wg, part);
+    else
+        hipLaunchKernelGGL((dec_gate_part_kernel<DT, 1>), dim3(P.nt * P.ks), dim3(DNT),
+                           gate_lds(P), s, P, (const uint8_t *)x, (const uint8_t *)wg, part);
     tm.mark("dec_gate_part_kernel");
 }
 

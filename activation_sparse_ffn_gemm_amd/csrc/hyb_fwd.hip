@@ -8,12 +8,16 @@
 // ELL rows (few nonzeros): a wave per row gathers one wu_t row and one wd row
 // per entry, as the TwELL forward does, several entries in flight.
 // Backup rows (many nonzeros, dense): two MFMA products over the rows'
-// stored h,
+// stored h (backup.hip),
 //   A = h (.) (x_O W_u)   [n_ovf x d_ff],   y_O = A W_d   [n_ovf x d_model],
 // with A kept as a float32 intermediate (for bf16 inputs as a hi/lo bf16 pair,
 // so the second product keeps about 16 significant bits of A).
 #include "mfma_tile.hpp"
 #include "rows.hpp"
+
+size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
+void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
+                   const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s);
 
 namespace {
 
@@ -82,135 +86,12 @@ __global__ __launch_bounds__(NT) void hfwd_ell_kernel(
     part.store_f(y, t, acc);
 }
 
-// ---------------------------------------------------------------- backup rows
-// A = h (.) (x_O W_u) for one 128 x 128 tile (backup rows x neurons).
-template <int DT>
-__global__ __launch_bounds__(mt::NT, 2) void hfwd_a_kernel(
-    const uint8_t *__restrict__ x, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu, int dm,
-    int dff, const void *__restrict__ dense, void *__restrict__ inter, size_t stride)
-{
-    using E = elem<DT>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[mt::TILE_LDS];
-    mt::Tiles As = (mt::Tiles)lds, Bs = As + 2;
-    const int n_ovf = min(*n_ovf_p, max_ovf);
-    const int m0 = blockIdx.y * mt::TILE, n0 = blockIdx.x * mt::TILE;
-    if (m0 >= n_ovf)
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const size_t rowbytes = (size_t)dm * sizeof(typename E::storage);
-    const int nk = (int)(rowbytes / mt::ROWB);
-    int src[4]; // token row of each staged A row (-1 past n_ovf)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid + mt::NT * i) >> 3;
-        src[i] = m0 + r < n_ovf ? ovf_rows[m0 + r] : -1;
-    }
-    auto load_a = [&](mt::Stage &st, int kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = (tid + mt::NT * i) & 7;
-            st.v[i] = src[i] >= 0 ? ldg16(x + (size_t)src[i] * rowbytes + (size_t)kt * mt::ROWB + c * 16)
-                                  : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto load_b = [&](mt::Stage &st, int kt) {
-        mt::load_k(st, [&](int r) { return wu + (size_t)(n0 + r) * rowbytes + (size_t)kt * mt::ROWB; },
-                   tid);
-    };
-    auto put = [&](uint8_t *S, const mt::Stage &st) { mt::store_k(S, st, tid); };
-    mt::Acc au;
-    mt::zero(au);
-    mt::gemm<DT>(au, As, Bs, nk, load_a, put, load_b, put, wm, wn, lane);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + mt::acc_row(wm, mi, e, lane);
-                if (m >= n_ovf)
-                    continue;
-                const size_t o = (size_t)m * dff + n0 + mt::acc_col(wn, ni, lane);
-                mt::put_inter<DT>(inter, stride, 0, o, E::load1(dense, o) * au[mi][ni][e]);
-            }
-}
-
-// y_O = A W_d for one 128 x 128 tile (backup rows x model columns), written to
-// the rows' places in y.
-template <int DT>
-__global__ __launch_bounds__(mt::NT, 2) void hfwd_y_kernel(
-    const void *__restrict__ inter, size_t stride, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wd, int dm,
-    int dff, float *__restrict__ y)
-{
-    using E = elem<DT>;
-    constexpr int esz = sizeof(typename E::storage);
-    constexpr int KE = mt::ROWB / esz;
-    constexpr int NSEG = DT == TWELL_BF16 ? 2 : 1; // (A hi, A lo) or A
-    __shared__ __attribute__((aligned(16))) uint8_t lds[mt::TILE_LDS];
-    mt::Tiles As = (mt::Tiles)lds, Bs = As + 2;
-    const int n_ovf = min(*n_ovf_p, max_ovf);
-    const int m0 = blockIdx.y * mt::TILE, n0 = blockIdx.x * mt::TILE;
-    if (m0 >= n_ovf)
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const size_t rowbytes = (size_t)dm * esz;
-    const int spseg = dff / KE; // K steps per segment
-    const uint8_t *ibase = (const uint8_t *)inter;
-    auto load_a = [&](mt::Stage &st, int kt) {
-        const int seg = kt / spseg, k0 = (kt % spseg) * KE;
-        const uint8_t *arr = ibase + (size_t)seg * stride * esz;
-        mt::load_k(st, [&](int r) {
-            return m0 + r < n_ovf ? arr + ((size_t)(m0 + r) * dff + k0) * esz : (const uint8_t *)nullptr;
-        }, tid);
-    };
-    auto load_b = [&](mt::Stage &st, int kt) {
-        const int k0 = (kt % spseg) * KE;
-        mt::load_mn<DT>(st, [&](int kk) { return wd + (size_t)(k0 + kk) * rowbytes + (size_t)n0 * esz; },
-                        [&](int r0) { return n0 + r0 < dm; }, tid);
-    };
-    auto put_a = [&](uint8_t *S, const mt::Stage &st) { mt::store_k(S, st, tid); };
-    auto put_b = [&](uint8_t *S, const mt::Stage &st) { mt::store_mn<DT>(S, st, tid); };
-    mt::Acc acc;
-    mt::zero(acc);
-    mt::gemm<DT>(acc, As, Bs, NSEG * spseg, load_a, put_a, load_b, put_b, wm, wn, lane);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int m = m0 + mt::acc_row(wm, mi, e, lane);
-            if (m >= n_ovf)
-                continue;
-            const size_t yrow = (size_t)ovf_rows[m] * dm;
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int n = n0 + mt::acc_col(wn, ni, lane);
-                if (n < dm)
-                    y[yrow + n] = acc[mi][ni][e];
-            }
-        }
-}
-
-size_t pad_rows(int max_ovf) { return (size_t)(max_ovf + mt::TILE - 1) / mt::TILE * mt::TILE; }
-
 template <int DT, int NW>
 void launch_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd, int dm, float *y,
                uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int T = h->T, dff = h->d_ff;
-    if (h->max_ovf > 0) {
-        const size_t stride = pad_rows(h->max_ovf) * dff;
-        const int mt_tiles = (int)(pad_rows(h->max_ovf) / mt::TILE);
-        hipLaunchKernelGGL((hfwd_a_kernel<DT>), dim3(dff / mt::TILE, mt_tiles), dim3(mt::NT), 0, s,
-                           (const uint8_t *)x, h->ovf_rows, h->n_ovf, h->max_ovf,
-                           (const uint8_t *)wu, dm, dff, h->dense, ws, stride);
-        tm.mark("hfwd_a_kernel");
-        hipLaunchKernelGGL((hfwd_y_kernel<DT>), dim3((dm + mt::TILE - 1) / mt::TILE, mt_tiles),
-                           dim3(mt::NT), 0, s, ws, stride, h->ovf_rows, h->n_ovf, h->max_ovf,
-                           (const uint8_t *)wd, dm, dff, y);
-        tm.mark("hfwd_y_kernel");
-    }
+    launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, tm, s);
     constexpr int NWP = NW < 16 ? NW : 16;
     constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
     const int parts = row_parts<DT>(dm, NWP);
@@ -236,9 +117,12 @@ void launch_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
 
 } // namespace
 
-// A's float32 intermediate: a hi/lo pair of bf16 arrays or one float32 array,
-// each [rows of the backup, padded to whole tiles][d_ff].
-size_t hyb_fwd_workspace(int max_ovf, int dff) { return 4 * pad_rows(max_ovf) * (size_t)dff; }
+// The backup rows' products (their intermediate A, W_d^T and the split-K
+// partials of y_O).
+size_t hyb_fwd_workspace(int dt, int dm, int max_ovf, int dff)
+{
+    return bk_workspace(dt, dm, dff, max_ovf, false);
+}
 
 hipError_t launch_hyb_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
                           const void *wd, int dm, float *y, void *ws, int32_t *status,

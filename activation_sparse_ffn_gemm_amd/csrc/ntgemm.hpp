@@ -1,0 +1,197 @@
+// Tiled MFMA main loop for dense products C[m][n] = sum_k A[m][k] B[n][k]
+// whose operands are both K-contiguous (every operand row is a memory row
+// along K), shared by the dense products over the hybrid's backup rows.
+//
+// A workgroup of WGM x WGN wave64s computes a BM x BN tile; each wave owns a
+// WM x WN sub-tile as (WM/32) x (WN/32) blocks of 32x32 MFMA accumulators.
+// Operands stream through LDS in K steps of 64 bytes per row (32 bf16 /
+// 16 f32), NST steps resident at once: the loads of step k + NST - 1 are
+// issued while step k is computed. Loads go straight from global memory to
+// LDS, 16 bytes per lane (one wave instruction fills 16 rows x 64 bytes), so
+// no registers are spent on staging; each wave waits only for its own loads
+// of the step it is about to use, then a barrier covers the others'. LDS rows
+// are XOR-swizzled in 16-byte chunks so that the 16 lanes a 128-bit fragment
+// read serves per cycle hit 16 distinct groups of the 64 banks.
+//
+// Rows are given per tile row by the caller (a gather of any rows is fine);
+// K steps map to byte offsets through a caller function, so a product may
+// run over several segments (e.g. the hi and lo halves of a bf16 pair, or two
+// operand pairs summed) and over any sub-range of them (split K).
+#pragma once
+
+#include "mfma_tile.hpp"
+
+namespace ng {
+
+constexpr int ROWB = 64; // bytes of one LDS row per K step
+constexpr int NST = 4;   // K steps resident in LDS
+constexpr int BLK = 1024; // bytes one wave's 16-byte-lane load writes: 16 rows
+
+template <int BM_, int BN_, int WGM_, int WGN_> struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+    static constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
+    static constexpr int NT = 64 * WGM * WGN, NWV = WGM * WGN;
+    static constexpr int STAGE = (BM + BN) * ROWB, NBLK = STAGE / BLK;
+    // blocks per wave: the first N_HI waves take WB_HI, the others WB_HI - 1
+    static constexpr int WB_HI = (NBLK + NWV - 1) / NWV, N_HI = NBLK - (WB_HI - 1) * NWV;
+    static constexpr int LDS = NST * STAGE;
+    static_assert(BM % 32 == 0 && BN % 32 == 0 && WM % 32 == 0 && WN % 32 == 0, "32x32 blocks");
+    static_assert(STAGE % BLK == 0 && BM % 16 == 0, "a block must not straddle the operands");
+    static_assert(2 * WB_HI < 64, "loads in flight must fit the vmcnt counter");
+};
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's
+// 16 bytes land at LDS byte lds + 16 l. Written as assembly so that the
+// compiler, which would otherwise make every LDS read and barrier wait for all
+// such loads in flight, leaves the waiting to the explicit vmcnt waits of the
+// K loop. M0 (the LDS base of the load) is written here; nothing else in these
+// kernels reads M0 on gfx950 (their LDS instructions do not use it), hence the
+// silenced warning about clobbering a reserved register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+DEVI void lds_dma16(const uint8_t *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+// Byte offset of 16-byte chunk c (0..3) of LDS row r (64-byte rows). Rows
+// r, r+4, r+8, r+12 start on the same bank; XOR-ing the chunk with (r / 4) % 4
+// separates them, so 16 consecutive rows at one chunk use 16 distinct groups.
+DEVI int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// Wait until at most n of this wave's vector-memory operations are pending
+// (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt
+// at their maximum, i.e. not waited on).
+template <int n> DEVI void wait_vm()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Byte offsets of one K step in the A rows and in the B rows.
+struct StepOff {
+    size_t a, b;
+};
+
+// Accumulators of one wave.
+template <class C> struct Acc {
+    floatx16_t v[C::MI][C::NI];
+};
+
+// Tile coordinates of accumulator element e of block (mi, ni) of this lane:
+// row 8(e/4) + 4(l/32) + e%4 and column l%32 of the block.
+template <class C> DEVI int acc_row(int wm, int mi, int e, int lane)
+{
+    return wm * C::WM + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+}
+template <class C> DEVI int acc_col(int wn, int ni, int lane)
+{
+    return wn * C::WN + ni * 32 + (lane & 31);
+}
+template <class C> DEVI int wave_m()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) / C::WGN;
+}
+template <class C> DEVI int wave_n()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) % C::WGN;
+}
+
+// acc += A B^T over K steps [kt0, kt1). rowa(r) / rowb(r) give the address of
+// tile row r's data at K offset 0 (every row must be readable: rows outside
+// an operand should repeat a valid row and their outputs be dropped);
+// off(kt) gives step kt's byte offsets. L: C::LDS bytes of shared memory.
+// Ends with a barrier: L may be reused right after.
+template <class C, int DT, class RowA, class RowB, class Off>
+DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, Acc<C> &acc)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
+    const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc.v[mi][ni][e] = 0.f;
+    const int nk = kt1 - kt0;
+    if (nk <= 0)
+        return;
+    // This wave's 1 KB blocks of a stage: block b holds tile rows
+    // 16b .. 16b+15 (A rows, then B rows). Lane l writes bytes 16l .. 16l+15
+    // of it, i.e. swizzled chunk l&3 of row 16b + l/4, so it loads the source
+    // chunk the swizzle maps there.
+    const int nb = wave < C::N_HI ? C::WB_HI : C::WB_HI - 1;
+    const int b0 = wave < C::N_HI ? wave * C::WB_HI
+                                  : C::N_HI * C::WB_HI + (wave - C::N_HI) * (C::WB_HI - 1);
+    const uint8_t *src[C::WB_HI];
+    bool isa[C::WB_HI];
+#pragma unroll
+    for (int i = 0; i < C::WB_HI; ++i) {
+        const int b = min(b0 + i, C::NBLK - 1);
+        const int r = 16 * b + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        isa[i] = 16 * b < C::BM; // uniform: a block is all A or all B rows
+        src[i] = (isa[i] ? rowa(r) : rowb(r - C::BM)) + c * 16;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8 *)L + b0 * BLK;
+    auto issue = [&](int kt) {
+        const uint32_t dst = lds0 + ((kt - kt0) % NST) * C::STAGE;
+        const StepOff o = off(kt);
+#pragma unroll
+        for (int i = 0; i < C::WB_HI; ++i)
+            if (i < nb) // uniform
+                lds_dma16(src[i] + (isa[i] ? o.a : o.b), dst + i * BLK);
+    };
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nk)
+            issue(kt0 + s);
+    for (int k = 0; k < nk; ++k) {
+        // this wave's loads of step k are done once at most the later steps' pend
+        const int later = min(nk - 1, k + NST - 2) - k;
+        if (later >= 2) {
+            if (nb == C::WB_HI)
+                wait_vm<2 * C::WB_HI>();
+            else
+                wait_vm<2 * (C::WB_HI - 1)>();
+        } else if (later == 1) {
+            if (nb == C::WB_HI)
+                wait_vm<C::WB_HI>();
+            else
+                wait_vm<C::WB_HI - 1>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads(); // all loads of step k are in; step k - 1 is consumed
+        if (k + NST - 1 < nk)
+            issue(kt0 + k + NST - 1);
+        const uint8_t *As = L + (k % NST) * C::STAGE, *Bs = As + C::BM * ROWB;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            uint4 fa[C::MI], fb[C::NI];
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+                fa[mi] = *(const uint4 *)(As + swz(wm * C::WM + mi * 32 + l32, 2 * g + half));
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                fb[ni] = *(const uint4 *)(Bs + swz(wn * C::WN + ni * 32 + l32, 2 * g + half));
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni)
+                    mt::mma_group<DT>(acc.v[mi][ni], fa[mi], fb[ni]);
+        }
+    }
+    __syncthreads(); // every wave is done reading the stages
+}
+
+} // namespace ng

@@ -1,14 +1,16 @@
 """Benchmark of the activation-sparse ReLU-gated FFN hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-twell_gate_pack (gate GEMM + TwELL epilogue) -> twell_ffn_fwd (fused up/down)
--> twell_to_hybrid -> hybrid_ffn_bwd (dx, dW_g, dW_u, dW_d for a synthetic
+One step = one training pass of the whole path over one batch of synthetic
+input: twell_gate_pack (gate GEMM + TwELL epilogue) -> twell_to_hybrid ->
+hybrid_ffn_fwd (the forward over the hybrid: ELL rows by gathers, backup rows
+by dense products) -> hybrid_ffn_bwd (dx, dW_g, dW_u, dW_d for a synthetic
 dy). The default workload is the 0.5B-scale layer at 1% gate density
 (T = 4096 tokens, d_model = 1024, d_ff = 2816, bf16). Inputs are resident in
 HBM before the timed region. Prints one JSON line.
 
 Beside the step it reports: per-stage times (HIP events on the stream the
-kernels run on), the roofline of the dominant kernel, the same layer run dense
+kernels run on), the roofline of the dominant kernel, the inference forward
+(twell_gate_pack -> twell_ffn_fwd) timed on its own, the same layer run dense
 in bf16 by torch (forward, and forward + backward), and the CPU oracle timed
 on this host (``cpu_baseline``).
 """
@@ -43,7 +45,9 @@ KERNEL_SOURCES = {
     "gate_pack_kernel": "gate_pack.hip", "ffn_fwd_kernel": "ffn_fwd.hip",
     "fwd_up_kernel": "ffn_fwd.hip", "fwd_down_kernel": "ffn_fwd.hip",
     "hyb_rows_kernel": "to_hybrid.hip", "hyb_slots_kernel": "to_hybrid.hip",
-    "hyb_dense_kernel": "to_hybrid.hip",
+    "hyb_dense_kernel": "to_hybrid.hip", "hfwd_ell_kernel": "hyb_fwd.hip",
+    "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "bk_ud_kernel": "backup.hip",
+    "bk_dx_kernel": "backup.hip", "bk_dw_kernel": "backup.hip",
 }
 
 
@@ -133,6 +137,8 @@ def main():
     y = torch.empty((T, dm), dtype=torch.float32, device=dev)
     fws_n = tw.fwd_workspace_bytes(tw.TWELL_BF16, T, dm, dff, w.width)
     fws = torch.empty(max(fws_n, 1), dtype=torch.uint8, device=dev)
+    hfws_n = tw.hybrid_fwd_workspace_bytes(tw.TWELL_BF16, T, dm, dff, w.K, w.max_ovf)
+    hfws = torch.empty(max(hfws_n, 1), dtype=torch.uint8, device=dev)
     hy = tw.empty_hybrid(T, dff, w.K, w.max_ovf, torch.bfloat16, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     grads = (torch.empty((T, dm), **f32), torch.empty((dff, dm), **f32),
@@ -140,19 +146,27 @@ def main():
     bws = torch.empty(tw.bwd_workspace_bytes(tw.TWELL_BF16, T, dm, dff, w.K, w.max_ovf),
                       dtype=torch.uint8, device=dev)
 
-    stages = ("gate_pack", "ffn_fwd", "to_hybrid", "bwd")
+    stages = ("gate_pack", "to_hybrid", "hybrid_fwd", "bwd")
     timers = {k: tw.KernelTimer() for k in stages}
 
     def step(timed=False):
         tm = timers if timed else {k: None for k in stages}
         tw.gate_pack(x, wg, width=w.width, out=twl, status=st, timing=tm["gate_pack"])
-        tw.ffn_fwd(x, twl, wu, wd, y=y, workspace=fws, status=st, timing=tm["ffn_fwd"])
         tw.to_hybrid(twl, w.K, w.max_ovf, out=hy, status=st, timing=tm["to_hybrid"])
+        tw.hybrid_fwd(x, hy, wu, wd, y=y, workspace=hfws, status=st, timing=tm["hybrid_fwd"])
         tw.ffn_bwd(x, dy, hy, wg, wu, wd, out=grads, workspace=bws, status=st,
                    timing=tm["bwd"], l1=a.l1)
 
+    ftimers = {k: tw.KernelTimer() for k in ("gate_pack", "ffn_fwd")}
+
+    def fwd_step(timed=False):
+        tm = ftimers if timed else {k: None for k in ftimers}
+        tw.gate_pack(x, wg, width=w.width, out=twl, status=st, timing=tm["gate_pack"])
+        tw.ffn_fwd(x, twl, wu, wd, y=y, workspace=fws, status=st, timing=tm["ffn_fwd"])
+
     for _ in range(a.warmup):
         step()
+        fwd_step()
     torch.cuda.synchronize()
     if int(st.item()) != 0:
         raise SystemExit(f"device status {int(st.item())}: a TwELL tile or the backup overflowed")
@@ -184,6 +198,22 @@ def main():
                 kern_ms[name] = kern_ms.get(name, 0.0) + ms / a.steps
                 stage_ms[k] += ms / a.steps
 
+    # inference forward on its own: gate + TwELL pack, fused up/down
+    torch.cuda.synchronize()
+    e_start.record()
+    for _ in range(a.steps):
+        fwd_step()
+    e_end.record()
+    torch.cuda.synchronize()
+    inf_ms = e_start.elapsed_time(e_end) / a.steps
+    fwd_kern = {}
+    for _ in range(a.steps):
+        fwd_step(timed=True)
+        torch.cuda.synchronize()
+        for k in ftimers:
+            for name, ms in ftimers[k].collect():
+                fwd_kern[name] = fwd_kern.get(name, 0.0) + ms / a.steps
+
     # ---- roofline of each kernel: algorithmic work of one launch. Bytes count
     # every row a kernel's algorithm reads (a gathered row once per use, as
     # the gather performs it), the index/value arrays it reads and what it
@@ -211,23 +241,30 @@ def main():
                               "per neuron wu_t + wd rows and three fp32 dW rows"),
         "bwd_dx_kernel": ("hbm", nnz_ell * (2 * row_b + 10) + 8 * T + T_ell * dm * 4,
                           "per ELL nonzero one wu_t row + one wg_t row + col, du, dg; dx rows"),
-        "mask_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff,
-                           "u_O and da_O: 2 GEMMs (beside the ELL transpose masks)"),
-        "ovf_dxdw_kernel": ("mfma", 5 * 2.0 * n_ovf * dm * dff,
-                            "dx_O (2 GEMMs) and dW_g, dW_u, dW_d += (3 GEMMs)"),
+        "hfwd_ell_kernel": ("hbm", nnz_ell * (2 * row_b + 4) + T_ell * (row_b + dm * 4),
+                            "per ELL nonzero one wu_t row + one wd row + (col, h); x, y rows"),
+        "bk_a_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "A = h_O (.) x_O W_u (1 GEMM)"),
+        "bk_y_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "y_O = A W_d (1 GEMM)"),
+        "bk_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "u_O and da_O (2 GEMMs)"),
+        "bk_dx_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "dx_O = du W_u^T + dg W_g^T (2 GEMMs)"),
+        "bk_dw_kernel": ("mfma", 3 * 2.0 * n_ovf * dm * dff, "dW_d, dW_u, dW_g += (3 GEMMs)"),
     }
     peak = {"mfma": BF16_PEAK_TFLOPS, "hbm": HBM_PEAK_GBS}
     unit = {"mfma": "TFLOP/s", "hbm": "GB/s"}
     scale = {"mfma": 1e12, "hbm": 1e9}
-    per_kernel = {}
-    for name, ms in kern_ms.items():
-        ent = {"ms": round(ms, 4)}
-        if name in work and work[name][1] > 0:
-            b, wk, desc = work[name]
-            ach = wk / (ms * 1e-3) / scale[b]
-            ent.update(bound=b, achieved=round(ach, 1), unit=unit[b],
-                       frac=round(ach / peak[b], 4), work=wk, work_unit=desc)
-        per_kernel[name] = ent
+    def entries(kms):
+        res = {}
+        for name, ms in kms.items():
+            ent = {"ms": round(ms, 4)}
+            if name in work and work[name][1] > 0:
+                b, wk, desc = work[name]
+                ach = wk / (ms * 1e-3) / scale[b]
+                ent.update(bound=b, achieved=round(ach, 1), unit=unit[b],
+                           frac=round(ach / peak[b], 4), work=wk, work_unit=desc)
+            res[name] = ent
+        return res
+
+    per_kernel = entries(kern_ms)
     dom = max((k for k in kern_ms if k in work and work[k][1] > 0), key=lambda k: kern_ms[k])
     b, wk, desc = work[dom]
     ach = wk / (kern_ms[dom] * 1e-3) / scale[b]
@@ -244,10 +281,10 @@ def main():
     hy_b = nbytes(hy.row_nnz, hy.row_slot, hy.ell_col, hy.ell_val, hy.ovf_rows, hy.dense,
                   hy.n_ovf)
     tw_b = nbytes(twl.count, twl.col, twl.val)
-    memory = {"hybrid_bytes": hy_b, "twell_bytes": tw_b, "fwd_workspace_bytes": fws_n,
+    memory = {"hybrid_bytes": hy_b, "twell_bytes": tw_b, "fwd_workspace_bytes": hfws_n,
               "bwd_workspace_bytes": bws.numel(),
               "sparse_saved_activation_bytes": hy_b,
-              "sparse_step_peak_bytes": tw_b + hy_b + max(fws_n, bws.numel()),
+              "sparse_step_peak_bytes": tw_b + hy_b + max(hfws_n, bws.numel()),
               "note": "activation memory only; x, dy, weights, y and gradients are the same "
                       "for both layers"}
 
@@ -339,13 +376,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs and weights, gate offset "
                                  "for the target density)",
-        "config": {"workload": a.workload, "step": "gate GEMM + TwELL pack, fused up/down, "
-                   "TwELL->hybrid, hybrid backward (dx, dW_g, dW_u, dW_d)", "T": T, "d_model": dm, "d_ff": dff,
+        "config": {"workload": a.workload, "step": "gate GEMM + TwELL pack, TwELL->hybrid, "
+                   "forward over the hybrid, hybrid backward (dx, dW_g, dW_u, dW_d)", "T": T,
+                   "d_model": dm, "d_ff": dff,
                    "density": w.density, "measured_density": round(nnz / (T * dff), 5),
                    "nnz": nnz, "nnz_ell": nnz_ell, "n_ovf": n_ovf, "twell_width": w.width,
                    "K": w.K, "max_ovf": w.max_ovf, "l1": a.l1},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "fwd_tokens_per_s": round(T / ((stage_ms["gate_pack"] + stage_ms["ffn_fwd"]) * 1e-3), 1),
+        "forward": {"step": "gate GEMM + TwELL pack, fused up/down over the TwELL",
+                    "ms": round(inf_ms, 4), "tokens_per_s": round(T / (inf_ms * 1e-3), 1),
+                    "kernels": entries(fwd_kern)},
         "roofline": roofline,
         "kernels": per_kernel,
         "dense_bf16": dense,
