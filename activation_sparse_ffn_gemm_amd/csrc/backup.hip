@@ -22,14 +22,16 @@
 // 16 significant bits); float32 inputs keep one float32 array.
 //
 // y_O and dx_O have few rows and a long K (d_ff, or 2-4 segments of it): K is
-// split over S workgroups per tile, each writing a float32 partial, and a
-// reduction pass adds the S partials in order and stores the rows.
+// split over S workgroups per tile, each writing a float32 partial; the ELL
+// row kernels that run next (they skip backup rows otherwise) add a backup
+// row's S partials in order and store the row (see BkPart).
 // Row counts are device values: workgroups whose rows all lie past n_ovf
 // return at once, and the grids are sized for the capacity max_ovf. Work
 // without an ordering between its parts shares a launch (the u/da tiles with
 // the transposes; the dx tiles with the dW tiles), so that a layer without
 // backup rows pays few launches.
 #include "ntgemm.hpp"
+#include "backup.hpp"
 
 namespace {
 
@@ -437,28 +439,6 @@ __global__ __launch_bounds__(C1::NT, 2) void bk_dxdw_kernel(
                 L);
 }
 
-// out[ovf_rows[m]][d] = sum over s, in order, of part[s][m][d] (m < n_ovf)
-__global__ __launch_bounds__(256) void bk_reduce_kernel(
-    const float *__restrict__ part, int S, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int R, float *__restrict__ out)
-{
-    const int n = n_rows(n_ovf_p, max_ovf);
-    const int q4 = dm / 4; // float4 per row
-    for (size_t q = blockIdx.x * 256 + threadIdx.x; q < (size_t)n * q4;
-         q += (size_t)gridDim.x * 256) {
-        const int m = (int)(q / q4), c = (int)(q % q4) * 4;
-        float4 v = *(const float4 *)(part + (size_t)m * dm + c);
-        for (int sp = 1; sp < S; ++sp) {
-            const float4 w = *(const float4 *)(part + ((size_t)sp * R + m) * dm + c);
-            v.x += w.x;
-            v.y += w.y;
-            v.z += w.z;
-            v.w += w.w;
-        }
-        *(float4 *)(out + (size_t)ovf_rows[m] * dm + c) = v;
-    }
-}
-
 } // namespace
 
 // ---------------------------------------------------------------- host side
@@ -508,9 +488,6 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
                        (const uint8_t *)(ws + L.wt), h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
                        (float *)(ws + L.part));
     tm.mark("bk_y_kernel");
-    hipLaunchKernelGGL(bk_reduce_kernel, dim3(256), dim3(256), 0, s, (const float *)(ws + L.part),
-                       L.S, h->ovf_rows, h->n_ovf, h->max_ovf, dm, L.R, y);
-    tm.mark("bk_y_reduce_kernel");
 }
 
 template <int DT>
@@ -543,9 +520,14 @@ void bk_dxdw_dt(const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu, fl
                        h->max_ovf, dm, dff, L.R, L.S, (float *)(ws + L.part), dwd, dwu, dwg,
                        n_dx);
     tm.mark("bk_dxdw_kernel");
-    hipLaunchKernelGGL(bk_reduce_kernel, dim3(256), dim3(256), 0, s, (const float *)(ws + L.part),
-                       L.S, h->ovf_rows, h->n_ovf, h->max_ovf, dm, L.R, dx);
-    tm.mark("bk_dx_reduce_kernel");
+}
+
+BkPart bk_part(int dt, int dm, int dff, int max_ovf, bool bwd, const void *ws)
+{
+    const BkLayout L = bk_layout(dt, dm, dff, max_ovf, bwd);
+    if (max_ovf <= 0)
+        return BkPart{nullptr, 0, 0};
+    return BkPart{(const float *)((const uint8_t *)ws + L.part), L.S, L.R};
 }
 
 size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd)

@@ -1,0 +1,67 @@
+// Host interface of the dense products over the hybrid's backup rows
+// (backup.hip), and the device helper that finishes them: the split-K
+// partials of y_O / dx_O are summed, in split order, by the ELL row kernels.
+#pragma once
+
+#include "common.hpp"
+
+// Float32 partials part[S][R][d_model] of the backup rows' y_O or dx_O
+// (part == nullptr: the hybrid has no backup capacity).
+struct BkPart {
+    const float *part;
+    int S, R;
+};
+
+size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
+BkPart bk_part(int dt, int dm, int dff, int max_ovf, bool bwd, const void *ws);
+void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
+                   const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s);
+void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
+                  const void *wu, const void *wg, const void *wd, int dm, float l1, void *ws,
+                  Timer &tm, hipStream_t s);
+void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
+                    float *dwg, void *ws, Timer &tm, hipStream_t s);
+
+// Row `slot` of the backup: words [base, base + 64 NW) of a d_model row (EPW
+// floats each, lane l owning words base + 64 c + l) of sum over s of
+// part[s][slot] into out_row. The S loads of a word are issued together.
+template <int NW, int EPW>
+DEVI void bk_finish_row(const BkPart &bp, int slot, int ndw, int base, int lane, float *out_row)
+{
+    const size_t stride = (size_t)bp.R * ndw * EPW;
+    const float *src = bp.part + (size_t)slot * ndw * EPW;
+#pragma unroll
+    for (int c = 0; c < NW; ++c) {
+        const int w = base + c * 64 + lane;
+        if (w >= ndw)
+            continue;
+        float acc[EPW];
+#pragma unroll
+        for (int e = 0; e < EPW; ++e)
+            acc[e] = 0.f;
+        for (int s0 = 0; s0 < bp.S; s0 += 8) {
+            float v[8][EPW];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const size_t o = (size_t)min(s0 + u, bp.S - 1) * stride + (size_t)w * EPW;
+                if constexpr (EPW == 2) {
+                    const float2 f = *(const float2 *)(src + o);
+                    v[u][0] = f.x;
+                    v[u][1] = f.y;
+                } else {
+                    v[u][0] = src[o];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < bp.S)
+#pragma unroll
+                    for (int e = 0; e < EPW; ++e)
+                        acc[e] += v[u][e];
+        }
+        if constexpr (EPW == 2)
+            *(float2 *)(out_row + (size_t)w * 2) = make_float2(acc[0], acc[1]);
+        else
+            out_row[w] = acc[0];
+    }
+}

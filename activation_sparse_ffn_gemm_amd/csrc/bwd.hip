@@ -29,18 +29,12 @@
 // backup.hip):
 //   6. U/DA: u and da of every backup row and neuron, then a, du, dg (dg zero
 //      where h is zero), launched before the ELL passes;
-//   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T, stored to their rows;
+//   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T as split-K partials,
+//      summed into their rows by the dx pass;
 //   8. DW:   dW += [a | du | dg]^T [dy | x | x] over the backup rows, after the
 //      neuron pass has written every dW row.
-#include "mfma_tile.hpp"
+#include "backup.hpp"
 #include "rows.hpp"
-
-size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
-void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
-                  const void *wu, const void *wg, const void *wd, int dm, float l1, void *ws,
-                  Timer &tm, hipStream_t s);
-void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
-                    float *dwg, void *ws, Timer &tm, hipStream_t s);
 
 namespace {
 
@@ -353,14 +347,20 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, const float *__restrict__ coef, int T, int K, int dff,
     const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wg, int dm,
-    float *__restrict__ dx)
+    float *__restrict__ dx, BkPart bp, int max_ovf)
 {
     using R = Row<DT, NW>;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (t >= T || row_slot[t] >= 0)
-        return; // a backup row's dx comes from the dense products
+    if (t >= T)
+        return;
     const R geo(dm, lane, blockIdx.y);
+    const int slot = row_slot[t];
+    if (slot >= 0) { // a backup row: dx is the sum of the dense product's partials
+        if (bp.part && slot < max_ovf)
+            bk_finish_row<NW, R::EPW>(bp, slot, geo.ndw, geo.base, lane, dx + (size_t)t * dm);
+        return;
+    }
     const size_t TK = (size_t)T * K, rb = (size_t)t * K;
     float acc[NW][R::EPW];
     geo.zero_f(acc);
@@ -463,13 +463,16 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                        dim3(64 * NSPLIT), 0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
                        (const uint8_t *)wd, dm, l1, coef, dwg, dwu, dwd);
     tm.mark("bwd_neuron_kernel");
+    // the backup rows' dW products add to the rows the neuron pass wrote; their
+    // dx partials are summed by the dx pass
+    launch_bk_dxdw((twell_dtype)DT, h, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
     if (T > 0) {
+        const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, true, ws + L.backup);
         hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, GD>), dim3(rgroups, parts), dim3(NT), 0, s,
                            h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dff,
-                           (const uint8_t *)wu, (const uint8_t *)wg, dm, dx);
+                           (const uint8_t *)wu, (const uint8_t *)wg, dm, dx, bp, h->max_ovf);
         tm.mark("bwd_dx_kernel");
     }
-    launch_bk_dxdw((twell_dtype)DT, h, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
 }
 
 template <int DT>

@@ -12,12 +12,9 @@
 //   A = h (.) (x_O W_u)   [n_ovf x d_ff],   y_O = A W_d   [n_ovf x d_model],
 // with A kept as a float32 intermediate (for bf16 inputs as a hi/lo bf16 pair,
 // so the second product keeps about 16 significant bits of A).
-#include "mfma_tile.hpp"
+#include "backup.hpp"
 #include "rows.hpp"
 
-size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
-void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
-                   const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s);
 
 namespace {
 
@@ -29,17 +26,24 @@ __global__ __launch_bounds__(NT) void hfwd_ell_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ row_nnz,
     const int32_t *__restrict__ row_slot, const int16_t *__restrict__ ell_col,
     const void *__restrict__ ell_val, int T, int K, int dff, const uint8_t *__restrict__ wu,
-    const uint8_t *__restrict__ wd, int dm, float *__restrict__ y, int32_t *__restrict__ status)
+    const uint8_t *__restrict__ wd, int dm, float *__restrict__ y, BkPart bp, int max_ovf,
+    int32_t *__restrict__ status)
 {
     using E = elem<DT>;
     using R = Row<DT, NW>;   // whole row, for the up dot product
     using RP = Row<DT, NWP>; // this wave's part of the row, for the down projection
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (t >= T || row_slot[t] >= 0)
-        return; // a backup row's y comes from the dense products
+    if (t >= T)
+        return;
     const R geo(dm, lane, 0);
     const RP part(dm, lane, blockIdx.y);
+    const int slot = row_slot[t];
+    if (slot >= 0) { // a backup row: y is the sum of the dense product's partials
+        if (bp.part && slot < max_ovf)
+            bk_finish_row<NWP, RP::EPW>(bp, slot, part.ndw, part.base, lane, y + (size_t)t * dm);
+        return;
+    }
     uint32_t xw[NW];
     geo.load_w(x, t, xw);
     float acc[NWP][RP::EPW];
@@ -92,13 +96,14 @@ void launch_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd,
 {
     const int T = h->T, dff = h->d_ff;
     launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, tm, s);
+    const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, false, ws);
     constexpr int NWP = NW < 16 ? NW : 16;
     constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
     const int parts = row_parts<DT>(dm, NWP);
     hipLaunchKernelGGL((hfwd_ell_kernel<DT, NW, NWP, G>), dim3((T + NT / 64 - 1) / (NT / 64), parts),
                        dim3(NT), 0, s, (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col,
                        h->ell_val, T, h->K, dff, (const uint8_t *)wu, (const uint8_t *)wd, dm, y,
-                       status);
+                       bp, h->max_ovf, status);
     tm.mark("hfwd_ell_kernel");
 }
 
