@@ -21,7 +21,7 @@ size_t bwd_workspace_layout(int dt, int T, int dm, int dff, int K, int max_ovf);
 hipError_t launch_hyb_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,
                           const void *wd, int dm, float *y, void *ws, int32_t *status,
                           twell_timing_t *timing, hipStream_t s);
-size_t hyb_fwd_workspace(int dt, int dm, int max_ovf, int dff);
+size_t hyb_fwd_workspace(int dt, int T, int dm, int max_ovf, int dff, int K);
 size_t dec_layer_workspace(int dt, int T, int dm, int dff, int W);
 hipError_t launch_dec_layer(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
                             const void *wd, int dm, const twell_t *o, float *y, void *ws,
@@ -230,7 +230,7 @@ size_t hybrid_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, in
 {
     if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
         return 0;
-    return hyb_fwd_workspace(dt, d_model, max_ovf, d_ff);
+    return hyb_fwd_workspace(dt, T, d_model, max_ovf, d_ff, K);
 }
 
 int hybrid_ffn_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,

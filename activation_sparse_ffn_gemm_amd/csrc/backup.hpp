@@ -22,18 +22,19 @@ void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t 
 void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
                     float *dwg, void *ws, Timer &tm, hipStream_t s);
 
-// Row `slot` of the backup: words [base, base + 64 NW) of a d_model row (EPW
-// floats each, lane l owning words base + 64 c + l) of sum over s of
-// part[s][slot] into out_row. The S loads of a word are issued together.
+// Row `slot` of the backup: words [base, min(base + 64 NW, end, ndw)) of a
+// d_model row (EPW floats each, lane l owning words base + 64 c + l) of sum
+// over s of part[s][slot] into out_row. The S loads of a word go out together.
 template <int NW, int EPW>
-DEVI void bk_finish_row(const BkPart &bp, int slot, int ndw, int base, int lane, float *out_row)
+DEVI void bk_finish_row(const BkPart &bp, int slot, int ndw, int base, int end, int lane,
+                        float *out_row)
 {
     const size_t stride = (size_t)bp.R * ndw * EPW;
     const float *src = bp.part + (size_t)slot * ndw * EPW;
 #pragma unroll
     for (int c = 0; c < NW; ++c) {
         const int w = base + c * 64 + lane;
-        if (w >= ndw)
+        if (w >= ndw || w >= end)
             continue;
         float acc[EPW];
 #pragma unroll

@@ -358,7 +358,8 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
     const int slot = row_slot[t];
     if (slot >= 0) { // a backup row: dx is the sum of the dense product's partials
         if (bp.part && slot < max_ovf)
-            bk_finish_row<NW, R::EPW>(bp, slot, geo.ndw, geo.base, lane, dx + (size_t)t * dm);
+            bk_finish_row<NW, R::EPW>(bp, slot, geo.ndw, geo.base, geo.ndw, lane,
+                                          dx + (size_t)t * dm);
         return;
     }
     const size_t TK = (size_t)T * K, rb = (size_t)t * K;

@@ -22,6 +22,7 @@
 //         the gathers spread over all L2 channels), accumulating y[t]'s slice.
 // Otherwise: one fused pass, a wave per token doing both projections, a is
 // never written to memory.
+#include "backup.hpp"
 #include "rows.hpp"
 
 namespace {
@@ -200,6 +201,21 @@ inline FwdLayout fwd_layout(int dt, int T, int dm, int dff, int W)
     return L;
 }
 
+// Slice-major copy of wd rows [b RL_ROWS, (b+1) RL_ROWS) (padding words set to 0).
+DEVI void copy_slices(int b, const uint32_t *__restrict__ wd, uint32_t *__restrict__ wds, int dff,
+                      Slices sl)
+{
+    const int per = NXCD * sl.swp;
+    for (int q = threadIdx.x; q < RL_ROWS * per; q += NT) {
+        const int i = b * RL_ROWS + q / per;
+        if (i >= dff)
+            break;
+        const int k = (q % per) / sl.swp, w = q % sl.swp, srcw = k * sl.sww + w;
+        const uint32_t v = wd[(size_t)i * sl.ndw + min(srcw, sl.ndw - 1)];
+        wds[((size_t)k * dff + i) * sl.swp + w] = (w < sl.sww && srcw < sl.ndw) ? v : 0u;
+    }
+}
+
 template <int DT, int NW, int G>
 __global__ __launch_bounds__(NT) void fwd_up_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ count,
@@ -214,16 +230,7 @@ __global__ __launch_bounds__(NT) void fwd_up_kernel(
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int b = blockIdx.x;
     if (b < n_copy) {
-        // slice-major copy of RL_ROWS rows of wd (padding words set to 0)
-        const int per = NXCD * sl.swp;
-        for (int q = threadIdx.x; q < RL_ROWS * per; q += NT) {
-            const int i = b * RL_ROWS + q / per;
-            if (i >= dff)
-                break;
-            const int k = (q % per) / sl.swp, w = q % sl.swp, srcw = k * sl.sww + w;
-            const uint32_t v = wd[(size_t)i * sl.ndw + min(srcw, sl.ndw - 1)];
-            wds[((size_t)k * dff + i) * sl.swp + w] = (w < sl.sww && srcw < sl.ndw) ? v : 0u;
-        }
+        copy_slices(b, wd, wds, dff, sl);
         return;
     }
     b -= n_copy; // n_copy is a multiple of 8: b % 8 is still the XCD
@@ -274,11 +281,109 @@ __global__ __launch_bounds__(NT) void fwd_up_kernel(
     });
 }
 
+// Up pass over a hybrid's ELL rows (the forward over the hybrid): XCD k takes
+// the entries whose column lies in its neuron tiles (k = 0 also takes corrupt
+// columns, which are reported and get a = 0), so every slot of every ELL row
+// gets its a = h u written exactly once, in place: ac[t][s] beside
+// ell_col[t][s], which the down pass reads as the entry list. Backup rows are
+// left to the dense products.
+template <int DT, int NW, int G>
+__global__ __launch_bounds__(NT) void hfwd_up_kernel(
+    const uint8_t *__restrict__ x, const int32_t *__restrict__ row_nnz,
+    const int32_t *__restrict__ row_slot, const int16_t *__restrict__ ell_col,
+    const void *__restrict__ ell_val, int T, int K, int nt, const uint8_t *__restrict__ wu,
+    int dm, int n_copy, const uint32_t *__restrict__ wd, uint32_t *__restrict__ wds, int dff,
+    Slices sl, float *__restrict__ ac, int32_t *__restrict__ status)
+{
+    using E = elem<DT>;
+    using R = Row<DT, NW>;
+    __shared__ int lcol[NT / 64][64];
+    __shared__ int lslot[NT / 64][64];
+    __shared__ float lval[NT / 64][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int b = blockIdx.x;
+    if (b < n_copy) {
+        copy_slices(b, wd, wds, dff, sl);
+        return;
+    }
+    b -= n_copy; // n_copy is a multiple of 8: b % 8 is still the XCD
+    const int k = b % NXCD;
+    const int t = (b / NXCD) * (NT / 64) + wv;
+    if (t >= T || row_slot[t] >= 0)
+        return;
+    const int c0 = (k * nt / NXCD) * TWELL_TILE_C, c1 = ((k + 1) * nt / NXCD) * TWELL_TILE_C;
+    const int n = min(row_nnz[t], K);
+    const size_t rb = (size_t)t * K;
+    const R geo(dm, lane, 0);
+    uint32_t xw[NW];
+    bool have_x = false;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const int s = s0 + lane;
+        int c = 0;
+        float h = 0.f;
+        bool mine = false;
+        if (s < n) {
+            c = ell_col[rb + s];
+            h = E::load1(ell_val, rb + s);
+            const bool bad = c < 0 || c >= dff;
+            mine = bad ? k == 0 : (c >= c0 && c < c1);
+            if (mine && bad) {
+                raise_status(status, TWELL_DEV_BAD_INDEX);
+                c = 0;
+                h = 0.f;
+            }
+        }
+        const uint64_t msk = __ballot(mine);
+        const int m = __popcll(msk);
+        if (m == 0) // uniform
+            continue;
+        if (!have_x) {
+            geo.load_w(x, t, xw);
+            have_x = true;
+        }
+        if (mine) {
+            const int r = __popcll(msk & below);
+            lcol[wv][r] = c;
+            lslot[wv][r] = s;
+            lval[wv][r] = h;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // stream the m entries through G register buffers; lane e keeps entry
+        // e's a and writes it at the end
+        uint32_t vu[G][NW];
+        auto fetch = [&](int e, uint32_t (&u)[NW]) { geo.load_w(wu, lcol[wv][min(e, m - 1)], u); };
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            fetch(g, vu[g]);
+        float a = 0.f;
+        for (int e0 = 0; e0 < m; e0 += G) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int e = e0 + g;
+                const float u = wave_sum(geo.dotw(xw, vu[g]));
+                if (lane == e && e < m)
+                    a = lval[wv][e] * u;
+                fetch(e + G, vu[g]);
+            }
+        }
+        if (lane < m)
+            ac[rb + lslot[wv][lane]] = a;
+        __builtin_amdgcn_wave_barrier(); // the lists are rewritten by the next chunk
+    }
+}
+
+// Down pass: y[t][slice k] from the token's (a, column) list. For the forward
+// over a hybrid (row_slot non-null) the list is the ELL row itself and a
+// backup row's slice is the sum, in split order, of the dense product's
+// partials.
 template <int DT, int SPL, int G>
 __global__ __launch_bounds__(NT) void fwd_down_kernel(
     const uint32_t *__restrict__ wds, int dff, Slices sl, const float *__restrict__ ac,
     const int16_t *__restrict__ cc, const int32_t *__restrict__ rn, int cap, int T, int dm,
-    float *__restrict__ y)
+    float *__restrict__ y, const int32_t *__restrict__ row_slot, BkPart bp, int max_ovf)
 {
     constexpr int EPW = DT == TWELL_BF16 ? 2 : 1;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -287,7 +392,16 @@ __global__ __launch_bounds__(NT) void fwd_down_kernel(
     const int nk = sl.valid(k);
     if (t >= T || nk == 0)
         return;
-    const int n = rn[t];
+    if (row_slot) {
+        const int slot = row_slot[t];
+        if (slot >= 0) {
+            if (bp.part && slot < max_ovf)
+                bk_finish_row<SPL, EPW>(bp, slot, sl.ndw, k * sl.sww, k * sl.sww + nk, lane,
+                                        y + (size_t)t * dm);
+            return;
+        }
+    }
+    const int n = min(rn[t], cap);
     const float *arow = ac + (size_t)t * cap;
     const int16_t *crow = cc + (size_t)t * cap;
     const uint32_t *slice = wds + (size_t)k * dff * sl.swp;
@@ -304,7 +418,7 @@ __global__ __launch_bounds__(NT) void fwd_down_kernel(
         uint32_t v[G][SPL];
         // the row's slice through a buffer descriptor: words past nk read 0
         auto fetch = [&](int e, uint32_t (&w)[SPL]) {
-            const int c = bcast(ci, min(e, m - 1));
+            const int c = min(max(bcast(ci, min(e, m - 1)), 0), dff - 1);
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(slice + (size_t)c * sl.swp), (short)0, nk * 4, BUF_DWORD3);
 #pragma unroll
@@ -379,13 +493,13 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
     const int spl = (sl.sww + 63) / 64;
     if (spl <= 1)
         hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
-                           dff, sl, ac, cc, rn, L.cap, T, dm, y);
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
     else if (spl == 2)
         hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
-                           dff, sl, ac, cc, rn, L.cap, T, dm, y);
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
     else
         hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
-                           dff, sl, ac, cc, rn, L.cap, T, dm, y);
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
     tm.mark("fwd_down_kernel");
 }
 
@@ -403,6 +517,73 @@ void launch_dt(const void *x, const twell_t *h, const void *wu, const void *wd, 
 }
 
 } // namespace
+
+// ---- the forward over a hybrid's ELL rows, two-pass form (hyb_fwd.hip)
+bool hyb_use_split(int dt, int T, int dm, int dff) { return use_split(dt, T, dm, dff); }
+
+// slice-major wd copy, then a per ELL slot (float32 [T][K])
+size_t hyb_split_workspace(int dt, int T, int dm, int dff, int K)
+{
+    const Slices sl = slices(dt, dm);
+    return up256((size_t)NXCD * dff * sl.swp * 4) + up256((size_t)T * K * 4);
+}
+
+namespace {
+template <int DT, int NW>
+void launch_hyb_split_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd, int dm,
+                         float *y, uint8_t *ws, BkPart bp, int32_t *status, Timer &tm,
+                         hipStream_t s)
+{
+    const int T = h->T, dff = h->d_ff, nt = dff / TWELL_TILE_C;
+    const int groups = (T + NT / 64 - 1) / (NT / 64);
+    const Slices sl = slices(DT, dm);
+    uint32_t *wds = (uint32_t *)ws;
+    float *ac = (float *)(ws + up256((size_t)NXCD * dff * sl.swp * 4));
+    const int n_copy = ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD;
+    constexpr int GU = NW <= 16 ? 4 : 2;
+    hipLaunchKernelGGL((hfwd_up_kernel<DT, NW, GU>), dim3(n_copy + groups * NXCD), dim3(NT), 0, s,
+                       (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col, h->ell_val, T,
+                       h->K, nt, (const uint8_t *)wu, dm, n_copy, (const uint32_t *)wd, wds, dff,
+                       sl, ac, status);
+    tm.mark("hfwd_up_kernel");
+    const int spl = (sl.sww + 63) / 64;
+    if (spl <= 1)
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
+                           h->max_ovf);
+    else if (spl == 2)
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
+                           h->max_ovf);
+    else
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
+                           h->max_ovf);
+    tm.mark("hfwd_down_kernel");
+}
+} // namespace
+
+void launch_hyb_split(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
+                      const void *wd, int dm, float *y, void *ws, BkPart bp, int32_t *status,
+                      Timer &tm, hipStream_t s)
+{
+#define TW_CASE(D, N) \
+    case N: launch_hyb_split_nw<D, N>(x, h, wu, wd, dm, y, (uint8_t *)ws, bp, status, tm, s); break;
+    if (dt == TWELL_BF16) {
+        switch (row_nw<TWELL_BF16>(dm)) {
+            TW_CASE(TWELL_BF16, 1) TW_CASE(TWELL_BF16, 2) TW_CASE(TWELL_BF16, 4)
+            TW_CASE(TWELL_BF16, 8) TW_CASE(TWELL_BF16, 16)
+        default: launch_hyb_split_nw<TWELL_BF16, 32>(x, h, wu, wd, dm, y, (uint8_t *)ws, bp, status, tm, s);
+        }
+    } else {
+        switch (row_nw<TWELL_F32>(dm)) {
+            TW_CASE(TWELL_F32, 1) TW_CASE(TWELL_F32, 2) TW_CASE(TWELL_F32, 4)
+            TW_CASE(TWELL_F32, 8) TW_CASE(TWELL_F32, 16)
+        default: launch_hyb_split_nw<TWELL_F32, 32>(x, h, wu, wd, dm, y, (uint8_t *)ws, bp, status, tm, s);
+        }
+    }
+#undef TW_CASE
+}
 
 size_t dec_ffn_workspace(int dt, int T, int dm, int dff, int W);
 hipError_t launch_dec_ffn(twell_dtype dt, const void *x, const twell_t *h, const void *wu_t,

@@ -16,6 +16,12 @@
 #include "rows.hpp"
 
 
+bool hyb_use_split(int dt, int T, int dm, int dff);
+size_t hyb_split_workspace(int dt, int T, int dm, int dff, int K);
+void launch_hyb_split(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
+                      const void *wd, int dm, float *y, void *ws, BkPart bp, int32_t *status,
+                      Timer &tm, hipStream_t s);
+
 namespace {
 
 constexpr int NT = 256; // 4 waves = 4 rows per workgroup
@@ -41,7 +47,8 @@ __global__ __launch_bounds__(NT) void hfwd_ell_kernel(
     const int slot = row_slot[t];
     if (slot >= 0) { // a backup row: y is the sum of the dense product's partials
         if (bp.part && slot < max_ovf)
-            bk_finish_row<NWP, RP::EPW>(bp, slot, part.ndw, part.base, lane, y + (size_t)t * dm);
+            bk_finish_row<NWP, RP::EPW>(bp, slot, part.ndw, part.base, part.ndw, lane,
+                                            y + (size_t)t * dm);
         return;
     }
     uint32_t xw[NW];
@@ -97,6 +104,11 @@ void launch_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd,
     const int T = h->T, dff = h->d_ff;
     launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, tm, s);
     const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, false, ws);
+    if (hyb_use_split(DT, T, dm, dff)) { // many tokens, large weights: XCD-local passes
+        const size_t off = (bk_workspace(DT, dm, dff, h->max_ovf, false) + 255) & ~(size_t)255;
+        launch_hyb_split((twell_dtype)DT, x, h, wu, wd, dm, y, ws + off, bp, status, tm, s);
+        return;
+    }
     constexpr int NWP = NW < 16 ? NW : 16;
     constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
     const int parts = row_parts<DT>(dm, NWP);
@@ -124,9 +136,10 @@ void launch_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
 
 // The backup rows' products (their intermediate A, W_d^T and the split-K
 // partials of y_O).
-size_t hyb_fwd_workspace(int dt, int dm, int max_ovf, int dff)
+size_t hyb_fwd_workspace(int dt, int T, int dm, int max_ovf, int dff, int K)
 {
-    return bk_workspace(dt, dm, dff, max_ovf, false);
+    const size_t bk = (bk_workspace(dt, dm, dff, max_ovf, false) + 255) & ~(size_t)255;
+    return bk + (hyb_use_split(dt, T, dm, dff) ? hyb_split_workspace(dt, T, dm, dff, K) : 0);
 }
 
 hipError_t launch_hyb_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu_t,

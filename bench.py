@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "fwd_up_kernel": "ffn_fwd.hip", "fwd_down_kernel": "ffn_fwd.hip",
     "hyb_rows_kernel": "to_hybrid.hip", "hyb_slots_kernel": "to_hybrid.hip",
     "hyb_dense_kernel": "to_hybrid.hip", "hfwd_ell_kernel": "hyb_fwd.hip",
+    "hfwd_up_kernel": "ffn_fwd.hip", "hfwd_down_kernel": "ffn_fwd.hip",
     "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "bk_ud_kernel": "backup.hip",
     "bk_dx_kernel": "backup.hip", "bk_dw_kernel": "backup.hip",
 }
@@ -243,6 +244,11 @@ def main():
                           "per ELL nonzero one wu_t row + one wg_t row + col, du, dg; dx rows"),
         "hfwd_ell_kernel": ("hbm", nnz_ell * (2 * row_b + 4) + T_ell * (row_b + dm * 4),
                             "per ELL nonzero one wu_t row + one wd row + (col, h); x, y rows"),
+        "hfwd_up_kernel": ("hbm", nnz_ell * (row_b + 8) + T_ell * row_b + 2 * dff * row_b,
+                           "per ELL nonzero one wu_t row + (col, h) + a written; x rows; wd "
+                           "slice-major copy (read + write)"),
+        "hfwd_down_kernel": ("hbm", nnz_ell * (row_b + 6) + T_ell * dm * 4,
+                             "per ELL nonzero one wd row (as 8 slices) + (col, a); y rows"),
         "bk_a_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "A = h_O (.) x_O W_u (1 GEMM)"),
         "bk_y_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "y_O = A W_d (1 GEMM)"),
         "bk_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "u_O and da_O (2 GEMMs)"),
