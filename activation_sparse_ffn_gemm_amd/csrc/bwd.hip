@@ -35,6 +35,7 @@
 //      neuron pass has written every dW row.
 #include "backup.hpp"
 #include "rows.hpp"
+#include "slices.hpp"
 
 namespace {
 
@@ -44,15 +45,26 @@ constexpr int CH = 1024;  // neurons per workgroup of the mask launch (8 KB of L
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The dx pass gathers two weight rows per entry. With many tokens and
+// weights well beyond one XCD's L2 it runs XCD-local (slices.hpp): XCD k sums
+// the k-th slice of d_model from an interleaved slice-major copy of wu_t and
+// wg_t, which the masks launch makes on the side.
+inline bool dx_split(int dt, int T, int dm, int dff)
+{
+    return T >= 1024 && (size_t)dff * dm * (dt == TWELL_BF16 ? 2 : 4) >= ((size_t)16 << 20);
+}
+
 struct Layout {
-    size_t coef, masks, cnt, colptr, csc, backup, total;
+    size_t coef, masks, cnt, colptr, csc, backup, wsl, total;
     int nblk;
+    bool split;
 };
 
 Layout layout(int dt, int T, int dm, int dff, int K, int max_ovf)
 {
     Layout L;
     L.nblk = (T + BR - 1) / BR;
+    L.split = dx_split(dt, T, dm, dff);
     size_t o = 0;
     L.coef = o;   o += up256((size_t)2 * T * K * 4); // du, dg per ELL slot
     L.masks = o;  o += up256((size_t)L.nblk * dff * 8);
@@ -60,6 +72,7 @@ Layout layout(int dt, int T, int dm, int dff, int K, int max_ovf)
     L.colptr = o; o += up256((size_t)(dff + 1) * 4);
     L.csc = o;    o += up256((size_t)T * K * 4);
     L.backup = o; o += up256(bk_workspace(dt, dm, dff, max_ovf, true));
+    L.wsl = o;    o += L.split ? up256((size_t)NXCD * dff * 2 * slices(dt, dm).swp * 4) : 0;
     L.total = o;
     return L;
 }
@@ -408,16 +421,123 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 }
 
 // ------------------------------------------------------------ masks launch
+// Workgroups b < n_mask build masks; the others (if any) copy wu_t and wg_t
+// into the dx pass's interleaved slice-major array.
 __global__ __launch_bounds__(NT) void mask_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, int T, int K, int dff, uint64_t *__restrict__ masks,
-    int32_t *__restrict__ cnt, int n_chunk)
+    int32_t *__restrict__ cnt, int n_chunk, int n_mask, const uint32_t *__restrict__ wu,
+    const uint32_t *__restrict__ wg, uint32_t *__restrict__ wsl, Slices sl)
 {
     __shared__ unsigned long long m[CH];
     __shared__ int rn[BR];
     const int b = blockIdx.x;
+    if (b >= n_mask) {
+        copy_slices_rows<2, NT>(b - n_mask, wu, wg, wsl, dff, sl);
+        return;
+    }
     ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk, b % n_chunk,
                    m, rn);
+}
+
+// ------------------------------------------------------------ 5'. dx, XCD-local
+// XCD k (workgroup b % 8) sums slice k of dx[t] for four tokens per workgroup:
+// per entry the slices of wu_t[i] and wg_t[i] (adjacent in the copy) with
+// the entry's du and dg. Backup rows get the sum of their dense product's
+// partials for the slice.
+template <int DT, int SPL, int G>
+__global__ __launch_bounds__(NT) void bwd_dxs_kernel(
+    const uint32_t *__restrict__ wsl, int dff, Slices sl, const int32_t *__restrict__ row_nnz,
+    const int32_t *__restrict__ row_slot, const int16_t *__restrict__ ell_col,
+    const float *__restrict__ coef, int T, int K, int dm, float *__restrict__ dx, BkPart bp,
+    int max_ovf)
+{
+    constexpr int EPW = DT == TWELL_BF16 ? 2 : 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int k = blockIdx.x % NXCD;
+    const int t = (blockIdx.x / NXCD) * (NT / 64) + wv;
+    const int nk = sl.valid(k);
+    if (t >= T || nk == 0)
+        return;
+    const int slot = row_slot[t];
+    if (slot >= 0) {
+        if (bp.part && slot < max_ovf)
+            bk_finish_row<SPL, EPW>(bp, slot, sl.ndw, k * sl.sww, k * sl.sww + nk, lane,
+                                    dx + (size_t)t * dm);
+        return;
+    }
+    const int n = min(row_nnz[t], K);
+    const size_t TK = (size_t)T * K, rb = (size_t)t * K;
+    const uint32_t *slice = wsl + (size_t)k * dff * 2 * sl.swp;
+    float acc[SPL][EPW];
+#pragma unroll
+    for (int q = 0; q < SPL; ++q)
+#pragma unroll
+        for (int e = 0; e < EPW; ++e)
+            acc[q][e] = 0.f;
+    for (int eb = 0; eb < n; eb += 64) {
+        const int m = min(64, n - eb), s = eb + lane;
+        int ci = 0;
+        float cu = 0.f, cg = 0.f;
+        if (lane < m) {
+            ci = ell_col[rb + s];
+            cu = coef[rb + s];
+            cg = coef[TK + rb + s];
+            if (ci < 0 || ci >= dff) {
+                ci = 0;
+                cu = cg = 0.f;
+            }
+        }
+        // the row's two slices through one buffer descriptor: words past the
+        // row's 2 swp read 0, words past nk are never stored
+        uint32_t vu[G][SPL], vg[G][SPL];
+        auto fetch = [&](int e, uint32_t (&u)[SPL], uint32_t (&g)[SPL]) {
+            const int c = bcast(ci, min(e, m - 1));
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(slice + (size_t)c * 2 * sl.swp), (short)0, 2 * sl.swp * 4, BUF_DWORD3);
+#pragma unroll
+            for (int q = 0; q < SPL; ++q) {
+                u[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (q * 64 + lane) * 4, 0, 0);
+                g[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (sl.swp + q * 64 + lane) * 4, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            fetch(g, vu[g], vg[g]);
+        for (int e0 = 0; e0 < m; e0 += G) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int e = e0 + g;
+                if (e < m) { // uniform
+                    const float a = bcast(cu, e), b = bcast(cg, e);
+#pragma unroll
+                    for (int q = 0; q < SPL; ++q) {
+                        if constexpr (EPW == 2) {
+                            acc[q][0] += a * bf16_lo(vu[g][q]);
+                            acc[q][1] += a * bf16_hi(vu[g][q]);
+                            acc[q][0] += b * bf16_lo(vg[g][q]);
+                            acc[q][1] += b * bf16_hi(vg[g][q]);
+                        } else {
+                            acc[q][0] += a * __uint_as_float(vu[g][q]);
+                            acc[q][0] += b * __uint_as_float(vg[g][q]);
+                        }
+                    }
+                }
+                fetch(e + G, vu[g], vg[g]);
+            }
+        }
+    }
+    float *row = dx + (size_t)t * dm + (size_t)k * sl.sww * EPW;
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+        const int w = q * 64 + lane;
+        if (w < nk) {
+            if constexpr (EPW == 2)
+                *(float2 *)(row + 2 * w) = make_float2(acc[q][0], acc[q][1]);
+            else
+                row[w] = acc[q][0];
+        }
+    }
 }
 
 template <int DT, int NW>
@@ -442,10 +562,14 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     constexpr int NWP = NW < ACC_NW ? NW : ACC_NW; // dx pass: words per lane of one part
     const int parts = row_parts<DT>(dm, NWP);
 
+    const Slices sl = slices(DT, dm);
+    uint32_t *wsl = (uint32_t *)(ws + L.wsl);
     if (T > 0) {
-        const int n_chunk = (dff + CH - 1) / CH;
-        hipLaunchKernelGGL(mask_kernel, dim3(L.nblk * n_chunk), dim3(NT), 0, s, h->row_nnz,
-                           h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk);
+        const int n_chunk = (dff + CH - 1) / CH, n_mask = L.nblk * n_chunk;
+        const int n_copy = L.split ? copy_groups(dff) : 0;
+        hipLaunchKernelGGL(mask_kernel, dim3(n_mask + n_copy), dim3(NT), 0, s, h->row_nnz,
+                           h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk, n_mask,
+                           (const uint32_t *)wu, (const uint32_t *)wg, wsl, sl);
         tm.mark("mask_kernel");
     }
     launch_bk_ud((twell_dtype)DT, x, dy, h, wu, wg, wd, dm, l1, ws + L.backup, tm, s);
@@ -469,10 +593,28 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     launch_bk_dxdw((twell_dtype)DT, h, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
     if (T > 0) {
         const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, true, ws + L.backup);
-        hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, GD>), dim3(rgroups, parts), dim3(NT), 0, s,
-                           h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dff,
-                           (const uint8_t *)wu, (const uint8_t *)wg, dm, dx, bp, h->max_ovf);
-        tm.mark("bwd_dx_kernel");
+        if (L.split) {
+            const int spl = (sl.sww + 63) / 64;
+            const dim3 grid(rgroups * NXCD);
+            if (spl <= 1)
+                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 1, 8>), grid, dim3(NT), 0, s, wsl, dff, sl,
+                                   h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dm, dx, bp,
+                                   h->max_ovf);
+            else if (spl == 2)
+                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 2, 4>), grid, dim3(NT), 0, s, wsl, dff, sl,
+                                   h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dm, dx, bp,
+                                   h->max_ovf);
+            else
+                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 4, 2>), grid, dim3(NT), 0, s, wsl, dff, sl,
+                                   h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dm, dx, bp,
+                                   h->max_ovf);
+            tm.mark("bwd_dxs_kernel");
+        } else {
+            hipLaunchKernelGGL((bwd_dx_kernel<DT, NWP, GD>), dim3(rgroups, parts), dim3(NT), 0, s,
+                               h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dff,
+                               (const uint8_t *)wu, (const uint8_t *)wg, dm, dx, bp, h->max_ovf);
+            tm.mark("bwd_dx_kernel");
+        }
     }
 }
 

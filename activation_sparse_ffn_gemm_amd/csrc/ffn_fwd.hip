@@ -24,6 +24,7 @@
 // never written to memory.
 #include "backup.hpp"
 #include "rows.hpp"
+#include "slices.hpp"
 
 namespace {
 
@@ -39,7 +40,6 @@ inline bool use_split(int dt, int T, int dm, int dff)
 {
     return T >= SPLIT_T && (size_t)dff * dm * (dt == TWELL_BF16 ? 2 : 4) >= SPLIT_W;
 }
-constexpr int RL_ROWS = 8;    // wd rows per workgroup of the slice-major copy
 
 // Stage the stored entries of row t, tiles [j0, j1), into LDS: element e of
 // the list is (column, value). Calls fn(p0, ne) after each pass of up to LIST
@@ -161,23 +161,6 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------- split
-// Geometry of the slice-major copy of wd: slice k holds words
-// [k sww, k sww + sww) of every row (fewer in the last slices), each row's
-// slice padded to swp words (a multiple of 32: whole 128-byte lines).
-struct Slices {
-    int ndw, sww, swp;
-    DEVI int valid(int k) const { return max(0, min(sww, ndw - k * sww)); }
-};
-
-inline Slices slices(int dt, int dm)
-{
-    Slices s;
-    s.ndw = dt == TWELL_BF16 ? dm / 2 : dm;
-    s.sww = (s.ndw + NXCD - 1) / NXCD;
-    s.swp = (s.sww + 31) / 32 * 32;
-    return s;
-}
-
 // Workspace of the two-pass design: slice-major wd, then the compact entry
 // lists (a as float32, columns as int16) and their lengths.
 struct FwdLayout {
@@ -201,19 +184,10 @@ inline FwdLayout fwd_layout(int dt, int T, int dm, int dff, int W)
     return L;
 }
 
-// Slice-major copy of wd rows [b RL_ROWS, (b+1) RL_ROWS) (padding words set to 0).
 DEVI void copy_slices(int b, const uint32_t *__restrict__ wd, uint32_t *__restrict__ wds, int dff,
                       Slices sl)
 {
-    const int per = NXCD * sl.swp;
-    for (int q = threadIdx.x; q < RL_ROWS * per; q += NT) {
-        const int i = b * RL_ROWS + q / per;
-        if (i >= dff)
-            break;
-        const int k = (q % per) / sl.swp, w = q % sl.swp, srcw = k * sl.sww + w;
-        const uint32_t v = wd[(size_t)i * sl.ndw + min(srcw, sl.ndw - 1)];
-        wds[((size_t)k * dff + i) * sl.swp + w] = (w < sl.sww && srcw < sl.ndw) ? v : 0u;
-    }
+    copy_slices_rows<1, NT>(b, wd, nullptr, wds, dff, sl);
 }
 
 template <int DT, int NW, int G>

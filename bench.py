@@ -242,6 +242,9 @@ def main():
                               "per neuron wu_t + wd rows and three fp32 dW rows"),
         "bwd_dx_kernel": ("hbm", nnz_ell * (2 * row_b + 10) + 8 * T + T_ell * dm * 4,
                           "per ELL nonzero one wu_t row + one wg_t row + col, du, dg; dx rows"),
+        "bwd_dxs_kernel": ("hbm", nnz_ell * (2 * row_b + 10) + 8 * T + T_ell * dm * 4,
+                           "per ELL nonzero one wu_t row + one wg_t row (as 8 slices each) + col, "
+                           "du, dg; dx rows"),
         "hfwd_ell_kernel": ("hbm", nnz_ell * (2 * row_b + 4) + T_ell * (row_b + dm * 4),
                             "per ELL nonzero one wu_t row + one wd row + (col, h); x, y rows"),
         "hfwd_up_kernel": ("hbm", nnz_ell * (row_b + 8) + T_ell * row_b + 2 * dff * row_b,
