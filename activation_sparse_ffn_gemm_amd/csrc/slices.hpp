@@ -34,21 +34,39 @@ constexpr int RL_ROWS = 8; // weight rows per workgroup of the copy
 inline int copy_groups(int dff) { return ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD; }
 
 // Workgroup b of NTH threads copies rows [b RL_ROWS, (b+1) RL_ROWS) of a (and
-// b) into the slice-major array dst (padding words set to 0).
+// b) into the slice-major array dst (padding words set to 0), 16 bytes per
+// lane: with d_model % 64 == 0, ndw, sww and swp are multiples of 4 words, so
+// a 4-word group is wholly inside or wholly outside a slice.
 template <int NSRC, int NTH>
 DEVI void copy_slices_rows(int b, const uint32_t *__restrict__ a, const uint32_t *__restrict__ bm,
                            uint32_t *__restrict__ dst, int dff, Slices sl)
 {
-    const int rw = NSRC * sl.swp; // words of one row of one slice
+    const int sw4 = sl.swp / 4, ss4 = sl.sww / 4, nd4 = sl.ndw / 4;
+    const int rw = NSRC * sw4; // 4-word groups of one row of one slice
     const int per = NXCD * rw;
-    for (int q = threadIdx.x; q < RL_ROWS * per; q += NTH) {
-        const int i = b * RL_ROWS + q / per;
-        if (i >= dff)
-            break;
-        const int k = (q % per) / rw, r = q % rw, m = r / sl.swp, w = r % sl.swp;
-        const int srcw = k * sl.sww + w;
-        const uint32_t *src = m == 0 ? a : bm;
-        const uint32_t v = src[(size_t)i * sl.ndw + min(srcw, sl.ndw - 1)];
-        dst[((size_t)k * dff + i) * rw + r] = (w < sl.sww && srcw < sl.ndw) ? v : 0u;
+    const int nq = min(RL_ROWS, dff - b * RL_ROWS) * per;
+    constexpr int U = 4; // independent loads in flight per thread
+    for (int q0 = threadIdx.x; q0 < nq; q0 += U * NTH) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = min(q0 + u * NTH, nq - 1);
+            const int i = b * RL_ROWS + q / per;
+            const int k = (q % per) / rw, r = q % rw, m = r / sw4, w = r % sw4;
+            const int src4 = k * ss4 + w;
+            const uint32_t *src = m == 0 ? a : bm;
+            v[u] = *(const uint4 *)(src + ((size_t)i * nd4 + min(src4, nd4 - 1)) * 4);
+            if (w >= ss4 || src4 >= nd4)
+                v[u] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * NTH;
+            if (q < nq) {
+                const int i = b * RL_ROWS + q / per;
+                const int k = (q % per) / rw, r = q % rw;
+                *(uint4 *)(dst + (((size_t)k * dff + i) * rw + r) * 4) = v[u];
+            }
+        }
     }
 }
