@@ -37,7 +37,6 @@ namespace {
 
 using C1 = ng::Cfg<128, 128, 2, 2>; // 4 waves, 64 x 64 each
 constexpr int TILE = 128;
-constexpr int TT = 64;              // transpose tile (elements per side)
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 int pad_rows(int max_ovf) { return (max_ovf + TILE - 1) / TILE * TILE; }
@@ -54,59 +53,6 @@ int split_k(int R, int dm, int nk)
     S = std::min(S, 16);
     S = std::min(S, std::max(1, nk / 16));
     return S;
-}
-
-// ---------------------------------------------------------------- transposes
-template <int DT> using Store = typename elem<DT>::storage;
-
-// One TT x TT tile of out[c][r] = in[src(r)][c] for c < cols and r < rows_out,
-// src(r) = r, or gather[r] for r < n_valid and a zero row past it (gather
-// non-null). 256 threads; lds: TT x (TT + 8) elements.
-template <typename T>
-DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols, int rows_out,
-                         const int32_t *__restrict__ gather, int n_valid, int bx, int by,
-                         uint8_t *lds)
-{
-    constexpr int V = 16 / sizeof(T), TP = TT + 8; // elements per 16-byte chunk, LDS pitch
-    T(*tile)[TP] = (T(*)[TP])lds;
-    const int c0 = bx * TT, r0 = by * TT, tid = threadIdx.x;
-    if (gather && r0 >= (n_valid + TT - 1) / TT * TT)
-        return; // never read: the products stop at the padded row count
-    constexpr int CPR = TT / V; // chunks per tile row
-    for (int q = tid; q < TT * CPR; q += 256) {
-        const int r = q / CPR, cc = q % CPR, gr = r0 + r, gc = c0 + cc * V;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (gr < n_valid && gc < cols) {
-            const int sr = gather ? gather[gr] : gr;
-            v = *(const uint4 *)(in + (size_t)sr * cols + gc);
-        }
-        const T *e = (const T *)&v;
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            tile[r][cc * V + k] = e[k];
-    }
-    __syncthreads();
-    for (int q = tid; q < TT * CPR; q += 256) {
-        const int c = q / CPR, rc = q % CPR, gc = c0 + c, gr = r0 + rc * V;
-        if (gc >= cols || gr >= rows_out)
-            continue;
-        T e[V];
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            e[k] = tile[rc * V + k][c];
-        *(uint4 *)(out + (size_t)gc * rows_out + gr) = *(const uint4 *)e;
-    }
-    __syncthreads(); // lds is reused by the workgroup's next tile
-}
-
-// Tiles of a weight transpose [dff][dm] -> [dm][dff]
-DEVI int wt_tiles(int dm, int dff) { return (dm / TT) * (dff / TT); }
-template <int DT>
-DEVI void weight_t_tile(const void *w, void *wt, int dm, int dff, int b, uint8_t *lds)
-{
-    const int nx = dm / TT;
-    transpose_tile<Store<DT>>((const Store<DT> *)w, (Store<DT> *)wt, dm, dff, nullptr, dff, b % nx,
-                              b / nx, lds);
 }
 
 // ---------------------------------------------------------------- products
@@ -363,39 +309,21 @@ __global__ __launch_bounds__(C1::NT, 2) void bk_a_kernel(
         weight_t_tile<DT>(wd, wdt, dm, dff, b - n_a, L);
 }
 
-// backward: the u/da tiles, then the transposes of W_u, W_g, x_O and dy_O
+// backward: the u/da tiles (the transposes run beside the ELL masks)
 template <int DT>
 __global__ __launch_bounds__(C1::NT, 1) void bk_ud_kernel(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
-    const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wg,
-    const uint8_t *__restrict__ wd, int dm, int dff, int R, const void *__restrict__ dense,
-    float l1, void *__restrict__ inter, void *__restrict__ inter_t, void *__restrict__ wt,
-    void *__restrict__ xt, int n_ud)
+    const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff, int R,
+    const void *__restrict__ dense, float l1, void *__restrict__ inter, void *__restrict__ inter_t)
 {
     __shared__ __attribute__((aligned(16))) uint8_t L[UD_LDS];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
-    int b = blockIdx.x;
-    const int nx = dff / TILE;
-    if (b < n_ud) {
-        ud_tile<DT, true>(x, dy, ovf_rows, n, wu, wd, dm, dff, R, dense, l1, inter, inter_t,
-                          b % nx, b / nx, L);
-        return;
-    }
-    b -= n_ud;
-    using T = Store<DT>;
-    const int nw = wt_tiles(dm, dff);
-    if (b < 2 * nw) { // W_u^T, W_g^T
-        const int z = b / nw;
-        weight_t_tile<DT>(z ? wg : wu, (T *)wt + (size_t)z * dm * dff, dm, dff, b % nw, L);
-        return;
-    }
-    b -= 2 * nw; // x_O^T, dy_O^T: [dm][R]
-    const int ng_ = (dm / TT) * (R / TT), z = b / ng_, q = b % ng_, gx = dm / TT;
-    transpose_tile<T>((const T *)(z ? dy : x), (T *)xt + (size_t)z * dm * R, dm, R, ovf_rows, n,
-                      q % gx, q / gx, L);
+    const int b = blockIdx.x, nx = dff / TILE;
+    ud_tile<DT, true>(x, dy, ovf_rows, n, wu, wd, dm, dff, R, dense, l1, inter, inter_t, b % nx,
+                      b / nx, L);
 }
 
 template <int DT, int NH>
@@ -491,18 +419,16 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
 }
 
 template <int DT>
-void bk_ud_dt(const void *x, const void *dy, const hybrid_t *h, const void *wu, const void *wg,
-              const void *wd, int dm, float l1, uint8_t *ws, Timer &tm, hipStream_t s)
+void bk_ud_dt(const void *x, const void *dy, const hybrid_t *h, const void *wu, const void *wd,
+              int dm, float l1, uint8_t *ws, Timer &tm, hipStream_t s)
 {
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
     const int n_ud = (dff / TILE) * (L.R / TILE);
-    const int n_t = 2 * (dm / TT) * (dff / TT) + 2 * (dm / TT) * (L.R / TT);
-    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud + n_t), dim3(C1::NT), 0, s,
-                       (const uint8_t *)x, (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
-                       (const uint8_t *)wu, (const uint8_t *)wg, (const uint8_t *)wd, dm, dff, L.R,
-                       h->dense, l1, (void *)(ws + L.inter), (void *)(ws + L.inter_t),
-                       (void *)(ws + L.wt), (void *)(ws + L.xt), n_ud);
+    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud), dim3(C1::NT), 0, s, (const uint8_t *)x,
+                       (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
+                       (const uint8_t *)wu, (const uint8_t *)wd, dm, dff, L.R, h->dense, l1,
+                       (void *)(ws + L.inter), (void *)(ws + L.inter_t));
     tm.mark("bk_ud_kernel");
 }
 
@@ -547,15 +473,24 @@ void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void 
 }
 
 void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
-                  const void *wu, const void *wg, const void *wd, int dm, float l1, void *ws,
-                  Timer &tm, hipStream_t s)
+                  const void *wu, const void *wd, int dm, float l1, void *ws, Timer &tm,
+                  hipStream_t s)
 {
     if (h->max_ovf <= 0 || h->T <= 0)
         return;
     if (dt == TWELL_BF16)
-        bk_ud_dt<TWELL_BF16>(x, dy, h, wu, wg, wd, dm, l1, (uint8_t *)ws, tm, s);
+        bk_ud_dt<TWELL_BF16>(x, dy, h, wu, wd, dm, l1, (uint8_t *)ws, tm, s);
     else
-        bk_ud_dt<TWELL_F32>(x, dy, h, wu, wg, wd, dm, l1, (uint8_t *)ws, tm, s);
+        bk_ud_dt<TWELL_F32>(x, dy, h, wu, wd, dm, l1, (uint8_t *)ws, tm, s);
+}
+
+BkXpose bk_xpose(int dt, int dm, int dff, int max_ovf, void *ws)
+{
+    if (max_ovf <= 0)
+        return BkXpose{nullptr, nullptr, 0, 0};
+    const BkLayout L = bk_layout(dt, dm, dff, max_ovf, true);
+    return BkXpose{(uint8_t *)ws + L.wt, (uint8_t *)ws + L.xt, L.R,
+                   bk_xpose_blocks(dm, dff, L.R)};
 }
 
 void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,

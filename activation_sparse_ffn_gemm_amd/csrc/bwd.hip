@@ -421,23 +421,36 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 }
 
 // ------------------------------------------------------------ masks launch
-// Workgroups b < n_mask build masks; the others (if any) copy wu_t and wg_t
-// into the dx pass's interleaved slice-major array.
+// Work that only has to be done before later passes rides on the masks
+// launch: workgroups b < n_mask build masks; the next n_copy copy wu_t and
+// wg_t into the dx pass's interleaved slice-major array; the rest make the
+// backup products' transposed copies.
+constexpr int MASK_LDS = CH * 8 + BR * 4;
+constexpr int XPOSE_LDS = TT * (TT + 8) * 4;
+template <int DT>
 __global__ __launch_bounds__(NT) void mask_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, int T, int K, int dff, uint64_t *__restrict__ masks,
-    int32_t *__restrict__ cnt, int n_chunk, int n_mask, const uint32_t *__restrict__ wu,
-    const uint32_t *__restrict__ wg, uint32_t *__restrict__ wsl, Slices sl)
+    int32_t *__restrict__ cnt, int n_chunk, int n_mask, int n_copy,
+    const uint32_t *__restrict__ wu, const uint32_t *__restrict__ wg, uint32_t *__restrict__ wsl,
+    Slices sl, BkXpose xp, const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
+    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
+    int dm)
 {
-    __shared__ unsigned long long m[CH];
-    __shared__ int rn[BR];
-    const int b = blockIdx.x;
-    if (b >= n_mask) {
-        copy_slices_rows<2, NT>(b - n_mask, wu, wg, wsl, dff, sl);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MASK_LDS > XPOSE_LDS ? MASK_LDS : XPOSE_LDS];
+    int b = blockIdx.x;
+    if (b < n_mask) {
+        ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk,
+                       b % n_chunk, (unsigned long long *)lds, (int *)(lds + CH * 8));
         return;
     }
-    ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk, b % n_chunk,
-                   m, rn);
+    b -= n_mask;
+    if (b < n_copy) {
+        copy_slices_rows<2, NT>(b, wu, wg, wsl, dff, sl);
+        return;
+    }
+    bk_xpose_block<DT>(b - n_copy, xp, x, dy, (const uint8_t *)wu, (const uint8_t *)wg, ovf_rows,
+                       n_ovf_p, max_ovf, dm, dff, lds);
 }
 
 // ------------------------------------------------------------ 5'. dx, XCD-local
@@ -567,12 +580,14 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     if (T > 0) {
         const int n_chunk = (dff + CH - 1) / CH, n_mask = L.nblk * n_chunk;
         const int n_copy = L.split ? copy_groups(dff) : 0;
-        hipLaunchKernelGGL(mask_kernel, dim3(n_mask + n_copy), dim3(NT), 0, s, h->row_nnz,
-                           h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk, n_mask,
-                           (const uint32_t *)wu, (const uint32_t *)wg, wsl, sl);
+        const BkXpose xp = bk_xpose(DT, dm, dff, h->max_ovf, ws + L.backup);
+        hipLaunchKernelGGL((mask_kernel<DT>), dim3(n_mask + n_copy + xp.blocks), dim3(NT), 0, s,
+                           h->row_nnz, h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk,
+                           n_mask, n_copy, (const uint32_t *)wu, (const uint32_t *)wg, wsl, sl,
+                           xp, xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf, dm);
         tm.mark("mask_kernel");
     }
-    launch_bk_ud((twell_dtype)DT, x, dy, h, wu, wg, wd, dm, l1, ws + L.backup, tm, s);
+    launch_bk_ud((twell_dtype)DT, x, dy, h, wu, wd, dm, l1, ws + L.backup, tm, s);
     hipLaunchKernelGGL(blk_prefix_kernel, dim3((dff + 63) / 64), dim3(NT), 0, s, cnt, L.nblk, dff,
                        colptr);
     tm.mark("blk_prefix_kernel");
