@@ -28,11 +28,14 @@ def status_word():
 # ------------------------------------------------------------ gate + TwELL
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (33, 192, 640), (64, 4096, 256),
-                                      (65, 128, 384), (200, 256, 384), (333, 512, 1024)])
+                                      (65, 128, 384), (200, 256, 384), (333, 512, 1024),
+                                      (2000, 256, 16384)])
 def test_gate_pack_integer_exact(orc, dtype, T, dm, dff):
     """Integer inputs: every sum is exact, so count, col and val match bit for
     bit, including exact g == 0 ties (not stored). T <= 64 runs the few-token
-    kernel (T = 33: a second, one-token chunk), T > 64 the tiled one."""
+    kernel (T = 33: a second, one-token chunk), T > 64 the tiled one with
+    192-token tiles, and 2000 x 16384 (512 tiles of 256 x 256) the 256-token
+    tiles with a ragged last token tile."""
     if dtype == "f32" and dm > 2048:
         pytest.skip("fp32 limit is d_model <= 2048")
     announce("gate_pack int", dtype, T, dm, dff)
