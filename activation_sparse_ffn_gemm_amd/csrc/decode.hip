@@ -29,7 +29,7 @@
 //                                 then phase 3.
 #include <algorithm>
 
-#include "mfma_tile.hpp"
+#include "ntgemm.hpp"
 #include "rows.hpp"
 
 namespace {
@@ -155,7 +155,7 @@ DEVI void gate_steps(const uint8_t *const (&xrow)[NC], const uint8_t *const (&wr
                 for (int c = 0; c < NC; ++c)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        mt::mma_group<DT>(acc[c][q], a[i][c], b[i][q]);
+                        ng::mma_group<DT>(acc[c][q], a[i][c], b[i][q]);
     }
 }
 

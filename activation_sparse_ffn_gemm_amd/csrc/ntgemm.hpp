@@ -1,6 +1,7 @@
 // Tiled MFMA main loop for dense products C[m][n] = sum_k A[m][k] B[n][k]
 // whose operands are both K-contiguous (every operand row is a memory row
-// along K), shared by the dense products over the hybrid's backup rows.
+// along K), shared by the gate GEMM and the dense products over the hybrid's
+// backup rows.
 //
 // A workgroup of WGM x WGN wave64s computes a BM x BN tile; each wave owns a
 // WM x WN sub-tile as (WM/32) x (WN/32) blocks of 32x32 MFMA accumulators.
@@ -19,9 +20,26 @@
 // operand pairs summed) and over any sub-range of them (split K).
 #pragma once
 
-#include "mfma_tile.hpp"
+#include "common.hpp"
 
 namespace ng {
+
+// One MFMA step over a 16-byte fragment per lane of each operand (32x32
+// output block). bf16: one 32x32x16 MFMA; f32: element q of both fragments is
+// the same k, so four 32x32x2 MFMAs cover the chunk.
+template <int DT> DEVI void mma_group(floatx16_t &acc, const uint4 &a, const uint4 &b);
+template <> DEVI void mma_group<TWELL_BF16>(floatx16_t &acc, const uint4 &a, const uint4 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+template <> DEVI void mma_group<TWELL_F32>(floatx16_t &acc, const uint4 &a, const uint4 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
 
 constexpr int ROWB = 64; // bytes of one LDS row per K step
 constexpr int NST = 4;   // K steps resident in LDS
@@ -188,7 +206,7 @@ DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, 
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni)
-                    mt::mma_group<DT>(acc.v[mi][ni], fa[mi], fb[ni]);
+                    mma_group<DT>(acc.v[mi][ni], fa[mi], fb[ni]);
         }
     }
     __syncthreads(); // every wave is done reading the stages
