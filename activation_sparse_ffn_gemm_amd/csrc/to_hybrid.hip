@@ -68,8 +68,9 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
     }
 }
 
-constexpr int BLK = 64;   // rows per workgroup of the slot/dense launch
+constexpr int BLK = 16;   // rows per workgroup of the slot/dense launch (few backup rows each)
 constexpr int DNT = 256;  // its threads
+constexpr int ROW_LDS = 32768; // bytes of one dense row built in LDS (d_ff 16384 bf16 / 8192 f32)
 
 template <int DT>
 __global__ __launch_bounds__(DNT) void hyb_dense_kernel(
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(DNT) void hyb_dense_kernel(
     using S = typename elem<DT>::storage;
     __shared__ int rows[BLK];
     __shared__ int n_here, n_before;
+    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[ROW_LDS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r0 = blockIdx.x * BLK;
     if (tid == 0)
@@ -102,13 +104,13 @@ __global__ __launch_bounds__(DNT) void hyb_dense_kernel(
         atomicAdd(&n_before, mine);
     __syncthreads();
     const int before = n_before;
-    // this block's rows: wave 0 numbers them (64 rows = one ballot)
+    // this block's rows: wave 0 numbers them (one ballot over lanes < BLK)
     if (wv == 0) {
         const int t = r0 + lane;
-        const bool f = t < T && row_nnz[t] > K;
+        const bool f = lane < BLK && t < T && row_nnz[t] > K;
         const unsigned long long m = __ballot(f);
         const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
-        if (t < T) {
+        if (lane < BLK && t < T) {
             row_slot[t] = f ? slot : -1;
             if (f && slot < max_ovf)
                 ovf_rows[slot] = t;
@@ -125,15 +127,23 @@ __global__ __launch_bounds__(DNT) void hyb_dense_kernel(
         }
     }
     __syncthreads();
-    // dense rows of this block's overflow rows (within capacity)
+    // dense rows of this block's overflow rows (within capacity), each built
+    // in LDS (zeros, then the row's entries) and stored with 16-byte lanes;
+    // rows wider than the LDS buffer go straight to memory
+    const bool in_lds = (size_t)dff * sizeof(S) <= ROW_LDS;
     for (int k = 0; k < n_here; ++k) {
         const int slot = before + k;
         if (slot >= max_ovf)
             break;
         const int t = rows[k];
         S *drow = (S *)dense + (size_t)slot * dff;
-        for (int i = tid; i < dff; i += DNT)
-            drow[i] = S(0);
+        S *brow = in_lds ? (S *)rowbuf : drow;
+        if (in_lds)
+            for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
+                ((uint4 *)rowbuf)[i] = make_uint4(0, 0, 0, 0);
+        else
+            for (int i = tid; i < dff; i += DNT)
+                drow[i] = S(0);
         __syncthreads();
         // every slot of the row's TwELL tiles, 8 per thread at a time (loads
         // unconditional, stores of the stored slots only)
@@ -154,13 +164,18 @@ __global__ __launch_bounds__(DNT) void hyb_dense_kernel(
                 const int q = q0 + u * DNT + tid;
                 if (q < nslot && q % W < min(n[u], W)) {
                     if (c[u] >= 0 && c[u] < dff)
-                        drow[c[u]] = v[u];
+                        brow[c[u]] = v[u];
                     else
                         raise_status(status, TWELL_DEV_BAD_INDEX);
                 }
             }
         }
         __syncthreads();
+        if (in_lds) {
+            for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
+                ((uint4 *)drow)[i] = ((const uint4 *)rowbuf)[i];
+            __syncthreads();
+        }
     }
 }
 
