@@ -96,9 +96,77 @@ def parse():
                    help="weight of the L1 activation penalty in the backward (training recipe)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--no-dense", action="store_true", help="skip the dense torch leg")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the few-token (2B decode) leg")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
     return p.parse_args()
+
+
+def graph_us(torch, fn, calls=10, replays=20):
+    """Mean microseconds of fn() captured in a HIP graph (calls per graph) and
+    replayed: launch gaps on the GPU are included, host overhead is not."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * calls)
+
+
+def decode_leg(torch, tw, synth, dev):
+    """The 2B-scale decode configuration (d_model 2304, d_ff 6144, 1%, W = 32)
+    at T = 1, 8, 32, 64 tokens: twell_decode_fwd (the whole layer) against the
+    dense bf16 layer, both graph-timed, and the weight bytes actually touched
+    (W_g whole, plus one wu_t and one wd row per distinct active neuron)."""
+    rows = []
+    for T in (1, 8, 32, 64):
+        w = synth.DECODE_2B.with_(T=T)
+        d = synth.make_inputs(w)
+        x, wg, wu, wd = (d[k].to(dev) for k in ("x", "wg_t", "wu_t", "wd"))
+        out = tw.empty_twell(T, w.d_ff, w.width, torch.bfloat16, dev)
+        y = torch.empty((T, w.d_model), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, tw.decode_workspace_bytes(tw.TWELL_BF16, T, w.d_model, w.d_ff,
+                                                            w.width)),
+                         dtype=torch.uint8, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        sparse = lambda: tw.decode_fwd(x, wg, wu, wd, width=w.width, out=out, y=y, workspace=ws,
+                                       status=st)
+        sp_us = graph_us(torch, sparse)
+        if int(st.item()) != 0:
+            raise SystemExit(f"decode T={T}: device status {int(st.item())}")
+        gu_t = torch.cat([wg, wu], 0).t().contiguous()
+        wd_c = wd.contiguous()
+        dff = w.d_ff
+
+        def dense():
+            gu = x @ gu_t
+            return (torch.relu(gu[:, :dff]) * gu[:, dff:]) @ wd_c
+        de_us = graph_us(torch, dense)
+        keep = torch.arange(w.width, device=dev)[None, None, :] < out.count.clamp(max=w.width)[:, :, None]
+        distinct = int(torch.unique(out.col[keep].long()).numel())
+        touched = dff * w.d_model * 2 + distinct * 2 * w.d_model * 2
+        rows.append({"T": T, "sparse_us": round(sp_us, 2), "dense_us": round(de_us, 2),
+                     "speedup": round(de_us / sp_us, 3), "weight_bytes_touched": touched,
+                     "touched_GBps": round(touched / (sp_us * 1e-6) / 1e9, 1),
+                     "nnz": int(out.count.clamp(max=w.width).sum())})
+    return {"workload": "2b-decode", "d_model": 2304, "d_ff": 6144, "density": 0.01,
+            "width": 32, "call": "twell_decode_fwd (gate partials, pack + up, down: 3 launches)",
+            "timing": "HIP graph of 10 calls, replayed 20 times", "by_T": rows}
 
 
 def main():
@@ -351,6 +419,8 @@ def main():
                  "saved_activation_bytes": int(dense_saved), "step_peak_bytes": int(dense_peak)}
         del p_gu, p_d, xr
 
+    decode = None if a.no_decode else decode_leg(torch, tw, synth, dev)
+
     # ---- CPU oracle on this host (bounded sample of the same workload)
     cpu = None
     if not a.no_cpu:
@@ -399,6 +469,7 @@ def main():
         "kernels": per_kernel,
         "dense_bf16": dense,
         "memory": memory,
+        "decode": decode,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
