@@ -32,7 +32,15 @@ constexpr int GM = 8; // token tiles per group of the tile order
 // (row, TwELL tile) pair from LDS: count = popcounts of its four masks,
 // entries = the set bits in ascending column order. Per lane this costs a
 // few dozen instructions instead of a pass over every accumulator row.
-template <class C> constexpr int vals_bytes() { return C::BN * C::BM * 2; }
+//
+// A column holds VS = BM + 4 values: the 32 lanes of a half-wave store 8 bytes
+// each at 32 consecutive columns, and a column stride of VS / 2 = 2 x odd
+// dwords sends them to 32 disjoint bank pairs (a stride of BM, a multiple of
+// 64 dwords, would put all 32 on one bank).
+template <class C> constexpr int vals_stride() { return C::BM + 4; }
+static_assert(((C192::BM + 4) / 2) % 2 == 0 && ((C192::BM + 4) / 4) % 2 == 1, "odd stride");
+static_assert(((C256::BM + 4) / 2) % 2 == 0 && ((C256::BM + 4) / 4) % 2 == 1, "odd stride");
+template <class C> constexpr int vals_bytes() { return C::BN * vals_stride<C>() * 2; }
 template <class C> constexpr int pack_lds() { return vals_bytes<C>() + C::BM * (C::BN / 32) * 4; }
 template <class C> constexpr int kernel_lds()
 {
@@ -46,9 +54,9 @@ DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, 
                     int32_t *__restrict__ status)
 {
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-    constexpr int BM = C::BM, BN = C::BN, NBK = BN / 32;
+    constexpr int BM = C::BM, BN = C::BN, NBK = BN / 32, VS = vals_stride<C>();
     const int half = lane >> 5, l32 = lane & 31;
-    uint16_t *vals = (uint16_t *)lds;                       // [BN][BM]
+    uint16_t *vals = (uint16_t *)lds;                       // [BN][VS]
     uint32_t *masks = (uint32_t *)(lds + vals_bytes<C>()); // [BM][NBK]
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
@@ -60,7 +68,7 @@ DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, 
                 const int r = wm * C::WM + mi * 32 + 8 * eg + 4 * half;
                 const bf16x2v p0 = {(__bf16)acc.v[mi][ni][4 * eg], (__bf16)acc.v[mi][ni][4 * eg + 1]};
                 const bf16x2v p1 = {(__bf16)acc.v[mi][ni][4 * eg + 2], (__bf16)acc.v[mi][ni][4 * eg + 3]};
-                *(uint2 *)(vals + (size_t)c * BM + r) =
+                *(uint2 *)(vals + (size_t)c * VS + r) =
                     make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
             }
         }
@@ -98,7 +106,7 @@ DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, 
                 const int c = tl * TWELL_TILE_C + k * 32 + __ffs(m) - 1;
                 m &= m - 1;
                 col[tj * W + p] = (int16_t)(n0 + c);
-                val[tj * W + p] = vals[(size_t)c * BM + r];
+                val[tj * W + p] = vals[(size_t)c * VS + r];
                 ++p;
             }
         }
