@@ -10,8 +10,8 @@
 // neurons give 242 workgroups, one round on 256 CUs); BM = 256 once there are
 // enough tiles for several rounds (fewer operand bytes per flop).
 //
-// The K loop is the shared LDS-DMA main loop (ntgemm.hpp): 64-byte K steps,
-// four resident, loads straight from global memory to LDS, per-wave vmcnt
+// The K loop is the shared LDS-DMA main loop (ntgemm.hpp): 128-byte K steps,
+// two resident, loads straight from global memory to LDS, per-wave vmcnt
 // waits, XOR-swizzled LDS rows.
 //
 // Epilogue, per row: one ballot per 32-column block gives the g > 0 mask;
@@ -22,8 +22,9 @@
 
 namespace {
 
-using C192 = ng::Cfg<192, 256, 2, 4>; // waves of 96 x 64 (3 x 2 blocks)
-using C256 = ng::Cfg<256, 256, 2, 4>; // waves of 128 x 64 (4 x 2 blocks)
+// 128-byte K steps, two resident: one barrier per four MFMA groups
+using C192 = ng::Cfg<192, 256, 2, 4, 2, 128>; // waves of 96 x 64 (3 x 2 blocks)
+using C256 = ng::Cfg<256, 256, 2, 4, 2, 128>; // waves of 128 x 64 (4 x 2 blocks)
 constexpr int GM = 8; // token tiles per group of the tile order
 
 // bf16 epilogue. The K loop's LDS is free again: the tile's values go there
@@ -231,9 +232,9 @@ __global__ __launch_bounds__(C::NT, 1) void gate_pack_kernel(
     // are not stored
     auto rowa = [&](int rr) { return x + (size_t)min(m0 + rr, T - 1) * rowbytes; };
     auto rowb = [&](int rr) { return wg + (size_t)min(n0 + rr, dff - 1) * rowbytes; };
-    auto off = [](int kt) { return ng::StepOff{(size_t)kt * ng::ROWB, (size_t)kt * ng::ROWB}; };
+    auto off = [](int kt) { return ng::StepOff{(size_t)kt * C::ROWB, (size_t)kt * C::ROWB}; };
     ng::Acc<C> acc;
-    ng::mainloop<C, DT>(L, rowa, rowb, off, 0, (int)(rowbytes / ng::ROWB), acc);
+    ng::mainloop<C, DT>(L, rowa, rowb, off, 0, (int)(rowbytes / C::ROWB), acc);
     // ---- epilogue. Accumulator element e of lane l in a 32x32 block holds
     // row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that block.
     if constexpr (DT == TWELL_BF16)

@@ -5,14 +5,15 @@
 //
 // A workgroup of WGM x WGN wave64s computes a BM x BN tile; each wave owns a
 // WM x WN sub-tile as (WM/32) x (WN/32) blocks of 32x32 MFMA accumulators.
-// Operands stream through LDS in K steps of 64 bytes per row (32 bf16 /
-// 16 f32), NST steps resident at once: the loads of step k + NST - 1 are
-// issued while step k is computed. Loads go straight from global memory to
-// LDS, 16 bytes per lane (one wave instruction fills 16 rows x 64 bytes), so
-// no registers are spent on staging; each wave waits only for its own loads
-// of the step it is about to use, then a barrier covers the others'. LDS rows
-// are XOR-swizzled in 16-byte chunks so that the 16 lanes a 128-bit fragment
-// read serves per cycle hit 16 distinct groups of the 64 banks.
+// Operands stream through LDS in K steps of ROWB = 64 or 128 bytes per row
+// (32 or 64 bf16), NST steps resident at once: the loads of step k + NST - 1
+// are issued while step k is computed. Loads go straight from global memory
+// to LDS, 16 bytes per lane (one wave instruction fills 1 KB: 16 rows of 64
+// bytes or 8 of 128), so no registers are spent on staging; each wave waits
+// only for its own loads of the step it is about to use, then a barrier
+// covers the others'. LDS rows are XOR-swizzled in 16-byte chunks so that the
+// 16 lanes a 128-bit fragment read serves per cycle hit 16 distinct groups of
+// the 64 banks.
 //
 // Rows are given per tile row by the caller (a gather of any rows is fine);
 // K steps map to byte offsets through a caller function, so a product may
@@ -41,21 +42,27 @@ template <> DEVI void mma_group<TWELL_F32>(floatx16_t &acc, const uint4 &a, cons
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-constexpr int ROWB = 64; // bytes of one LDS row per K step
-constexpr int NST = 4;   // K steps resident in LDS
-constexpr int BLK = 1024; // bytes one wave's 16-byte-lane load writes: 16 rows
+constexpr int ROWB = 64; // default bytes of one LDS row per K step
+constexpr int BLK = 1024; // bytes one wave's 16-byte-lane load writes
 
-template <int BM_, int BN_, int WGM_, int WGN_> struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+// NST: K steps resident in LDS (NST - 1 steps of loads in flight).
+// ROWB_: bytes of K per step and operand row (64 or 128): a step runs
+// ROWB_ / 32 MFMA groups between two barriers.
+template <int BM_, int BN_, int WGM_, int WGN_, int NST_ = 4, int ROWB_ = ROWB> struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NST = NST_, ROWB = ROWB_;
     static constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
     static constexpr int NT = 64 * WGM * WGN, NWV = WGM * WGN;
+    // 16-byte chunks per row, rows per 1 KB load block, rows per 256-byte
+    // LDS bank line, MFMA groups per step
+    static constexpr int CPR = ROWB / 16, RPB = BLK / ROWB, SW = 256 / ROWB, NG = ROWB / 32;
     static constexpr int STAGE = (BM + BN) * ROWB, NBLK = STAGE / BLK;
+    static_assert(ROWB == 64 || ROWB == 128, "64- or 128-byte K steps");
     // blocks per wave: the first N_HI waves take WB_HI, the others WB_HI - 1
     static constexpr int WB_HI = (NBLK + NWV - 1) / NWV, N_HI = NBLK - (WB_HI - 1) * NWV;
     static constexpr int LDS = NST * STAGE;
     static_assert(BM % 32 == 0 && BN % 32 == 0 && WM % 32 == 0 && WN % 32 == 0, "32x32 blocks");
-    static_assert(STAGE % BLK == 0 && BM % 16 == 0, "a block must not straddle the operands");
-    static_assert(2 * WB_HI < 64, "loads in flight must fit the vmcnt counter");
+    static_assert(STAGE % BLK == 0 && BM % RPB == 0, "a block must not straddle the operands");
+    static_assert(NST >= 2 && (NST - 2) * WB_HI < 64, "loads in flight must fit the vmcnt counter");
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -78,10 +85,15 @@ DEVI void lds_dma16(const uint8_t *g, uint32_t lds)
 }
 #pragma clang diagnostic pop
 
-// Byte offset of 16-byte chunk c (0..3) of LDS row r (64-byte rows). Rows
-// r, r+4, r+8, r+12 start on the same bank; XOR-ing the chunk with (r / 4) % 4
-// separates them, so 16 consecutive rows at one chunk use 16 distinct groups.
-DEVI int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+// Byte offset of 16-byte chunk c of LDS row r. With 64-byte rows, rows r,
+// r+4, r+8, r+12 start on the same bank and XOR-ing the chunk with (r / 4) % 4
+// separates them; with 128-byte rows the same holds for r, r+2, ..., r+14 and
+// (r / 2) % 8. Either way 16 consecutive rows at one chunk use 16 distinct
+// 4-bank groups.
+template <class C> DEVI int swz(int r, int c)
+{
+    return r * C::ROWB + ((c ^ ((r / C::SW) % C::CPR)) << 4);
+}
 
 // Wait until at most n of this wave's vector-memory operations are pending
 // (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt
@@ -90,6 +102,19 @@ template <int n> DEVI void wait_vm()
 {
     static_assert(n >= 0 && n < 64, "vmcnt is six bits");
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait_vm<later * per>() for a run-time later in [0, L] (per, L compile-time)
+template <int per, int L> DEVI void wait_vm_steps(int later)
+{
+    if constexpr (L <= 0) {
+        wait_vm<0>();
+    } else {
+        if (later >= L)
+            wait_vm<L * per>();
+        else
+            wait_vm_steps<per, L - 1>(later);
+    }
 }
 
 // Byte offsets of one K step in the A rows and in the B rows.
@@ -144,9 +169,9 @@ DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, 
     if (nk <= 0)
         return;
     // This wave's 1 KB blocks of a stage: block b holds tile rows
-    // 16b .. 16b+15 (A rows, then B rows). Lane l writes bytes 16l .. 16l+15
-    // of it, i.e. swizzled chunk l&3 of row 16b + l/4, so it loads the source
-    // chunk the swizzle maps there.
+    // RPB b .. RPB b + RPB - 1 (A rows, then B rows). Lane l writes bytes
+    // 16l .. 16l+15 of it, i.e. swizzled chunk l % CPR of row RPB b + l / CPR,
+    // so it loads the source chunk the swizzle maps there.
     const int nb = wave < C::N_HI ? C::WB_HI : C::WB_HI - 1;
     const int b0 = wave < C::N_HI ? wave * C::WB_HI
                                   : C::N_HI * C::WB_HI + (wave - C::N_HI) * (C::WB_HI - 1);
@@ -155,11 +180,12 @@ DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, 
 #pragma unroll
     for (int i = 0; i < C::WB_HI; ++i) {
         const int b = min(b0 + i, C::NBLK - 1);
-        const int r = 16 * b + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
-        isa[i] = 16 * b < C::BM; // uniform: a block is all A or all B rows
+        const int r = C::RPB * b + lane / C::CPR;
+        const int c = (lane % C::CPR) ^ ((r / C::SW) % C::CPR);
+        isa[i] = C::RPB * b < C::BM; // uniform: a block is all A or all B rows
         src[i] = (isa[i] ? rowa(r) : rowb(r - C::BM)) + c * 16;
     }
+    constexpr int NST = C::NST;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8 *)L + b0 * BLK;
     auto issue = [&](int kt) {
         const uint32_t dst = lds0 + ((kt - kt0) % NST) * C::STAGE;
@@ -176,32 +202,23 @@ DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, 
     for (int k = 0; k < nk; ++k) {
         // this wave's loads of step k are done once at most the later steps' pend
         const int later = min(nk - 1, k + NST - 2) - k;
-        if (later >= 2) {
-            if (nb == C::WB_HI)
-                wait_vm<2 * C::WB_HI>();
-            else
-                wait_vm<2 * (C::WB_HI - 1)>();
-        } else if (later == 1) {
-            if (nb == C::WB_HI)
-                wait_vm<C::WB_HI>();
-            else
-                wait_vm<C::WB_HI - 1>();
-        } else {
-            wait_vm<0>();
-        }
+        if (nb == C::WB_HI)
+            wait_vm_steps<C::WB_HI, NST - 2>(later);
+        else
+            wait_vm_steps<C::WB_HI - 1, NST - 2>(later);
         __syncthreads(); // all loads of step k are in; step k - 1 is consumed
         if (k + NST - 1 < nk)
             issue(kt0 + k + NST - 1);
-        const uint8_t *As = L + (k % NST) * C::STAGE, *Bs = As + C::BM * ROWB;
+        const uint8_t *As = L + (k % NST) * C::STAGE, *Bs = As + C::BM * C::ROWB;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < C::NG; ++g) {
             uint4 fa[C::MI], fb[C::NI];
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
-                fa[mi] = *(const uint4 *)(As + swz(wm * C::WM + mi * 32 + l32, 2 * g + half));
+                fa[mi] = *(const uint4 *)(As + swz<C>(wm * C::WM + mi * 32 + l32, 2 * g + half));
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                fb[ni] = *(const uint4 *)(Bs + swz(wn * C::WN + ni * 32 + l32, 2 * g + half));
+                fb[ni] = *(const uint4 *)(Bs + swz<C>(wn * C::WN + ni * 32 + l32, 2 * g + half));
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
