@@ -48,18 +48,37 @@ KERNEL_SOURCES = {
     "hyb_dense_kernel": "to_hybrid.hip", "hfwd_ell_kernel": "hyb_fwd.hip",
     "hfwd_up_kernel": "ffn_fwd.hip", "hfwd_down_kernel": "ffn_fwd.hip",
     "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "bk_ud_kernel": "backup.hip",
-    "bk_dx_kernel": "backup.hip", "bk_dw_kernel": "backup.hip",
+    "bk_dxdw_kernel": "backup.hip", "dec_gate_part_kernel": "decode.hip",
+    "dec_pack_kernel": "decode.hip", "dec_up_kernel": "decode.hip",
+    "dec_down_kernel": "decode.hip",
 }
 
 
+def source_closure(name):
+    """The source file and every local header it includes, transitively
+    (quoted includes, looked up in csrc/ then include/), sorted."""
+    import re
+    dirs = (CSRC, os.path.join(ROOT, "include"))
+    seen, todo = set(), [name]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        path = next(os.path.join(d, f) for d in dirs if os.path.exists(os.path.join(d, f)))
+        with open(path) as fh:
+            todo += re.findall(r'^\s*#\s*include\s+"([^"]+)"', fh.read(), re.M)
+    return sorted(seen)
+
+
 def kernel_sources_sha256(kernel):
-    """sha256 over the kernel's .hip file and every shared header."""
+    """sha256 over the kernel's .hip file and the headers it includes."""
     import hashlib
     h = hashlib.sha256()
-    names = [KERNEL_SOURCES.get(kernel, "bwd.hip")]
-    names += sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
-    for f in names:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+    dirs = (CSRC, os.path.join(ROOT, "include"))
+    for f in source_closure(KERNEL_SOURCES.get(kernel, "bwd.hip")):
+        path = next(os.path.join(d, f) for d in dirs if os.path.exists(os.path.join(d, f)))
+        with open(path, "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
