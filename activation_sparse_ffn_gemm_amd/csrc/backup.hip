@@ -35,7 +35,13 @@
 
 namespace {
 
-using C1 = ng::Cfg<128, 128, 2, 2>; // 4 waves, 64 x 64 each
+// Tiles of 128 x 128, four waves of 64 x 64. The u/da products (one
+// workgroup per CU, short K = d_model) keep 64-byte K steps, four resident;
+// the split-K row x weight products and the dW products take 128-byte steps,
+// two resident (one barrier per four MFMA groups).
+using CU = ng::Cfg<128, 128, 2, 2>;
+using CW = ng::Cfg<128, 128, 2, 2, 2, 128>;
+static_assert(CU::NT == CW::NT && CU::LDS == CW::LDS, "the kernels size LDS and blocks once");
 constexpr int TILE = 128;
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -90,44 +96,44 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     if (m0 >= n)
         return;
     const size_t rowbytes = (size_t)dm * esz;
-    const int nk = (int)(rowbytes / ng::ROWB);
-    auto off = [](int kt) { return ng::StepOff{(size_t)kt * ng::ROWB, (size_t)kt * ng::ROWB}; };
+    const int nk = (int)(rowbytes / CU::ROWB);
+    auto off = [](int kt) { return ng::StepOff{(size_t)kt * CU::ROWB, (size_t)kt * CU::ROWB}; };
     auto rows_of = [&](const uint8_t *src) {
         return [=](int r) { return src + (size_t)ovf_rows[min(m0 + r, n - 1)] * rowbytes; };
     };
     auto wrows_of = [&](const uint8_t *w) {
         return [=](int r) { return w + (size_t)(i0 + r) * rowbytes; };
     };
-    ng::Acc<C1> au;
-    ng::mainloop<C1, DT>(L, rows_of(x), wrows_of(wu), off, 0, nk, au);
-    ng::Acc<C1> ad;
+    ng::Acc<CU> au;
+    ng::mainloop<CU, DT>(L, rows_of(x), wrows_of(wu), off, 0, nk, au);
+    ng::Acc<CU> ad;
     if constexpr (BWD)
-        ng::mainloop<C1, DT>(L, rows_of(dy), wrows_of(wd), off, 0, nk, ad);
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<C1>(), wn = ng::wave_n<C1>();
+        ng::mainloop<CU, DT>(L, rows_of(dy), wrows_of(wd), off, 0, nk, ad);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<CU>(), wn = ng::wave_n<CU>();
     const size_t plane = (size_t)R * dff; // elements per intermediate array
     // every h of this lane's elements first: the loads all go out before any
     // store, instead of one load-wait-store chain per element
-    float hv[C1::MI][C1::NI][16];
+    float hv[CU::MI][CU::NI][16];
 #pragma unroll
-    for (int mi = 0; mi < C1::MI; ++mi)
+    for (int mi = 0; mi < CU::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < C1::NI; ++ni)
+        for (int ni = 0; ni < CU::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int m = m0 + ng::acc_row<C1>(wm, mi, e, lane);
-                const int i = i0 + ng::acc_col<C1>(wn, ni, lane);
+                const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
+                const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
                 hv[mi][ni][e] = m < n ? E::load1(dense, (size_t)m * dff + i) : 0.f;
             }
     // a, du, dg of this lane's elements: u's accumulators become a, da's du
-    float dgv[C1::MI][C1::NI][16];
+    float dgv[CU::MI][CU::NI][16];
 #pragma unroll
-    for (int mi = 0; mi < C1::MI; ++mi)
+    for (int mi = 0; mi < CU::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < C1::NI; ++ni)
+        for (int ni = 0; ni < CU::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int m = m0 + ng::acc_row<C1>(wm, mi, e, lane);
-                const int i = i0 + ng::acc_col<C1>(wn, ni, lane);
+                const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
+                const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
                 const size_t o = (size_t)m * dff + i;
                 const float h = hv[mi][ni][e], u = au.v[mi][ni][e];
                 au.v[mi][ni][e] = h * u;
@@ -149,13 +155,13 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
         for (int q = 0; q < 3 * NH; ++q) { // (a, du, dg) x (hi, lo)
             const int which = q / NH, part = q % NH;
 #pragma unroll
-            for (int mi = 0; mi < C1::MI; ++mi)
+            for (int mi = 0; mi < CU::MI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < C1::NI; ++ni)
+                for (int ni = 0; ni < CU::NI; ++ni)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
-                        const int r = ng::acc_row<C1>(wm, mi, 4 * g, lane);
-                        const int c = ng::acc_col<C1>(wn, ni, lane);
+                        const int r = ng::acc_row<CU>(wm, mi, 4 * g, lane);
+                        const int c = ng::acc_col<CU>(wn, ni, lane);
                         uint8_t *dst = L + c * P + r * esz;
                         float v[4];
 #pragma unroll
@@ -180,7 +186,7 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
             __syncthreads();
             uint8_t *tbase = (uint8_t *)inter_t + (size_t)q * plane * esz;
             constexpr int CPR = TILE * esz / 16; // 16-byte chunks per row
-            for (int t = threadIdx.x; t < TILE * CPR; t += C1::NT) {
+            for (int t = threadIdx.x; t < TILE * CPR; t += CU::NT) {
                 const int c = t / CPR, ch = t % CPR;
                 *(uint4 *)(tbase + ((size_t)(i0 + c) * R + m0) * esz + ch * 16) =
                     *(const uint4 *)(L + c * P + ch * 16);
@@ -206,27 +212,27 @@ DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ 
         return;
     const size_t rowbytes = (size_t)dff * esz, plane = (size_t)R * dff * esz,
                  wplane = (size_t)dm * dff * esz;
-    const int spseg = (int)(rowbytes / ng::ROWB), nk = NSEG * spseg;
+    const int spseg = (int)(rowbytes / CW::ROWB), nk = NSEG * spseg;
     const int kt0 = (int)((long)nk * sp / S), kt1 = (int)((long)nk * (sp + 1) / S);
     auto off = [&](int kt) {
         const int q = kt / spseg, kk = kt % spseg;
-        return ng::StepOff{q * plane + (size_t)kk * ng::ROWB,
-                           (q >> BSHIFT) * wplane + (size_t)kk * ng::ROWB};
+        return ng::StepOff{q * plane + (size_t)kk * CW::ROWB,
+                           (q >> BSHIFT) * wplane + (size_t)kk * CW::ROWB};
     };
     auto rowa = [&](int r) { return a + (size_t)(m0 + r) * rowbytes; };
     auto rowb = [&](int r) { return wt + (size_t)min(d0 + r, dm - 1) * rowbytes; };
-    ng::Acc<C1> acc;
-    ng::mainloop<C1, DT>(L, rowa, rowb, off, kt0, kt1, acc);
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<C1>(), wn = ng::wave_n<C1>();
+    ng::Acc<CW> acc;
+    ng::mainloop<CW, DT>(L, rowa, rowb, off, kt0, kt1, acc);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
     float *p = part + (size_t)sp * R * dm;
 #pragma unroll
-    for (int mi = 0; mi < C1::MI; ++mi)
+    for (int mi = 0; mi < CW::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < C1::NI; ++ni)
+        for (int ni = 0; ni < CW::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int m = m0 + ng::acc_row<C1>(wm, mi, e, lane);
-                const int d = d0 + ng::acc_col<C1>(wn, ni, lane);
+                const int m = m0 + ng::acc_row<CW>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
                 if (m < n && d < dm)
                     p[(size_t)m * dm + d] = acc.v[mi][ni][e];
             }
@@ -242,7 +248,7 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    constexpr int KE = ng::ROWB / esz; // rows per K step
+    constexpr int KE = CW::ROWB / esz; // rows per K step
     if (n <= 0)
         return;
     const int d0 = bx * TILE, i0 = by * TILE;
@@ -253,51 +259,51 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt
     const int spseg = (n + KE - 1) / KE, nk = NH * spseg;
     auto off = [&](int kt) {
         const int q = kt / spseg, kk = kt % spseg;
-        return ng::StepOff{q * plane + (size_t)kk * ng::ROWB, (size_t)kk * ng::ROWB};
+        return ng::StepOff{q * plane + (size_t)kk * CW::ROWB, (size_t)kk * CW::ROWB};
     };
     auto rowa = [&](int r) { return ta + (size_t)(i0 + r) * rowbytes; };
     auto rowb = [&](int r) { return tx + (size_t)min(d0 + r, dm - 1) * rowbytes; };
-    ng::Acc<C1> acc;
-    ng::mainloop<C1, DT>(L, rowa, rowb, off, 0, nk, acc);
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<C1>(), wn = ng::wave_n<C1>();
+    ng::Acc<CW> acc;
+    ng::mainloop<CW, DT>(L, rowa, rowb, off, 0, nk, acc);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
     // all of this lane's current dW values first (loads in flight together),
     // then the sums
-    float cur[C1::MI][C1::NI][16];
+    float cur[CW::MI][CW::NI][16];
 #pragma unroll
-    for (int mi = 0; mi < C1::MI; ++mi)
+    for (int mi = 0; mi < CW::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < C1::NI; ++ni)
+        for (int ni = 0; ni < CW::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int i = i0 + ng::acc_row<C1>(wm, mi, e, lane);
-                const int d = d0 + ng::acc_col<C1>(wn, ni, lane);
+                const int i = i0 + ng::acc_row<CW>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
                 cur[mi][ni][e] = d < dm ? out[(size_t)i * dm + d] : 0.f;
             }
 #pragma unroll
-    for (int mi = 0; mi < C1::MI; ++mi)
+    for (int mi = 0; mi < CW::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < C1::NI; ++ni)
+        for (int ni = 0; ni < CW::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int i = i0 + ng::acc_row<C1>(wm, mi, e, lane);
-                const int d = d0 + ng::acc_col<C1>(wn, ni, lane);
+                const int i = i0 + ng::acc_row<CW>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
                 if (d < dm)
                     out[(size_t)i * dm + d] = cur[mi][ni][e] + acc.v[mi][ni][e];
             }
 }
 
 // ---------------------------------------------------------------- kernels
-constexpr int UD_LDS = C1::LDS > TILE * (4 * TILE + 16) ? C1::LDS : TILE * (4 * TILE + 16);
+constexpr int UD_LDS = CW::LDS > TILE * (4 * TILE + 16) ? CW::LDS : TILE * (4 * TILE + 16);
 
 // forward: the A tiles, then (other workgroups) the W_d transpose
 template <int DT>
-__global__ __launch_bounds__(C1::NT, 2) void bk_a_kernel(
+__global__ __launch_bounds__(CW::NT, 2) void bk_a_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ ovf_rows,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
     const uint8_t *__restrict__ wd, int dm, int dff, int R, const void *__restrict__ dense,
     void *__restrict__ inter, void *__restrict__ wdt, int n_a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t L[C1::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(C1::NT, 2) void bk_a_kernel(
 
 // backward: the u/da tiles (the transposes run beside the ELL masks)
 template <int DT>
-__global__ __launch_bounds__(C1::NT, 1) void bk_ud_kernel(
+__global__ __launch_bounds__(CW::NT, 1) void bk_ud_kernel(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff, int R,
@@ -327,19 +333,19 @@ __global__ __launch_bounds__(C1::NT, 1) void bk_ud_kernel(
 }
 
 template <int DT, int NH>
-__global__ __launch_bounds__(C1::NT, 2) void bk_y_kernel(
+__global__ __launch_bounds__(CW::NT, 2) void bk_y_kernel(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ wdt,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
     float *__restrict__ part)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t L[C1::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
     rowsw_tile<DT, NH, 4>(a, wdt, n_rows(n_ovf_p, max_ovf), dm, dff, R, S, part, blockIdx.x,
                           blockIdx.y, blockIdx.z, L);
 }
 
 // backward: the dx_O tiles (K split), then the dW tiles
 template <int DT>
-__global__ __launch_bounds__(C1::NT, 2) void bk_dxdw_kernel(
+__global__ __launch_bounds__(CW::NT, 2) void bk_dxdw_kernel(
     const uint8_t *__restrict__ inter, const uint8_t *__restrict__ wt,
     const uint8_t *__restrict__ inter_t, const uint8_t *__restrict__ xt,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(C1::NT, 2) void bk_dxdw_kernel(
     float *__restrict__ dwg, int n_dx)
 {
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    __shared__ __attribute__((aligned(16))) uint8_t L[C1::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
@@ -387,7 +393,7 @@ BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
     const size_t esz = dt == TWELL_BF16 ? 2 : 4, nh = dt == TWELL_BF16 ? 2 : 1;
     L.R = pad_rows(max_ovf);
     const int nseg = (int)(bwd ? 2 * nh : nh);
-    L.S = split_k(L.R, dm, nseg * (int)(dff * esz / ng::ROWB));
+    L.S = split_k(L.R, dm, nseg * (int)(dff * esz / CW::ROWB));
     size_t o = 0;
     L.inter = o;   o += up256((bwd ? 2 : 1) * nh * L.R * dff * esz);
     L.inter_t = o; o += bwd ? up256(3 * nh * L.R * dff * esz) : 0;
@@ -405,14 +411,14 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, false);
     const int n_a = (dff / TILE) * (L.R / TILE);
-    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a + (dm / TT) * (dff / TT)), dim3(C1::NT), 0, s,
+    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a + (dm / TT) * (dff / TT)), dim3(CW::NT), 0, s,
                        (const uint8_t *)x, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
                        (const uint8_t *)wd, dm, dff, L.R, h->dense, (void *)(ws + L.inter),
                        (void *)(ws + L.wt), n_a);
     tm.mark("bk_a_kernel");
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
     hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + TILE - 1) / TILE, L.R / TILE, L.S),
-                       dim3(C1::NT), 0, s, (const uint8_t *)(ws + L.inter),
+                       dim3(CW::NT), 0, s, (const uint8_t *)(ws + L.inter),
                        (const uint8_t *)(ws + L.wt), h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
                        (float *)(ws + L.part));
     tm.mark("bk_y_kernel");
@@ -425,7 +431,7 @@ void bk_ud_dt(const void *x, const void *dy, const hybrid_t *h, const void *wu, 
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
     const int n_ud = (dff / TILE) * (L.R / TILE);
-    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud), dim3(C1::NT), 0, s, (const uint8_t *)x,
+    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud), dim3(CW::NT), 0, s, (const uint8_t *)x,
                        (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
                        (const uint8_t *)wu, (const uint8_t *)wd, dm, dff, L.R, h->dense, l1,
                        (void *)(ws + L.inter), (void *)(ws + L.inter_t));
@@ -440,7 +446,7 @@ void bk_dxdw_dt(const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu, fl
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
     const int nd = (dm + TILE - 1) / TILE;
     const int n_dx = nd * (L.R / TILE) * L.S, n_dw = nd * (dff / TILE) * 3;
-    hipLaunchKernelGGL((bk_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(C1::NT), 0, s,
+    hipLaunchKernelGGL((bk_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(CW::NT), 0, s,
                        (const uint8_t *)(ws + L.inter), (const uint8_t *)(ws + L.wt),
                        (const uint8_t *)(ws + L.inter_t), (const uint8_t *)(ws + L.xt), h->n_ovf,
                        h->max_ovf, dm, dff, L.R, L.S, (float *)(ws + L.part), dwd, dwu, dwg,
