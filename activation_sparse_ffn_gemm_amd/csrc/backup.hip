@@ -64,6 +64,7 @@ int split_k(int R, int dm, int nk)
 // ---------------------------------------------------------------- products
 DEVI int n_rows(const int32_t *n_ovf_p, int max_ovf) { return min(*n_ovf_p, max_ovf); }
 
+
 // hi/lo (bf16) or plain (f32) store of an intermediate value
 template <int DT> DEVI void put2(void *base, size_t lo_off, size_t o, float v)
 {
@@ -77,10 +78,28 @@ template <int DT> DEVI void put2(void *base, size_t lo_off, size_t o, float v)
     }
 }
 
-// u (and da) of one tile of backup rows x neurons; the epilogue writes
-//   fwd (BWD = false): A = h u            -> a [R][dff] (hi, lo)
-//   bwd (BWD = true):  du, dg             -> [R][dff] (hi, lo each)
-//                      a, du, dg          -> [dff][R] (hi, lo each)
+// u (and da) of one tile of backup rows x neurons on eight waves in two
+// groups of four, each group on its own CU::LDS bytes of L:
+//   fwd (BWD = false): the groups sum the two halves of K of u; epilogue
+//                      A = h u -> a [R][dff] (hi, lo)
+//   bwd (BWD = true):  group 0 runs u = x_O W_u, group 1 da = dy_O W_d^T;
+//                      epilogue du, dg -> [R][dff] (hi, lo each) and
+//                      a, du, dg -> [dff][R] (hi, lo each)
+// Each wave's sub-tile has two 32-row block rows (mi = 0, 1): group g runs
+// the epilogue of block row g, so the groups swap the other block row's
+// accumulators through LDS first (in the forward u = first half + second
+// half, in that order). A workgroup of one group would leave one wave per
+// SIMD, too few to cover the MFMA and LDS latencies; these products have few
+// tiles, so the second group is not taken from other tiles.
+constexpr int UD_NT = 2 * CU::NT;
+static_assert(CU::MI == 2, "one block row per group");
+template <int DT> constexpr int ud_lds()
+{
+    constexpr int P = TILE * (int)sizeof(Store<DT>) + 16;
+    return 2 * CU::LDS > TILE * P ? 2 * CU::LDS : TILE * P;
+}
+static_assert(2 * CU::LDS >= 2 * CU::NWV * CU::NI * 16 * 64 * 4, "accumulator exchange");
+
 template <int DT, bool BWD>
 DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                   const int32_t *__restrict__ ovf_rows, int n, const uint8_t *__restrict__ wu,
@@ -91,102 +110,131 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1; // arrays per intermediate
+    constexpr int NI = CU::NI;
     constexpr int P = TILE * esz + 16;          // row pitch (bytes) of the transposed tile in LDS
     const int m0 = by * TILE, i0 = bx * TILE;
     if (m0 >= n)
         return;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wave / CU::NWV, wg = wave % CU::NWV;
+    const int wm = wg / CU::WGN, wn = wg % CU::WGN, lane = threadIdx.x & 63;
     const size_t rowbytes = (size_t)dm * esz;
-    const int nk = (int)(rowbytes / CU::ROWB);
+    const int nk = (int)(rowbytes / CU::ROWB); // even: d_model % 64 == 0
     auto off = [](int kt) { return ng::StepOff{(size_t)kt * CU::ROWB, (size_t)kt * CU::ROWB}; };
-    auto rows_of = [&](const uint8_t *src) {
-        return [=](int r) { return src + (size_t)ovf_rows[min(m0 + r, n - 1)] * rowbytes; };
+    const uint8_t *src = BWD && grp ? dy : x, *w = BWD && grp ? wd : wu;
+    auto rowa = [&](int r) { return src + (size_t)ovf_rows[min(m0 + r, n - 1)] * rowbytes; };
+    auto rowb = [&](int r) { return w + (size_t)(i0 + r) * rowbytes; };
+    const int kt0 = BWD ? 0 : grp * (nk / 2), kt1 = BWD ? nk : kt0 + nk / 2;
+    ng::Acc<CU> acc; // group 0: u (fwd: its first K half); group 1: da (fwd: u, second half)
+    ng::mainloop<CU, DT>(L + grp * CU::LDS, rowa, rowb, off, kt0, kt1, acc, grp * CU::NWV);
+    // swap: group g stores block row 1 - g of its accumulators in exchange
+    // area g, lane-major per (wave, block column, element group), then reads
+    // block row g of the other group's from area 1 - g
+    float4 *X = (float4 *)L;
+    auto xi = [&](int area, int ni, int eg) {
+        return (((area * CU::NWV + wg) * NI + ni) * 4 + eg) * 64 + lane;
     };
-    auto wrows_of = [&](const uint8_t *w) {
-        return [=](int r) { return w + (size_t)(i0 + r) * rowbytes; };
-    };
-    ng::Acc<CU> au;
-    ng::mainloop<CU, DT>(L, rows_of(x), wrows_of(wu), off, 0, nk, au);
-    ng::Acc<CU> ad;
-    if constexpr (BWD)
-        ng::mainloop<CU, DT>(L, rows_of(dy), wrows_of(wd), off, 0, nk, ad);
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<CU>(), wn = ng::wave_n<CU>();
+    float own[NI][16], oth[NI][16];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            own[ni][e] = grp ? acc.v[1][ni][e] : acc.v[0][ni][e];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int eg = 0; eg < 4; ++eg) {
+            const int mo = 1 - grp;
+            X[xi(grp, ni, eg)] =
+                make_float4(mo ? acc.v[1][ni][4 * eg] : acc.v[0][ni][4 * eg],
+                            mo ? acc.v[1][ni][4 * eg + 1] : acc.v[0][ni][4 * eg + 1],
+                            mo ? acc.v[1][ni][4 * eg + 2] : acc.v[0][ni][4 * eg + 2],
+                            mo ? acc.v[1][ni][4 * eg + 3] : acc.v[0][ni][4 * eg + 3]);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int eg = 0; eg < 4; ++eg) {
+            const float4 v = X[xi(1 - grp, ni, eg)];
+            oth[ni][4 * eg] = v.x;
+            oth[ni][4 * eg + 1] = v.y;
+            oth[ni][4 * eg + 2] = v.z;
+            oth[ni][4 * eg + 3] = v.w;
+        }
+    __syncthreads(); // L is free again
+    // block row grp of this wave: u and (bwd) da of each element
+    const int mi = grp;
     const size_t plane = (size_t)R * dff; // elements per intermediate array
-    // every h of this lane's elements first: the loads all go out before any
-    // store, instead of one load-wait-store chain per element
-    float hv[CU::MI][CU::NI][16];
+    float hv[NI][16];
 #pragma unroll
-    for (int mi = 0; mi < CU::MI; ++mi)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < CU::NI; ++ni)
+        for (int e = 0; e < 16; ++e) {
+            const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
+            const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
+            hv[ni][e] = m < n ? E::load1(dense, (size_t)m * dff + i) : 0.f;
+        }
+    // own / oth become a and (bwd) du, hv becomes dg
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
-                const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
-                hv[mi][ni][e] = m < n ? E::load1(dense, (size_t)m * dff + i) : 0.f;
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
+            const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
+            const size_t o = (size_t)m * dff + i;
+            const float h = hv[ni][e];
+            if constexpr (!BWD) {
+                const float u = grp ? oth[ni][e] + own[ni][e] : own[ni][e] + oth[ni][e];
+                put2<DT>(inter, plane, o, h * u);
+            } else {
+                const float u = grp ? oth[ni][e] : own[ni][e];
+                const float da = grp ? own[ni][e] : oth[ni][e];
+                const float du = da * h, dg = h != 0.f ? da * u + l1 : 0.f;
+                own[ni][e] = h * u; // a
+                oth[ni][e] = du;
+                hv[ni][e] = dg;
+                put2<DT>(inter, plane, o, du);
+                put2<DT>((uint8_t *)inter + NH * plane * esz, plane, o, dg);
             }
-    // a, du, dg of this lane's elements: u's accumulators become a, da's du
-    float dgv[CU::MI][CU::NI][16];
-#pragma unroll
-    for (int mi = 0; mi < CU::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < CU::NI; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
-                const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
-                const size_t o = (size_t)m * dff + i;
-                const float h = hv[mi][ni][e], u = au.v[mi][ni][e];
-                au.v[mi][ni][e] = h * u;
-                if constexpr (!BWD) {
-                    put2<DT>(inter, plane, o, h * u);
-                } else {
-                    const float da = ad.v[mi][ni][e];
-                    const float du = da * h, dg = h != 0.f ? da * u + l1 : 0.f;
-                    ad.v[mi][ni][e] = du;
-                    dgv[mi][ni][e] = dg;
-                    put2<DT>(inter, plane, o, du);
-                    put2<DT>((uint8_t *)inter + NH * plane * esz, plane, o, dg);
-                }
-            }
+        }
     if constexpr (BWD) {
         // Transposed copies [dff][R] of a, du, dg (hi and lo halves for bf16):
-        // each half goes through LDS as [i][m] so that the global stores run
-        // along m, 16 bytes per lane.
+        // each half goes through LDS as [i][m] (both groups' block rows), then
+        // the workgroup stores it along m, 16 bytes per lane.
+#pragma unroll 1
         for (int q = 0; q < 3 * NH; ++q) { // (a, du, dg) x (hi, lo)
             const int which = q / NH, part = q % NH;
 #pragma unroll
-            for (int mi = 0; mi < CU::MI; ++mi)
+            for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-                for (int ni = 0; ni < CU::NI; ++ni)
+                for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
+                    const int r = ng::acc_row<CU>(wm, mi, 4 * g, lane);
+                    const int c = ng::acc_col<CU>(wn, ni, lane);
+                    uint8_t *dst = L + c * P + r * esz;
+                    float v[4];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
-                        const int r = ng::acc_row<CU>(wm, mi, 4 * g, lane);
-                        const int c = ng::acc_col<CU>(wn, ni, lane);
-                        uint8_t *dst = L + c * P + r * esz;
-                        float v[4];
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = 4 * g + k;
+                        v[k] = which == 0 ? own[ni][e] : (which == 1 ? oth[ni][e] : hv[ni][e]);
+                    }
+                    if constexpr (DT == TWELL_BF16) {
+                        uint16_t hw[4];
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
-                            const int e = 4 * g + k;
-                            v[k] = which == 0 ? au.v[mi][ni][e]
-                                              : (which == 1 ? ad.v[mi][ni][e] : dgv[mi][ni][e]);
+                            const uint16_t hi = f32_to_bf16(v[k]);
+                            hw[k] = part == 0 ? hi : f32_to_bf16(v[k] - bf16_to_f32(hi));
                         }
-                        if constexpr (DT == TWELL_BF16) {
-                            uint16_t hw[4];
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                const uint16_t hi = f32_to_bf16(v[k]);
-                                hw[k] = part == 0 ? hi : f32_to_bf16(v[k] - bf16_to_f32(hi));
-                            }
-                            *(uint2 *)dst = make_uint2(hw[0] | ((uint32_t)hw[1] << 16),
-                                                       hw[2] | ((uint32_t)hw[3] << 16));
-                        } else {
-                            *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
-                        }
+                        *(uint2 *)dst = make_uint2(hw[0] | ((uint32_t)hw[1] << 16),
+                                                   hw[2] | ((uint32_t)hw[3] << 16));
+                    } else {
+                        *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
                     }
+                }
             __syncthreads();
             uint8_t *tbase = (uint8_t *)inter_t + (size_t)q * plane * esz;
             constexpr int CPR = TILE * esz / 16; // 16-byte chunks per row
-            for (int t = threadIdx.x; t < TILE * CPR; t += CU::NT) {
+            for (int t = threadIdx.x; t < TILE * CPR; t += UD_NT) {
                 const int c = t / CPR, ch = t % CPR;
                 *(uint4 *)(tbase + ((size_t)(i0 + c) * R + m0) * esz + ch * 16) =
                     *(const uint4 *)(L + c * P + ch * 16);
@@ -293,17 +341,15 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt
 }
 
 // ---------------------------------------------------------------- kernels
-constexpr int UD_LDS = CW::LDS > TILE * (4 * TILE + 16) ? CW::LDS : TILE * (4 * TILE + 16);
-
 // forward: the A tiles, then (other workgroups) the W_d transpose
 template <int DT>
-__global__ __launch_bounds__(CW::NT, 2) void bk_a_kernel(
+__global__ __launch_bounds__(UD_NT, 1) void bk_a_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ ovf_rows,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
     const uint8_t *__restrict__ wd, int dm, int dff, int R, const void *__restrict__ dense,
     void *__restrict__ inter, void *__restrict__ wdt, int n_a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t L[ud_lds<DT>()];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
@@ -312,18 +358,18 @@ __global__ __launch_bounds__(CW::NT, 2) void bk_a_kernel(
         ud_tile<DT, false>(x, nullptr, ovf_rows, n, wu, nullptr, dm, dff, R, dense, 0.f, inter,
                            nullptr, b % nx, b / nx, L);
     else
-        weight_t_tile<DT>(wd, wdt, dm, dff, b - n_a, L);
+        weight_t_tile<DT, UD_NT>(wd, wdt, dm, dff, b - n_a, L);
 }
 
 // backward: the u/da tiles (the transposes run beside the ELL masks)
 template <int DT>
-__global__ __launch_bounds__(CW::NT, 1) void bk_ud_kernel(
+__global__ __launch_bounds__(UD_NT, 1) void bk_ud_kernel(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff, int R,
     const void *__restrict__ dense, float l1, void *__restrict__ inter, void *__restrict__ inter_t)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t L[UD_LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t L[ud_lds<DT>()];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
@@ -411,16 +457,16 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, false);
     const int n_a = (dff / TILE) * (L.R / TILE);
-    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a + (dm / TT) * (dff / TT)), dim3(CW::NT), 0, s,
-                       (const uint8_t *)x, h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu,
-                       (const uint8_t *)wd, dm, dff, L.R, h->dense, (void *)(ws + L.inter),
-                       (void *)(ws + L.wt), n_a);
+    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a + (dm / TT) * (dff / TT)), dim3(UD_NT),
+                       0, s, (const uint8_t *)x, h->ovf_rows, h->n_ovf, h->max_ovf,
+                       (const uint8_t *)wu, (const uint8_t *)wd, dm, dff, L.R, h->dense,
+                       (void *)(ws + L.inter), (void *)(ws + L.wt), n_a);
     tm.mark("bk_a_kernel");
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
     hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + TILE - 1) / TILE, L.R / TILE, L.S),
-                       dim3(CW::NT), 0, s, (const uint8_t *)(ws + L.inter),
-                       (const uint8_t *)(ws + L.wt), h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
-                       (float *)(ws + L.part));
+                       dim3(CW::NT), 0, s,
+                       (const uint8_t *)(ws + L.inter), (const uint8_t *)(ws + L.wt), h->n_ovf,
+                       h->max_ovf, dm, dff, L.R, L.S, (float *)(ws + L.part));
     tm.mark("bk_y_kernel");
 }
 
@@ -431,8 +477,8 @@ void bk_ud_dt(const void *x, const void *dy, const hybrid_t *h, const void *wu, 
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
     const int n_ud = (dff / TILE) * (L.R / TILE);
-    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud), dim3(CW::NT), 0, s, (const uint8_t *)x,
-                       (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
+    hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud), dim3(UD_NT), 0, s,
+                       (const uint8_t *)x, (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
                        (const uint8_t *)wu, (const uint8_t *)wd, dm, dff, L.R, h->dense, l1,
                        (void *)(ws + L.inter), (void *)(ws + L.inter_t));
     tm.mark("bk_ud_kernel");

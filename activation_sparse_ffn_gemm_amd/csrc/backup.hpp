@@ -75,8 +75,8 @@ template <int DT> using Store = typename elem<DT>::storage;
 
 // One TT x TT tile of out[c][r] = in[src(r)][c] for c < cols and r < rows_out,
 // src(r) = r, or gather[r] for r < n_valid and a zero row past it (gather
-// non-null). 256 threads; lds: TT x (TT + 8) elements.
-template <typename T>
+// non-null). NTH threads; lds: TT x (TT + 8) elements.
+template <typename T, int NTH = 256>
 DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols, int rows_out,
                          const int32_t *__restrict__ gather, int n_valid, int bx, int by,
                          uint8_t *lds)
@@ -87,7 +87,7 @@ DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols
     if (gather && r0 >= (n_valid + TT - 1) / TT * TT)
         return; // never read: the products stop at the padded row count
     constexpr int CPR = TT / V; // chunks per tile row
-    for (int q = tid; q < TT * CPR; q += 256) {
+    for (int q = tid; q < TT * CPR; q += NTH) {
         const int r = q / CPR, cc = q % CPR, gr = r0 + r, gc = c0 + cc * V;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (gr < n_valid && gc < cols) {
@@ -100,7 +100,7 @@ DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols
             tile[r][cc * V + k] = e[k];
     }
     __syncthreads();
-    for (int q = tid; q < TT * CPR; q += 256) {
+    for (int q = tid; q < TT * CPR; q += NTH) {
         const int c = q / CPR, rc = q % CPR, gc = c0 + c, gr = r0 + rc * V;
         if (gc >= cols || gr >= rows_out)
             continue;
@@ -115,12 +115,12 @@ DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols
 
 // Tiles of a weight transpose [dff][dm] -> [dm][dff]
 DEVI int wt_tiles(int dm, int dff) { return (dm / TT) * (dff / TT); }
-template <int DT>
+template <int DT, int NTH = 256>
 DEVI void weight_t_tile(const void *w, void *wt, int dm, int dff, int b, uint8_t *lds)
 {
     const int nx = dm / TT;
-    transpose_tile<Store<DT>>((const Store<DT> *)w, (Store<DT> *)wt, dm, dff, nullptr, dff, b % nx,
-                              b / nx, lds);
+    transpose_tile<Store<DT>, NTH>((const Store<DT> *)w, (Store<DT> *)wt, dm, dff, nullptr, dff,
+                                   b % nx, b / nx, lds);
 }
 
 

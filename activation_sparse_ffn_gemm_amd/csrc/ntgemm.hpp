@@ -151,11 +151,16 @@ template <class C> DEVI int wave_n()
 // an operand should repeat a valid row and their outputs be dropped);
 // off(kt) gives step kt's byte offsets. L: C::LDS bytes of shared memory.
 // Ends with a barrier: L may be reused right after.
+// wave0: the first of the C::NWV waves that run this product. Several groups
+// of waves of one workgroup may run products of their own side by side (each
+// on its own L); the barriers are the workgroup's, so every group must run
+// the same number of K steps.
 template <class C, int DT, class RowA, class RowB, class Off>
-DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, Acc<C> &acc)
+DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, Acc<C> &acc,
+                   int wave0 = 0)
 {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) - wave0;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
