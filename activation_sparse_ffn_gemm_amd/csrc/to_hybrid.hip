@@ -7,7 +7,7 @@
 //   1. rows:  one wave per row sums the tile counts (row_nnz) and, for a row
 //             with row_nnz <= K, concatenates its tiles into ELL row t; the
 //             tiles are in column order, so the ELL row is ascending.
-//   2. slots + dense: one workgroup per block of 64 rows counts the overflow
+//   2. slots + dense: one workgroup per block of BLK rows counts the overflow
 //             rows before its block (a reduction over row_nnz), numbers its
 //             own overflow rows after them in row order (backup slots in
 //             ascending row order), writes row_slot, ovf_rows, and the dense
@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
     }
 }
 
-constexpr int BLK = 16;   // rows per workgroup of the slot/dense launch (few backup rows each)
+constexpr int BLK = 4;    // rows per workgroup of the slot/dense launch: a workgroup builds
+                          // its backup rows one after another, so blocks stay small
 constexpr int DNT = 256;  // its threads
 constexpr int ROW_LDS = 32768; // bytes of one dense row built in LDS (d_ff 16384 bf16 / 8192 f32)
 
