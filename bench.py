@@ -307,6 +307,8 @@ def main():
     # the gather performs it), the index/value arrays it reads and what it
     # writes; flops count the dense contractions' 2 m n k.
     n_t = dff // 128
+    nblk = (T + 63) // 64                        # 64-row blocks of the CSC masks
+    dx_split = T >= 1024 and dff * dm * 2 >= (16 << 20)  # the backward's XCD-local dx pass
     row_b = dm * 2                               # one bf16 row of d_model
     T_ell = T - n_ovf
     twell_b = T * n_t * 4 + nnz * 4              # count + (int16 col, bf16 val) per entry
@@ -342,8 +344,22 @@ def main():
         "bk_a_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "A = h_O (.) x_O W_u (1 GEMM)"),
         "bk_y_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "y_O = A W_d (1 GEMM)"),
         "bk_ud_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "u_O and da_O (2 GEMMs)"),
-        "bk_dx_kernel": ("mfma", 2 * 2.0 * n_ovf * dm * dff, "dx_O = du W_u^T + dg W_g^T (2 GEMMs)"),
-        "bk_dw_kernel": ("mfma", 3 * 2.0 * n_ovf * dm * dff, "dW_d, dW_u, dW_g += (3 GEMMs)"),
+        "bk_dxdw_kernel": ("mfma", 5 * 2.0 * n_ovf * dm * dff,
+                           "dx_O = du W_u^T + dg W_g^T (2 GEMMs) and dW_d, dW_u, dW_g += "
+                           "(3 GEMMs)"),
+        "mask_kernel": ("hbm", 8 * T + nnz_ell * 2 + nblk * dff * 12
+                        + (4 * dff * row_b if dx_split else 0)
+                        + (4 * dff * row_b + 4 * n_ovf * row_b if n_ovf > 0 else 0),
+                        "row_nnz, row_slot per row, column per ELL entry read; 64-row block "
+                        "mask and count per neuron written; on the same launch the slice-major "
+                        "wu_t, wg_t copy (XCD-local dx) and the backup's transposed W_u, W_g, "
+                        "x_O, dy_O (read + write)"),
+        "blk_prefix_kernel": ("hbm", nblk * dff * 12 + dff * 4,
+                              "block counts read twice and rewritten as prefixes; totals"),
+        "colptr_kernel": ("hbm", dff * 8 + 4, "neuron totals read, column pointers written"),
+        "csc_fill_kernel": ("hbm", 8 * T + nnz_ell * 22,
+                            "per ELL entry: column, mask, block prefix, column pointer read, "
+                            "slot written"),
     }
     peak = {"mfma": BF16_PEAK_TFLOPS, "hbm": HBM_PEAK_GBS}
     unit = {"mfma": "TFLOP/s", "hbm": "GB/s"}
