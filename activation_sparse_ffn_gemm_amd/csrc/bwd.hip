@@ -567,10 +567,12 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     const uint8_t *xb = (const uint8_t *)x, *dyb = (const uint8_t *)dy;
     const int rgroups = (T + NT / 64 - 1) / (NT / 64);
     constexpr int NWN = NW < 16 ? NW : 16;          // neuron pass: accumulated words per lane
-    // entries in flight per wave (neuron pass, dx pass); waves sharing one
-    // neuron's entries (narrow rows only: wide rows leave no registers for it)
-    constexpr int GN = NW <= 16 ? 2 : 1;
-    constexpr int GD = NW <= 4 ? 4 : 2;
+    // entries in flight per wave (neuron pass, dx pass): one beyond the
+    // narrowest rows, since resident waves hide the gathers' latency better
+    // than a second register buffer does; waves sharing one neuron's entries
+    // (narrow rows only: wide rows leave no registers for it)
+    constexpr int GN = 1;
+    constexpr int GD = NW <= 4 ? 4 : 1;
     constexpr int NSPLIT = NW <= 8 ? 4 : 1;
     constexpr int NWP = NW < ACC_NW ? NW : ACC_NW; // dx pass: words per lane of one part
     const int parts = row_parts<DT>(dm, NWP);

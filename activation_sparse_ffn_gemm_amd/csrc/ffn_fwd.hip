@@ -443,7 +443,10 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
     const int groups = (T + NT / 64 - 1) / (NT / 64);
     if (!use_split(DT, T, dm, dff)) {
         constexpr int NWP = NW < 16 ? NW : 16; // whole rows up to d_model 2048 (bf16)
-        constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
+        // entries in flight per wave: one for rows of 1 KB and more, where the
+        // registers of a second would cost a wave per SIMD (the gathers are
+        // latency-bound: resident waves hide more than deeper buffers)
+        constexpr int G = NW <= 4 ? 4 : 1;
         const int parts = row_parts<DT>(dm, NWP);
         hipLaunchKernelGGL((ffn_fwd_kernel<DT, NW, NWP, G>), dim3(groups, parts), dim3(NT), 0, s,
                            (const uint8_t *)x, h->count, h->col, h->val, T, nt, h->width,
@@ -458,7 +461,7 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
     int16_t *cc = (int16_t *)(ws + L.cc);
     int32_t *rn = (int32_t *)(ws + L.rn);
     const int n_copy = ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD;
-    constexpr int GU = NW <= 16 ? 4 : 2; // entries in flight per wave (no accumulators here)
+    constexpr int GU = NW <= 8 ? 2 : 1; // entries in flight per wave (occupancy first)
     hipLaunchKernelGGL((fwd_up_kernel<DT, NW, GU>), dim3(n_copy + groups * NXCD), dim3(NT), 0, s,
                        (const uint8_t *)x, h->count, h->col, h->val, T, nt, h->width,
                        (const uint8_t *)wu, dm, n_copy, (const uint32_t *)wd, wds, dff, sl, ac,
@@ -514,7 +517,7 @@ void launch_hyb_split_nw(const void *x, const hybrid_t *h, const void *wu, const
     uint32_t *wds = (uint32_t *)ws;
     float *ac = (float *)(ws + up256((size_t)NXCD * dff * sl.swp * 4));
     const int n_copy = ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD;
-    constexpr int GU = NW <= 16 ? 4 : 2;
+    constexpr int GU = NW <= 8 ? 2 : 1;
     hipLaunchKernelGGL((hfwd_up_kernel<DT, NW, GU>), dim3(n_copy + groups * NXCD), dim3(NT), 0, s,
                        (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col, h->ell_val, T,
                        h->K, nt, (const uint8_t *)wu, dm, n_copy, (const uint32_t *)wd, wds, dff,

@@ -110,7 +110,7 @@ void launch_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd,
         return;
     }
     constexpr int NWP = NW < 16 ? NW : 16;
-    constexpr int G = NW <= 4 ? 4 : (NW <= 16 ? 2 : 1); // entries in flight per wave
+    constexpr int G = NW <= 4 ? 4 : 1; // entries in flight per wave (occupancy first)
     const int parts = row_parts<DT>(dm, NWP);
     hipLaunchKernelGGL((hfwd_ell_kernel<DT, NW, NWP, G>), dim3((T + NT / 64 - 1) / (NT / 64), parts),
                        dim3(NT), 0, s, (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col,

@@ -117,6 +117,8 @@ def parse():
     p.add_argument("--no-dense", action="store_true", help="skip the dense torch leg")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the few-token (2B decode) leg")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the 1.5B forward density sweep leg")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
     return p.parse_args()
@@ -186,6 +188,65 @@ def decode_leg(torch, tw, synth, dev):
     return {"workload": "2b-decode", "d_model": 2304, "d_ff": 6144, "density": 0.01,
             "width": 32, "call": "twell_decode_fwd (gate partials, pack + up, down: 3 launches)",
             "timing": "HIP graph of 10 calls, replayed 20 times", "by_T": rows}
+
+
+def sweep_leg(torch, tw, synth, dev):
+    """The 1.5B-scale forward (T 8192, d_model 2048, d_ff 5632) at gate
+    densities 0.5, 1, 2, 5 and 20%: gate GEMM + TwELL pack, then the fused
+    up/down, against the dense bf16 forward of the same shape, both
+    graph-timed. The TwELL width is 32 slots per tile up to 5% and 64 at 20%
+    (about 26 nonzeros per 128-column tile there)."""
+    rows = []
+    for dens in synth.SWEEP_1P5B:
+        width = 32 if dens <= 0.05 else 64
+        w = synth.SCALE_1P5B.with_(density=dens, width=width)
+        d = synth.make_inputs(w)
+        x, wg, wu, wd = (d[k].to(dev) for k in ("x", "wg_t", "wu_t", "wd"))
+        del d
+        T, dm, dff = w.T, w.d_model, w.d_ff
+        out = tw.empty_twell(T, dff, width, torch.bfloat16, dev)
+        y = torch.empty((T, dm), dtype=torch.float32, device=dev)
+        gws = torch.empty(max(1, tw.gate_workspace_bytes(tw.TWELL_BF16, T, dm, dff)),
+                          dtype=torch.uint8, device=dev)
+        fws = torch.empty(max(1, tw.fwd_workspace_bytes(tw.TWELL_BF16, T, dm, dff, width)),
+                          dtype=torch.uint8, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def sparse():
+            tw.gate_pack(x, wg, width=width, out=out, status=st, workspace=gws)
+            tw.ffn_fwd(x, out, wu, wd, y=y, workspace=fws, status=st)
+        sp_us = graph_us(torch, sparse, calls=4, replays=10)
+        if int(st.item()) != 0:
+            raise SystemExit(f"sweep density {dens}: device status {int(st.item())}")
+        nnz = int(out.count.clamp(max=width).sum())
+        # per-kernel times: the same calls with events between the kernels
+        tms = (tw.KernelTimer(), tw.KernelTimer())
+        kern = {}
+        for _ in range(5):
+            tw.gate_pack(x, wg, width=width, out=out, status=st, workspace=gws, timing=tms[0])
+            tw.ffn_fwd(x, out, wu, wd, y=y, workspace=fws, status=st, timing=tms[1])
+            torch.cuda.synchronize()
+            for tm in tms:
+                for name, ms in tm.collect():
+                    kern[name] = kern.get(name, 0.0) + ms * 1e3 / 5
+        gu_t = torch.cat([wg, wu], 0).t().contiguous()
+        wd_c = wd.contiguous()
+
+        def dense():
+            gu = x @ gu_t
+            return (torch.relu(gu[:, :dff]) * gu[:, dff:]) @ wd_c
+        de_us = graph_us(torch, dense, calls=4, replays=10)
+        rows.append({"density": dens, "measured_density": round(nnz / (T * dff), 5),
+                     "width": width, "sparse_us": round(sp_us, 1), "dense_us": round(de_us, 1),
+                     "sparse_tokens_per_s": round(T / (sp_us * 1e-6), 1),
+                     "dense_tokens_per_s": round(T / (de_us * 1e-6), 1),
+                     "speedup": round(de_us / sp_us, 3),
+                     "kernel_us": {k: round(v, 1) for k, v in kern.items()}})
+        del x, wg, wu, wd, out, y, gws, fws, gu_t, wd_c
+        torch.cuda.empty_cache()
+    return {"workload": "1.5b-fwd", "T": 8192, "d_model": 2048, "d_ff": 5632,
+            "call": "twell_gate_pack + twell_ffn_fwd (inference forward)",
+            "timing": "HIP graph of 4 calls, replayed 10 times", "by_density": rows}
 
 
 def main():
@@ -455,6 +516,7 @@ def main():
         del p_gu, p_d, xr
 
     decode = None if a.no_decode else decode_leg(torch, tw, synth, dev)
+    sweep = None if a.no_sweep else sweep_leg(torch, tw, synth, dev)
 
     # ---- CPU oracle on this host (bounded sample of the same workload)
     cpu = None
@@ -505,6 +567,7 @@ def main():
         "dense_bf16": dense,
         "memory": memory,
         "decode": decode,
+        "density_sweep": sweep,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
