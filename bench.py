@@ -444,7 +444,12 @@ def main():
     traffic, traffic_note = measured_traffic(dom, a.workload)
     roofline = {"kernel": dom, "bound": b, "achieved": round(ach, 1), "peak": peak[b],
                 "unit": unit[b], "frac": round(ach / peak[b], 4), "traffic": traffic,
-                "traffic_note": traffic_note, "launch_ms": round(kern_ms[dom], 4),
+                "traffic_note": traffic_note,
+                "note": ("algorithmic bytes count every gathered row once per use; rows served "
+                         "again from L2 or the MALL let them run above the HBM peak, and "
+                         "traffic (HBM-side bytes from the counters) is then below them"
+                         if b == "hbm" else "algorithmic flops of the dense contraction"),
+                "launch_ms": round(kern_ms[dom], 4),
                 "work_per_launch": wk, "work_unit": desc}
 
     # ---- layer memory: what the sparse path keeps between forward and backward
