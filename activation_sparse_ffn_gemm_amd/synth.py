@@ -78,6 +78,12 @@ TRAIN_1P5B = Workload("1.5b-train-skewed", 8192, 2048, 5632, "bf16", 0.01,
                       width=TILE_C)
 
 
+def sweep_workload(density: float) -> Workload:
+    """The 1.5B forward at one sweep density. TwELL width 32 up to 5% (at most
+    about 6.4 expected nonzeros per 128-column tile) and 64 at 20% (about 26)."""
+    return SCALE_1P5B.with_(density=density, width=32 if density <= 0.05 else 64)
+
+
 def _rng(seed: int, stream: int) -> np.random.Generator:
     return np.random.default_rng([seed, stream])
 

@@ -198,8 +198,8 @@ def sweep_leg(torch, tw, synth, dev):
     (about 26 nonzeros per 128-column tile there)."""
     rows = []
     for dens in synth.SWEEP_1P5B:
-        width = 32 if dens <= 0.05 else 64
-        w = synth.SCALE_1P5B.with_(density=dens, width=width)
+        w = synth.sweep_workload(dens)
+        width = w.width
         d = synth.make_inputs(w)
         x, wg, wu, wd = (d[k].to(dev) for k in ("x", "wg_t", "wu_t", "wd"))
         del d

@@ -207,7 +207,7 @@ def test_forward_1p5b_sweep_sampled(orc):
     checked (rows are independent)."""
     rows = np.sort(np.random.default_rng(5).choice(8192, 128, replace=False))
     for rho in synth.SWEEP_1P5B:
-        w = synth.SCALE_1P5B.with_(density=rho, width=128 if rho >= 0.05 else 32)
+        w = synth.sweep_workload(rho)  # the widths bench.py's sweep runs
         announce("forward 1.5b sweep", rho)
         d = synth.make_inputs(w)
         x, wg, wu, wd = upload(d)
@@ -218,7 +218,7 @@ def test_forward_1p5b_sweep_sampled(orc):
         assert int(st.item()) == 0
         x64 = f64(d["x"][rows])
         g = orc.gate(x64, f64(d["wg_t"]))
-        tw_r, _ = oracle_twell_for_gpu(orc, g, 128, "bf16", "cpu")
+        tw_r, _ = oracle_twell_for_gpu(orc, g, w.width, "bf16", "cpu")
         y_ref = orc.ffn_twell(x64, tw_r, f64(d["wu_t"]), f64(d["wd"]))
         assert_close(y[rows], y_ref, "bf16", f"y rho={rho}")
         del x, wg, wu, wd, t, y
