@@ -482,6 +482,16 @@ __global__ __launch_bounds__(NT) void bwd_dxs_kernel(
     const int n = min(row_nnz[t], K);
     const size_t TK = (size_t)T * K, rb = (size_t)t * K;
     const uint32_t *slice = wsl + (size_t)k * dff * 2 * sl.swp;
+    // one descriptor over this XCD's slice array (rows of 2 swp words); a
+    // lane's word offsets are clamped to the padded slice, words past nk are
+    // never stored
+    const int rowb = 2 * sl.swp * 4;
+    const __amdgpu_buffer_rsrc_t rs_all = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)slice, (short)0, dff * rowb, BUF_DWORD3);
+    int offq[SPL];
+#pragma unroll
+    for (int q = 0; q < SPL; ++q)
+        offq[q] = min(q * 64 + lane, sl.swp - 1) * 4;
     float acc[SPL][EPW];
 #pragma unroll
     for (int q = 0; q < SPL; ++q)
@@ -501,17 +511,15 @@ __global__ __launch_bounds__(NT) void bwd_dxs_kernel(
                 cu = cg = 0.f;
             }
         }
-        // the row's two slices through one buffer descriptor: words past the
-        // row's 2 swp read 0, words past nk are never stored
+        // the row's two slices (W_u's, then W_g's)
         uint32_t vu[G][SPL], vg[G][SPL];
         auto fetch = [&](int e, uint32_t (&u)[SPL], uint32_t (&g)[SPL]) {
-            const int c = bcast(ci, min(e, m - 1));
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(slice + (size_t)c * 2 * sl.swp), (short)0, 2 * sl.swp * 4, BUF_DWORD3);
+            const int rc = bcast(ci, min(e, m - 1)) * rowb;
 #pragma unroll
             for (int q = 0; q < SPL; ++q) {
-                u[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (q * 64 + lane) * 4, 0, 0);
-                g[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (sl.swp + q * 64 + lane) * 4, 0, 0);
+                u[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_all, rc + offq[q], 0, 0);
+                g[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_all, rc + sl.swp * 4 + offq[q], 0,
+                                                            0);
             }
         };
 #pragma unroll

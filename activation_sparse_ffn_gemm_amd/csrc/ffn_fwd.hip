@@ -393,6 +393,15 @@ __global__ __launch_bounds__(NT) void fwd_down_kernel(
     const float *arow = ac + (size_t)t * cap;
     const int16_t *crow = cc + (size_t)t * cap;
     const uint32_t *slice = wds + (size_t)k * dff * sl.swp;
+    // one descriptor over this XCD's slice array; a lane's word offsets are
+    // clamped to the padded slice (words past nk are never stored)
+    const int rowb = sl.swp * 4;
+    const __amdgpu_buffer_rsrc_t rs_all = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)slice, (short)0, dff * rowb, BUF_DWORD3);
+    int offq[SPL];
+#pragma unroll
+    for (int q = 0; q < SPL; ++q)
+        offq[q] = min(q * 64 + lane, sl.swp - 1) * 4;
     float acc[SPL][EPW];
 #pragma unroll
     for (int c = 0; c < SPL; ++c)
@@ -404,14 +413,11 @@ __global__ __launch_bounds__(NT) void fwd_down_kernel(
         const int ci = lane < m ? crow[eb + lane] : 0;
         const float av = lane < m ? arow[eb + lane] : 0.f;
         uint32_t v[G][SPL];
-        // the row's slice through a buffer descriptor: words past nk read 0
         auto fetch = [&](int e, uint32_t (&w)[SPL]) {
             const int c = min(max(bcast(ci, min(e, m - 1)), 0), dff - 1);
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(slice + (size_t)c * sl.swp), (short)0, nk * 4, BUF_DWORD3);
 #pragma unroll
             for (int q = 0; q < SPL; ++q)
-                w[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (q * 64 + lane) * 4, 0, 0);
+                w[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_all, c * rowb + offq[q], 0, 0);
         };
 #pragma unroll
         for (int g = 0; g < G; ++g)
