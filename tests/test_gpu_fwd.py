@@ -162,6 +162,21 @@ def test_ffn_fwd_integer_exact(orc, dtype, T, dm, dff):
     assert np.array_equal(f64(y), y_ref)
 
 
+@pytest.mark.parametrize("dtype,T,dm,dff,W", [("f32", 77, 320, 384, 1), ("bf16", 77, 320, 384, 5),
+                                              ("bf16", 300, 1024, 2816, 7),
+                                              ("bf16", 1029, 2048, 4096, 7)])
+def test_ffn_fwd_narrow_width_exact(orc, dtype, T, dm, dff, W):
+    """TwELL widths below the 8 slots a lane stages at once, with tiles holding
+    more nonzeros than W (the first W are stored, as the oracle's pack keeps
+    them): the staging reads slots of the next tile and past the row's last
+    tile, which must never be used. 1029 tokens take the two-pass path."""
+    announce("ffn_fwd narrow W", dtype, T, dm, dff, W)
+    d = synth.make_integer_inputs(T, dm, dff, dtype, 0.05)
+    y, y_ref, g = _fwd_on_oracle_twell(orc, d, dtype, W)
+    assert orc.twell_pack(g, W=W)["overflow"]
+    assert np.array_equal(f64(y), y_ref)
+
+
 @pytest.mark.parametrize("w", [synth.TINY_F32, synth.SCALE_0P5B, synth.DECODE_2B.with_(T=64),
                                synth.DECODE_2B.with_(T=1)], ids=lambda w: f"{w.name}-{w.T}")
 def test_ffn_fwd_on_oracle_twell(orc, w):
