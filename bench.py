@@ -252,7 +252,7 @@ def sweep_leg(torch, tw, synth, dev):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the layer is not sharded "
+        print(json.dumps({"error": "libtwell runs on one GPU only; the layer is not sharded "
                                    "across GPUs (bench.py --gpus 1)"}), flush=True)
         sys.exit(2)
     import torch
