@@ -276,8 +276,8 @@ def decode_workspace_bytes(dtype, T, d_model, d_ff, width) -> int:
 
 def decode_fwd(x, wg_t, wu_t, wd, width=TILE_C, out: Twell | None = None, y=None,
                workspace=None, status=None, timing: KernelTimer | None = None):
-    """The whole layer for T <= DECODE_T tokens in one launch; returns
-    (TwELL of h, y float32)."""
+    """The whole layer for T <= DECODE_T tokens in one call (three launches
+    on the current stream); returns (TwELL of h, y float32)."""
     T, dm = x.shape
     d_ff = wg_t.shape[0]
     if out is None:
