@@ -311,11 +311,9 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt
     };
     auto rowa = [&](int r) { return ta + (size_t)(i0 + r) * rowbytes; };
     auto rowb = [&](int r) { return tx + (size_t)min(d0 + r, dm - 1) * rowbytes; };
-    ng::Acc<CW> acc;
-    ng::mainloop<CW, DT>(L, rowa, rowb, off, 0, nk, acc);
     const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
-    // all of this lane's current dW values first (loads in flight together),
-    // then the sums
+    // all of this lane's current dW values, requested before the K loop (they
+    // do not depend on it): their latency overlaps the loop's first loads
     float cur[CW::MI][CW::NI][16];
 #pragma unroll
     for (int mi = 0; mi < CW::MI; ++mi)
@@ -325,8 +323,12 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt
             for (int e = 0; e < 16; ++e) {
                 const int i = i0 + ng::acc_row<CW>(wm, mi, e, lane);
                 const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
-                cur[mi][ni][e] = d < dm ? out[(size_t)i * dm + d] : 0.f;
+                // unconditional load (column clamped into the row), then select
+                const float v = out[(size_t)i * dm + min(d, dm - 1)];
+                cur[mi][ni][e] = d < dm ? v : 0.f;
             }
+    ng::Acc<CW> acc;
+    ng::mainloop<CW, DT>(L, rowa, rowb, off, 0, nk, acc);
 #pragma unroll
     for (int mi = 0; mi < CW::MI; ++mi)
 #pragma unroll
