@@ -201,43 +201,56 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     if constexpr (BWD) {
         // Transposed copies [dff][R] of a, du, dg (hi and lo halves for bf16):
         // each half goes through LDS as [i][m] (both groups' block rows), then
-        // the workgroup stores it along m, 16 bytes per lane.
+        // the workgroup stores it along m, 16 bytes per lane. QB halves share
+        // one LDS round (three for bf16: two rounds instead of six).
+        constexpr int PLANE = TILE * P;
+        constexpr int QB = ud_lds<DT>() / PLANE >= 3 ? 3 : 1;
+        static_assert((3 * NH) % QB == 0 && QB * PLANE <= ud_lds<DT>(), "LDS rounds");
 #pragma unroll 1
-        for (int q = 0; q < 3 * NH; ++q) { // (a, du, dg) x (hi, lo)
-            const int which = q / NH, part = q % NH;
+        for (int qb = 0; qb < 3 * NH; qb += QB) {
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
+            for (int qq = 0; qq < QB; ++qq) {
+                const int q = qb + qq; // (a, du, dg) x (hi, lo)
+                const int which = q / NH, part = q % NH;
+                uint8_t *Lq = L + qq * PLANE;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
-                    const int r = ng::acc_row<CU>(wm, mi, 4 * g, lane);
-                    const int c = ng::acc_col<CU>(wn, ni, lane);
-                    uint8_t *dst = L + c * P + r * esz;
-                    float v[4];
+                for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int e = 4 * g + k;
-                        v[k] = which == 0 ? own[ni][e] : (which == 1 ? oth[ni][e] : hv[ni][e]);
-                    }
-                    if constexpr (DT == TWELL_BF16) {
-                        uint16_t hw[4];
+                    for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
+                        const int r = ng::acc_row<CU>(wm, mi, 4 * g, lane);
+                        const int c = ng::acc_col<CU>(wn, ni, lane);
+                        uint8_t *dst = Lq + c * P + r * esz;
+                        float v[4];
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
-                            const uint16_t hi = f32_to_bf16(v[k]);
-                            hw[k] = part == 0 ? hi : f32_to_bf16(v[k] - bf16_to_f32(hi));
+                            const int e = 4 * g + k;
+                            v[k] = which == 0 ? own[ni][e] : (which == 1 ? oth[ni][e] : hv[ni][e]);
                         }
-                        *(uint2 *)dst = make_uint2(hw[0] | ((uint32_t)hw[1] << 16),
-                                                   hw[2] | ((uint32_t)hw[3] << 16));
-                    } else {
-                        *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                        if constexpr (DT == TWELL_BF16) {
+                            uint16_t hw[4];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                const uint16_t hi = f32_to_bf16(v[k]);
+                                hw[k] = part == 0 ? hi : f32_to_bf16(v[k] - bf16_to_f32(hi));
+                            }
+                            *(uint2 *)dst = make_uint2(hw[0] | ((uint32_t)hw[1] << 16),
+                                                       hw[2] | ((uint32_t)hw[3] << 16));
+                        } else {
+                            *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                        }
                     }
-                }
+            }
             __syncthreads();
-            uint8_t *tbase = (uint8_t *)inter_t + (size_t)q * plane * esz;
             constexpr int CPR = TILE * esz / 16; // 16-byte chunks per row
-            for (int t = threadIdx.x; t < TILE * CPR; t += UD_NT) {
-                const int c = t / CPR, ch = t % CPR;
-                *(uint4 *)(tbase + ((size_t)(i0 + c) * R + m0) * esz + ch * 16) =
-                    *(const uint4 *)(L + c * P + ch * 16);
+#pragma unroll
+            for (int qq = 0; qq < QB; ++qq) {
+                uint8_t *tbase = (uint8_t *)inter_t + (size_t)(qb + qq) * plane * esz;
+                const uint8_t *Lq = L + qq * PLANE;
+                for (int t = threadIdx.x; t < TILE * CPR; t += UD_NT) {
+                    const int c = t / CPR, ch = t % CPR;
+                    *(uint4 *)(tbase + ((size_t)(i0 + c) * R + m0) * esz + ch * 16) =
+                        *(const uint4 *)(Lq + c * P + ch * 16);
+                }
             }
             __syncthreads();
         }
