@@ -180,13 +180,12 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
-            const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
-            const size_t o = (size_t)m * dff + i;
             const float h = hv[ni][e];
             if constexpr (!BWD) {
+                const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
+                const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
                 const float u = grp ? oth[ni][e] + own[ni][e] : own[ni][e] + oth[ni][e];
-                put2<DT>(inter, plane, o, h * u);
+                put2<DT>(inter, plane, (size_t)m * dff + i, h * u);
             } else {
                 const float u = grp ? oth[ni][e] : own[ni][e];
                 const float da = grp ? own[ni][e] : oth[ni][e];
@@ -194,16 +193,56 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                 own[ni][e] = h * u; // a
                 oth[ni][e] = du;
                 hv[ni][e] = dg;
-                put2<DT>(inter, plane, o, du);
-                put2<DT>((uint8_t *)inter + NH * plane * esz, plane, o, dg);
             }
         }
     if constexpr (BWD) {
+        constexpr int PLANE = TILE * P;
+        constexpr int CPR = TILE * esz / 16; // 16-byte chunks per tile row
+        // du and dg as [R][dff] (planes du hi, du lo, dg hi, dg lo for bf16):
+        // each plane's tile goes through LDS as [m][i], then the workgroup
+        // stores it along i, 16 bytes per lane. QR planes per LDS round.
+        constexpr int NR = 2 * NH;
+        constexpr int QR = ud_lds<DT>() / PLANE >= 2 ? 2 : 1;
+        static_assert(NR % QR == 0 && QR * PLANE <= ud_lds<DT>(), "LDS rounds");
+#pragma unroll 1
+        for (int qb = 0; qb < NR; qb += QR) {
+#pragma unroll
+            for (int qq = 0; qq < QR; ++qq) {
+                const int q = qb + qq, which = q / NH, part = q % NH; // which: du, dg
+                uint8_t *Lq = L + qq * PLANE;
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = ng::acc_row<CU>(wm, mi, e, lane);
+                        const int c = ng::acc_col<CU>(wn, ni, lane);
+                        const float v = which == 0 ? oth[ni][e] : hv[ni][e];
+                        if constexpr (DT == TWELL_BF16) {
+                            const uint16_t hi = f32_to_bf16(v);
+                            *(uint16_t *)(Lq + r * P + c * 2) =
+                                part == 0 ? hi : f32_to_bf16(v - bf16_to_f32(hi));
+                        } else {
+                            *(float *)(Lq + r * P + c * 4) = v;
+                        }
+                    }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int qq = 0; qq < QR; ++qq) {
+                uint8_t *base = (uint8_t *)inter + (size_t)(qb + qq) * plane * esz;
+                const uint8_t *Lq = L + qq * PLANE;
+                for (int t = threadIdx.x; t < TILE * CPR; t += UD_NT) {
+                    const int r = t / CPR, ch = t % CPR;
+                    *(uint4 *)(base + ((size_t)(m0 + r) * dff + i0) * esz + ch * 16) =
+                        *(const uint4 *)(Lq + r * P + ch * 16);
+                }
+            }
+            __syncthreads();
+        }
         // Transposed copies [dff][R] of a, du, dg (hi and lo halves for bf16):
         // each half goes through LDS as [i][m] (both groups' block rows), then
         // the workgroup stores it along m, 16 bytes per lane. QB halves share
         // one LDS round (three for bf16: two rounds instead of six).
-        constexpr int PLANE = TILE * P;
         constexpr int QB = ud_lds<DT>() / PLANE >= 3 ? 3 : 1;
         static_assert((3 * NH) % QB == 0 && QB * PLANE <= ud_lds<DT>(), "LDS rounds");
 #pragma unroll 1
@@ -241,7 +280,6 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                     }
             }
             __syncthreads();
-            constexpr int CPR = TILE * esz / 16; // 16-byte chunks per row
 #pragma unroll
             for (int qq = 0; qq < QB; ++qq) {
                 uint8_t *tbase = (uint8_t *)inter_t + (size_t)(qb + qq) * plane * esz;
