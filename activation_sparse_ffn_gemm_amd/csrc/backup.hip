@@ -64,20 +64,6 @@ int split_k(int R, int dm, int nk)
 // ---------------------------------------------------------------- products
 DEVI int n_rows(const int32_t *n_ovf_p, int max_ovf) { return min(*n_ovf_p, max_ovf); }
 
-
-// hi/lo (bf16) or plain (f32) store of an intermediate value
-template <int DT> DEVI void put2(void *base, size_t lo_off, size_t o, float v)
-{
-    if constexpr (DT == TWELL_BF16) {
-        uint16_t *p = (uint16_t *)base;
-        const uint16_t hi = f32_to_bf16(v);
-        p[o] = hi;
-        p[lo_off + o] = f32_to_bf16(v - bf16_to_f32(hi));
-    } else {
-        ((float *)base)[o] = v;
-    }
-}
-
 // u (and da) of one tile of backup rows x neurons on eight waves in two
 // groups of four, each group on its own CU::LDS bytes of L:
 //   fwd (BWD = false): the groups sum the two halves of K of u; epilogue
@@ -182,10 +168,8 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
         for (int e = 0; e < 16; ++e) {
             const float h = hv[ni][e];
             if constexpr (!BWD) {
-                const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
-                const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
                 const float u = grp ? oth[ni][e] + own[ni][e] : own[ni][e] + oth[ni][e];
-                put2<DT>(inter, plane, (size_t)m * dff + i, h * u);
+                own[ni][e] = h * u; // A
             } else {
                 const float u = grp ? oth[ni][e] : own[ni][e];
                 const float da = grp ? own[ni][e] : oth[ni][e];
@@ -195,20 +179,20 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                 hv[ni][e] = dg;
             }
         }
-    if constexpr (BWD) {
-        constexpr int PLANE = TILE * P;
-        constexpr int CPR = TILE * esz / 16; // 16-byte chunks per tile row
-        // du and dg as [R][dff] (planes du hi, du lo, dg hi, dg lo for bf16):
-        // each plane's tile goes through LDS as [m][i], then the workgroup
-        // stores it along i, 16 bytes per lane. QR planes per LDS round.
-        constexpr int NR = 2 * NH;
+    constexpr int PLANE = TILE * P;
+    constexpr int CPR = TILE * esz / 16; // 16-byte chunks per tile row
+    {
+        // A (fwd) or du and dg (bwd) as [R][dff] (planes hi, lo of each for
+        // bf16): each plane's tile goes through LDS as [m][i], then the
+        // workgroup stores it along i, 16 bytes per lane. QR planes per round.
+        constexpr int NR = (BWD ? 2 : 1) * NH;
         constexpr int QR = ud_lds<DT>() / PLANE >= 2 ? 2 : 1;
         static_assert(NR % QR == 0 && QR * PLANE <= ud_lds<DT>(), "LDS rounds");
 #pragma unroll 1
         for (int qb = 0; qb < NR; qb += QR) {
 #pragma unroll
             for (int qq = 0; qq < QR; ++qq) {
-                const int q = qb + qq, which = q / NH, part = q % NH; // which: du, dg
+                const int q = qb + qq, which = q / NH, part = q % NH; // bwd: du, dg
                 uint8_t *Lq = L + qq * PLANE;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
@@ -216,7 +200,7 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                     for (int e = 0; e < 16; ++e) {
                         const int r = ng::acc_row<CU>(wm, mi, e, lane);
                         const int c = ng::acc_col<CU>(wn, ni, lane);
-                        const float v = which == 0 ? oth[ni][e] : hv[ni][e];
+                        const float v = !BWD ? own[ni][e] : (which == 0 ? oth[ni][e] : hv[ni][e]);
                         if constexpr (DT == TWELL_BF16) {
                             const uint16_t hi = f32_to_bf16(v);
                             *(uint16_t *)(Lq + r * P + c * 2) =
@@ -239,6 +223,8 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
             }
             __syncthreads();
         }
+    }
+    if constexpr (BWD) {
         // Transposed copies [dff][R] of a, du, dg (hi and lo halves for bf16):
         // each half goes through LDS as [i][m] (both groups' block rows), then
         // the workgroup stores it along m, 16 bytes per lane. QB halves share
