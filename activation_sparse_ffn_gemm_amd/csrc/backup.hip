@@ -316,9 +316,11 @@ DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ 
         for (int ni = 0; ni < CW::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
+                // rows past n are padding rows of the R-row partial (never
+                // read): only the column needs a test, no branch per row
                 const int m = m0 + ng::acc_row<CW>(wm, mi, e, lane);
                 const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
-                if (m < n && d < dm)
+                if (d < dm)
                     p[(size_t)m * dm + d] = acc.v[mi][ni][e];
             }
 }
