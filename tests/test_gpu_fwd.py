@@ -261,6 +261,25 @@ def test_to_hybrid_on_oracle_twell_exact(orc, dtype):
         assert_hybrid_equal(hybrid_to_numpy(hy), ref)
 
 
+@pytest.mark.parametrize("dtype,dff", [("bf16", 640), ("bf16", 16512), ("f32", 8320)])
+def test_to_hybrid_wide_rows_exact(orc, dtype, dff):
+    """Backup rows built in the workgroup's 32 KB LDS row buffer (640) and, when
+    a row is wider than it (16512 bf16, 8320 f32), straight in memory; 203
+    tokens leave a ragged last block of rows."""
+    announce("to_hybrid wide rows", dtype, dff)
+    d = synth.make_integer_inputs(203, 128, dff, dtype, 0.03, skew_rows=11)
+    g = orc.gate(f64(d["x"]), f64(d["wg_t"]))
+    K = int(np.sort((g > 0).sum(1))[-12])
+    tw_r, (cnt, col, val) = oracle_twell_for_gpu(orc, g, 128, dtype, DEV)
+    ref = orc.to_hybrid(tw_r, K, 64)
+    assert ref["n_ovf"] >= 11
+    st = status_word()
+    hy = tw.to_hybrid(tw.Twell(cnt, col, val), K, 64, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert_hybrid_equal(hybrid_to_numpy(hy), ref)
+
+
 def test_to_hybrid_end_to_end_integer(orc):
     """GPU gate_pack -> GPU to_hybrid on integer inputs equals the oracle."""
     announce("to_hybrid e2e int")
