@@ -169,34 +169,48 @@ __global__ __launch_bounds__(NT) void blk_prefix_kernel(int32_t *__restrict__ cn
 
 constexpr int SCAN_NT = 1024;
 
-// in-place exclusive scan of colptr[0..dff); colptr[dff] = total
+// In-place exclusive scan of colptr[0..dff); colptr[dff] = total. Thread t
+// owns a run of consecutive elements (at most 32 for d_ff <= 32768): it sums
+// its run (8 loads in flight, indices clamped, values masked), one
+// block-wide scan of the run totals gives each run its start, and the thread
+// rewrites its own run. A clamped load outside the run is never used.
 __global__ __launch_bounds__(SCAN_NT) void colptr_kernel(int32_t *__restrict__ colptr, int dff)
 {
     __shared__ int wsum[SCAN_NT / 64];
-    __shared__ int carry;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (tid == 0)
-        carry = 0;
-    __syncthreads();
-    for (int i0 = 0; i0 < dff; i0 += SCAN_NT) {
-        const int i = i0 + tid;
-        const int v = i < dff ? colptr[i] : 0;
-        const int incl = wave_incl_scan(v, lane);
-        if (lane == 63)
-            wsum[wv] = incl;
-        __syncthreads();
-        int before = carry;
-        for (int w = 0; w < wv; ++w)
-            before += wsum[w];
-        if (i < dff)
-            colptr[i] = before + incl - v;
-        __syncthreads();
-        if (tid == SCAN_NT - 1)
-            carry = before + incl;
-        __syncthreads();
+    const int per = (dff + SCAN_NT - 1) / SCAN_NT;
+    const int b0 = min(dff, tid * per), b1 = min(dff, b0 + per);
+    int tot = 0;
+    for (int k0 = b0; k0 < b1; k0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = colptr[min(k0 + u, dff - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            tot += k0 + u < b1 ? v[u] : 0;
     }
-    if (tid == 0)
-        colptr[dff] = carry;
+    const int incl = wave_incl_scan(tot, lane);
+    if (lane == 63)
+        wsum[wv] = incl;
+    __syncthreads();
+    int run = incl - tot;
+    for (int w = 0; w < wv; ++w)
+        run += wsum[w];
+    for (int k0 = b0; k0 < b1; k0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = colptr[min(k0 + u, dff - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < b1) {
+                colptr[k0 + u] = run;
+                run += v[u];
+            }
+    }
+    if (tid == SCAN_NT - 1) // the last thread's run ends at the total
+        colptr[dff] = run;
 }
 
 // ------------------------------------------------------------ 3. fill
