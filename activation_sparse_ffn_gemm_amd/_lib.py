@@ -145,6 +145,116 @@ def _ptr(t):
     return None if t is None else c_p(t.data_ptr())
 
 
+# ---- argument checks: the C-ABI sees only pointers, so every tensor's shape,
+# dtype, layout and device is checked here, before any call reaches the GPU
+def _req(t, name, shape, dtype, device=None):
+    """t must be a contiguous tensor of `shape` and `dtype` (on `device` if
+    given); raises TwellError otherwise."""
+    if not isinstance(t, torch.Tensor):
+        raise TwellError(f"{name}: expected a tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise TwellError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TwellError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise TwellError(f"{name}: must be contiguous (row-major), e.g. not a transposed view")
+    if device is not None and t.device != torch.device(device):
+        raise TwellError(f"{name}: on {t.device}, expected {device}")
+
+
+def _ws_form(workspace):
+    if workspace is not None and (not isinstance(workspace, torch.Tensor)
+                                  or workspace.dtype != torch.uint8 or workspace.dim() != 1
+                                  or not workspace.is_contiguous()):
+        raise TwellError("workspace: expected a contiguous 1-D uint8 tensor")
+
+
+def _on_gpu(*named):
+    """Every given tensor lives on one GPU; returns that device. (The
+    workspace's form is checked first: it is the one argument whose shape the
+    other checks do not cover.)"""
+    for name, t in named:
+        if name == "workspace":
+            _ws_form(t)
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise TwellError(f"{name}: on {t.device}; the library runs on the GPU only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise TwellError(f"{name}: on {t.device}, other arguments on {dev}")
+    return dev
+
+
+def _ws(workspace, need, device):
+    """The caller's workspace, checked, or a new one of `need` bytes."""
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+    _ws_form(workspace)
+    if workspace.numel() < need:
+        raise TwellError(f"workspace: {workspace.numel()} bytes, need {need}")
+    return workspace
+
+
+def _status(status, device):
+    if status is not None:
+        _req(status, "status", (1,), torch.int32)
+    return status
+
+
+def _check_weights(d_ff, d_model, dtype, **w):
+    for name, t in w.items():
+        _req(t, name, (d_ff, d_model), dtype)
+
+
+def _check_twell(tw, T, dtype):
+    if not isinstance(tw, Twell):
+        raise TwellError("expected a Twell")
+    nt = tw.count.shape[1] if tw.count.dim() == 2 else -1
+    if tw.count.dim() != 2 or tw.col.dim() != 3:
+        raise TwellError("twell: count must be [T][d_ff/128], col/val [T][d_ff/128][width]")
+    W = tw.col.shape[2]
+    _req(tw.count, "twell.count", (T, nt), torch.int32)
+    _req(tw.col, "twell.col", (T, nt, W), torch.int16)
+    _req(tw.val, "twell.val", (T, nt, W), dtype)
+
+
+def _check_hybrid(hy, T, dtype):
+    if not isinstance(hy, Hybrid):
+        raise TwellError("expected a Hybrid")
+    if hy.ell_col.dim() != 2 or hy.dense.dim() != 2:
+        raise TwellError("hybrid: ell_col/ell_val must be [T][K], dense [max_ovf][d_ff]")
+    K, mo, dff = hy.ell_col.shape[1], hy.dense.shape[0], hy.dense.shape[1]
+    _req(hy.row_nnz, "hybrid.row_nnz", (T,), torch.int32)
+    _req(hy.row_slot, "hybrid.row_slot", (T,), torch.int32)
+    _req(hy.ell_col, "hybrid.ell_col", (T, K), torch.int16)
+    _req(hy.ell_val, "hybrid.ell_val", (T, K), dtype)
+    _req(hy.ovf_rows, "hybrid.ovf_rows", (mo,), torch.int32)
+    _req(hy.dense, "hybrid.dense", (mo, dff), dtype)
+    _req(hy.n_ovf, "hybrid.n_ovf", (1,), torch.int32)
+
+
+def _twell_tensors(tw):
+    return [("twell.count", tw.count), ("twell.col", tw.col), ("twell.val", tw.val)]
+
+
+def _hybrid_tensors(hy):
+    return [("hybrid.row_nnz", hy.row_nnz), ("hybrid.row_slot", hy.row_slot),
+            ("hybrid.ell_col", hy.ell_col), ("hybrid.ell_val", hy.ell_val),
+            ("hybrid.ovf_rows", hy.ovf_rows), ("hybrid.dense", hy.dense),
+            ("hybrid.n_ovf", hy.n_ovf)]
+
+
+def _x2(x, name="x"):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise TwellError(f"{name}: expected a [T][d_model] tensor")
+    _dt(x)
+    return x.shape
+
+
 def _stream(device) -> c_p:
     return c_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -236,12 +346,22 @@ def gate_workspace_bytes(dtype, T, d_model, d_ff) -> int:
 
 def gate_pack(x, wg_t, width=TILE_C, out: Twell | None = None, status=None,
               timing: KernelTimer | None = None, workspace=None) -> Twell:
-    T, dm = x.shape
+    T, dm = _x2(x)
+    _req(x, "x", (T, dm), x.dtype)
+    if not isinstance(wg_t, torch.Tensor) or wg_t.dim() != 2:
+        raise TwellError("wg_t: expected a [d_ff][d_model] tensor")
+    d_ff = wg_t.shape[0]
+    _req(wg_t, "wg_t", (d_ff, dm), x.dtype)
     if out is None:
-        out = empty_twell(T, wg_t.shape[0], width, x.dtype, x.device)
-    need = gate_workspace_bytes(_dt(x), T, dm, wg_t.shape[0])
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        out = empty_twell(T, d_ff, width, x.dtype, x.device)
+    _check_twell(out, T, x.dtype)
+    if out.d_ff != d_ff:
+        raise TwellError(f"out: d_ff {out.d_ff}, wg_t has {d_ff} rows")
+    dev = _on_gpu(("x", x), ("wg_t", wg_t), *_twell_tensors(out), ("status", status),
+                  ("workspace", workspace))
+    _status(status, dev)
+    need = gate_workspace_bytes(_dt(x), T, dm, d_ff)
+    workspace = _ws(workspace, need, dev)
     nbytes = 0 if workspace is None else workspace.numel()
     c = out.c()
     _check(load().twell_gate_pack(_dt(x), _ptr(x), _ptr(wg_t), T, dm, ctypes.byref(c),
@@ -256,12 +376,18 @@ def fwd_workspace_bytes(dtype, T, d_model, d_ff, width) -> int:
 
 def ffn_fwd(x, tw: Twell, wu_t, wd, y=None, workspace=None, status=None,
             timing: KernelTimer | None = None):
-    T, dm = x.shape
+    T, dm = _x2(x)
+    _req(x, "x", (T, dm), x.dtype)
+    _check_twell(tw, T, x.dtype)
+    _check_weights(tw.d_ff, dm, x.dtype, wu_t=wu_t, wd=wd)
     if y is None:
         y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
+    _req(y, "y", (T, dm), torch.float32)
+    dev = _on_gpu(("x", x), *_twell_tensors(tw), ("wu_t", wu_t), ("wd", wd), ("y", y),
+                  ("status", status), ("workspace", workspace))
+    _status(status, dev)
     need = fwd_workspace_bytes(_dt(x), T, dm, tw.d_ff, tw.width)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _ws(workspace, need, dev)
     nbytes = 0 if workspace is None else workspace.numel()
     c = tw.c()
     _check(load().twell_ffn_fwd(_dt(x), _ptr(x), ctypes.byref(c), _ptr(wu_t), _ptr(wd), dm,
@@ -278,15 +404,27 @@ def decode_fwd(x, wg_t, wu_t, wd, width=TILE_C, out: Twell | None = None, y=None
                workspace=None, status=None, timing: KernelTimer | None = None):
     """The whole layer for T <= DECODE_T tokens in one call (three launches
     on the current stream); returns (TwELL of h, y float32)."""
-    T, dm = x.shape
+    T, dm = _x2(x)
+    _req(x, "x", (T, dm), x.dtype)
+    if not isinstance(wg_t, torch.Tensor) or wg_t.dim() != 2:
+        raise TwellError("wg_t: expected a [d_ff][d_model] tensor")
     d_ff = wg_t.shape[0]
+    _check_weights(d_ff, dm, x.dtype, wg_t=wg_t, wu_t=wu_t, wd=wd)
+    if T > DECODE_T:
+        raise TwellError(f"decode_fwd takes at most {DECODE_T} tokens, got {T}")
     if out is None:
         out = empty_twell(T, d_ff, width, x.dtype, x.device)
+    _check_twell(out, T, x.dtype)
+    if out.d_ff != d_ff:
+        raise TwellError(f"out: d_ff {out.d_ff}, wg_t has {d_ff} rows")
     if y is None:
         y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
+    _req(y, "y", (T, dm), torch.float32)
+    dev = _on_gpu(("x", x), ("wg_t", wg_t), ("wu_t", wu_t), ("wd", wd), *_twell_tensors(out),
+                  ("y", y), ("status", status), ("workspace", workspace))
+    _status(status, dev)
     need = decode_workspace_bytes(_dt(x), T, dm, d_ff, out.width)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _ws(workspace, need, dev)
     nbytes = 0 if workspace is None else workspace.numel()
     c = out.c()
     _check(load().twell_decode_fwd(_dt(x), _ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), dm,
@@ -298,8 +436,18 @@ def decode_fwd(x, wg_t, wu_t, wd, width=TILE_C, out: Twell | None = None, y=None
 
 def to_hybrid(tw: Twell, K, max_ovf, out: Hybrid | None = None, status=None,
               timing: KernelTimer | None = None) -> Hybrid:
+    if not isinstance(tw, Twell):
+        raise TwellError("expected a Twell")
+    _check_twell(tw, tw.T, tw.val.dtype)
+    _dt(tw.val)
     if out is None:
         out = empty_hybrid(tw.T, tw.d_ff, K, max_ovf, tw.val.dtype, tw.val.device)
+    _check_hybrid(out, tw.T, tw.val.dtype)
+    if (out.K, out.max_ovf, out.d_ff) != (K, max_ovf, tw.d_ff):
+        raise TwellError(f"out: (K, max_ovf, d_ff) = {(out.K, out.max_ovf, out.d_ff)}, "
+                         f"expected {(K, max_ovf, tw.d_ff)}")
+    dev = _on_gpu(*_twell_tensors(tw), *_hybrid_tensors(out), ("status", status))
+    _status(status, dev)
     ct, ch = tw.c(), out.c()
     _check(load().twell_to_hybrid(ctypes.byref(ct), ctypes.byref(ch), _ptr(status),
                                   _timing(timing), _stream(tw.val.device)), "twell_to_hybrid")
@@ -313,12 +461,18 @@ def hybrid_fwd_workspace_bytes(dtype, T, d_model, d_ff, K, max_ovf) -> int:
 def hybrid_fwd(x, hy: Hybrid, wu_t, wd, y=None, workspace=None, status=None,
                timing: KernelTimer | None = None):
     """Training forward over a hybrid; returns y (float32)."""
-    T, dm = x.shape
+    T, dm = _x2(x)
+    _req(x, "x", (T, dm), x.dtype)
+    _check_hybrid(hy, T, x.dtype)
+    _check_weights(hy.d_ff, dm, x.dtype, wu_t=wu_t, wd=wd)
     if y is None:
         y = torch.empty((T, dm), dtype=torch.float32, device=x.device)
+    _req(y, "y", (T, dm), torch.float32)
+    dev = _on_gpu(("x", x), *_hybrid_tensors(hy), ("wu_t", wu_t), ("wd", wd), ("y", y),
+                  ("status", status), ("workspace", workspace))
+    _status(status, dev)
     need = hybrid_fwd_workspace_bytes(_dt(x), T, dm, hy.d_ff, hy.K, hy.max_ovf)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _ws(workspace, need, dev)
     nbytes = 0 if workspace is None else workspace.numel()
     ch = hy.c()
     _check(load().hybrid_ffn_fwd(_dt(x), _ptr(x), ctypes.byref(ch), _ptr(wu_t), _ptr(wd), dm,
@@ -335,18 +489,30 @@ def ffn_bwd(x, dy, hy: Hybrid, wg_t, wu_t, wd, out=None, workspace=None, status=
             timing: KernelTimer | None = None, l1: float = 0.0):
     """Returns (dx, dwg_t, dwu_t, dwd), all float32; l1 weights an activation
     penalty l1 * sum(h) whose gradient is included."""
-    T, dm = x.shape
-    d_ff = wg_t.shape[0]
+    T, dm = _x2(x)
+    _req(x, "x", (T, dm), x.dtype)
+    _req(dy, "dy", (T, dm), x.dtype)
+    _check_hybrid(hy, T, x.dtype)
+    d_ff = hy.d_ff
+    _check_weights(d_ff, dm, x.dtype, wg_t=wg_t, wu_t=wu_t, wd=wd)
     if out is None:
         f = dict(dtype=torch.float32, device=x.device)
         out = (torch.empty((T, dm), **f), torch.empty((d_ff, dm), **f),
                torch.empty((d_ff, dm), **f), torch.empty((d_ff, dm), **f))
+    if len(out) != 4:
+        raise TwellError("out: expected (dx, dwg_t, dwu_t, dwd)")
+    dx, dwg, dwu, dwd = out
+    _req(dx, "dx", (T, dm), torch.float32)
+    for name, t in (("dwg_t", dwg), ("dwu_t", dwu), ("dwd", dwd)):
+        _req(t, name, (d_ff, dm), torch.float32)
+    dev = _on_gpu(("x", x), ("dy", dy), *_hybrid_tensors(hy), ("wg_t", wg_t), ("wu_t", wu_t),
+                  ("wd", wd), ("dx", dx), ("dwg_t", dwg), ("dwu_t", dwu), ("dwd", dwd),
+                  ("status", status), ("workspace", workspace))
+    _status(status, dev)
     need = bwd_workspace_bytes(_dt(x), T, dm, d_ff, hy.K, hy.max_ovf)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _ws(workspace, need, dev)
     nbytes = 0 if workspace is None else workspace.numel()
     ch = hy.c()
-    dx, dwg, dwu, dwd = out
     _check(load().hybrid_ffn_bwd(_dt(x), _ptr(x), _ptr(dy), ctypes.byref(ch), _ptr(wg_t),
                                  _ptr(wu_t), _ptr(wd), dm, float(l1), _ptr(dx), _ptr(dwg),
                                  _ptr(dwu),

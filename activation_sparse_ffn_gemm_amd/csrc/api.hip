@@ -68,6 +68,10 @@ int check_hybrid(const hybrid_t *h, twell_dtype dt)
         return TWELL_E_DTYPE;
     if (h->T < 0 || h->K < 1 || h->K > h->d_ff || h->K > 32767 || h->max_ovf < 0)
         return TWELL_E_SHAPE;
+    // ELL slots are numbered t * K + s in 32-bit integers (the backward's
+    // transpose of the pattern)
+    if ((int64_t)h->T * h->K > INT32_MAX)
+        return TWELL_E_SHAPE;
     if (int rc = check_dff(h->d_ff))
         return rc;
     if (!h->n_ovf)
@@ -262,7 +266,8 @@ int hybrid_ffn_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void 
 size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                   int32_t K, int32_t max_ovf)
 {
-    if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
+    if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0 ||
+        (int64_t)T * K > INT32_MAX)
         return 0;
     return bwd_workspace_layout(dt, T, d_model, d_ff, K, max_ovf);
 }

@@ -114,7 +114,9 @@ typedef struct {
  * Hybrid ELL + dense backup (section 2.B.3 of the summary page: rows with few
  * nonzeros in a compact ELL matrix, overflow rows redirected to a dense
  * backup). A row with row_nnz <= K is an ELL row; any other row is an
- * overflow row and goes whole to the backup.
+ * overflow row and goes whole to the backup. 1 <= K <= min(d_ff, 32767) and
+ * T * K <= 2^31 - 1 (ELL slots are numbered in 32-bit integers); calls given
+ * a larger hybrid return TWELL_E_SHAPE.
  *   row_nnz  [T] int32: stored entries of the row (sum over tiles of
  *                       min(count, width))
  *   row_slot [T] int32: -1 for an ELL row, else the row's backup slot; slots

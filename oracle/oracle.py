@@ -46,6 +46,7 @@ def load(path: str) -> ctypes.CDLL:
     L.orc_bwd_hybrid.argtypes = [P, P, I, I, I, P, P, P, P, I, P, P, P, P, D, P, P, P, P]
     L.orc_bwd_dense.argtypes = [P, P, I, I, I, P, P, P, D, P, P, P, P]
     L.orc_num_threads.argtypes = []
+    L.orc_set_num_threads.argtypes = [I]
     _lib = L
     return L
 
@@ -72,6 +73,12 @@ def _p(a: np.ndarray):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not
+    depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def gate(x, wg_t) -> np.ndarray:

@@ -455,3 +455,10 @@ int orc_num_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Threads the parallel loops use from now on (n >= 1). Results do not depend
+ * on it (no reduction is split), only the time does. */
+void orc_set_num_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}

@@ -6,12 +6,24 @@ Comparison rules (tolerances as fixed for this layer):
   count equals the size of the stored set; columns ascend inside a tile.
 * bf16 inputs, fp32 accumulation: |gpu - ref| <= 2e-2 * (|ref| + 1e-2) for
   every element.
-* fp32 inputs, "1e-5 relative" read norm-wise over the compared array:
-  max |gpu - ref| <= 1e-5 * max |ref|. An element-wise relative bound cannot
-  hold in fp32: a d_model-term dot product accumulated in fp32 carries an
-  absolute error near sqrt(d_model) * 2^-24 * |partial sums| (about 1e-6
-  here), which exceeds 1e-5 * |ref| wherever the sum cancels towards zero.
+* fp32 inputs, "1e-5 relative", element by element against the size of the
+  terms that make up each element:
+      |gpu - ref| <= 1e-5 * (|ref| + mag)
+  where mag is the sum of the absolute values of every product that enters
+  the element (for g[t, i]: sum_k |x[t, k] wg_t[i, k]|; for y and the
+  gradients the same sum taken through every level of the computation). A
+  rounding error of fp32 accumulation is proportional to that sum, not to
+  |ref|, which can cancel towards zero; an element whose terms are all small
+  gets a small bound, whatever the rest of the array holds. mag is computed
+  in float64 by the oracle itself run on the absolute values of the inputs:
+  every output of the layer is a sum of products of inputs, so that run
+  returns exactly the sum of the absolute terms.
 * integer-valued inputs: bit-exact.
+
+Padding: the layouts leave slots past a (row, tile)'s count, ELL slots past a
+row's length and backup rows past n_ovf unspecified. Every upload here fills
+them with NaN values and in-range columns or rows, so a kernel that used one
+would turn its output into NaN or a wrong sum, not into a silent exact zero.
 """
 from __future__ import annotations
 
@@ -38,13 +50,27 @@ def tdtype(dtype: str):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
-def assert_close(gpu, ref, dtype: str, what: str = ""):
-    gpu, ref = f64(gpu), f64(ref)
-    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+def tolerance(ref, dtype: str, mag=None, extra=None) -> np.ndarray:
+    """Per-element bound on |gpu - ref| (rules in the module docstring). mag:
+    the elements' sums of absolute terms (required for fp32); extra: an
+    allowance added for entries a test knows to be ambiguous."""
+    ref = f64(ref)
     if dtype == "f32":
-        tol = np.full(ref.shape, TOL[dtype] * max(np.abs(ref).max(initial=0.0), 1e-30))
+        assert mag is not None, "fp32 comparisons need the sums of absolute terms"
+        mag = f64(mag)
+        assert mag.shape == ref.shape
+        tol = TOL[dtype] * (np.abs(ref) + mag)
     else:
         tol = TOL[dtype] * (np.abs(ref) + 1e-2)
+    if extra is not None:
+        tol = tol + f64(extra)
+    return tol
+
+
+def assert_close(gpu, ref, dtype: str, what: str = "", mag=None, extra=None):
+    gpu, ref = f64(gpu), f64(ref)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    tol = tolerance(ref, dtype, mag, extra)
     err = np.abs(gpu - ref)
     bad = ~(err <= tol)
     if bad.any():
@@ -67,8 +93,10 @@ def twell_dense(count, col, val, d_ff: int):
     return H, M
 
 
-def assert_twell_matches(tw_gpu, g_ref: np.ndarray, dtype: str, W: int, exact: bool = False):
-    """GPU TwELL (torch tensors) against the oracle's pre-activations."""
+def assert_twell_matches(tw_gpu, g_ref: np.ndarray, dtype: str, W: int, exact: bool = False,
+                         g_mag=None):
+    """GPU TwELL (torch tensors) against the oracle's pre-activations; g_mag:
+    the gate's sums of absolute terms (gate_mag), needed for fp32 values."""
     count = tw_gpu.count.cpu().numpy()
     col = tw_gpu.col.cpu().numpy()
     val = tw_gpu.val.cpu()
@@ -98,20 +126,112 @@ def assert_twell_matches(tw_gpu, g_ref: np.ndarray, dtype: str, W: int, exact: b
             amb = np.abs(g_ref[diff])
             assert np.all(amb < BAND), f"pattern mismatch outside the ambiguity band: {amb.max()}"
         both = M & Mref
-        assert_close(H[both], g_ref[both], dtype, "TwELL values")
+        assert_close(H[both], g_ref[both], dtype, "TwELL values",
+                     mag=None if g_mag is None else f64(g_mag)[both])
 
 
-def oracle_twell_for_gpu(orc, g_ref, W: int, dtype: str, device):
+def poison_cols(shape, d_ff: int, seed: int = 99) -> np.ndarray:
+    """In-range column indices for padding slots (seeded)."""
+    return np.random.default_rng(seed).integers(0, d_ff, shape)
+
+
+def oracle_twell_for_gpu(orc, g_ref, W: int, dtype: str, device, poison: bool = True):
     """Oracle TwELL with values rounded to the storage dtype, as numpy and as
-    device tensors (int32 counts, int16 columns)."""
+    device tensors (int32 counts, int16 columns). Padding slots (at or past
+    min(count, W)) carry NaN values and in-range columns unless poison is
+    False."""
     tw = orc.twell_pack(g_ref, W=W)
-    val_s = to_storage(tw["val"], dtype)
     tw_r = dict(tw)
-    tw_r["val"] = f64(val_s)
-    col = np.where(tw["col"] < 0, 0, tw["col"]).astype(np.int16)
-    dev = (torch.from_numpy(tw["count"]).to(device), torch.from_numpy(col).to(device),
-           val_s.to(device))
+    tw_r["val"] = f64(to_storage(tw["val"], dtype))
+    T, nt = tw["count"].shape
+    pad = np.arange(W)[None, None, :] >= np.minimum(tw["count"], W)[:, :, None]
+    col = tw["col"].copy()
+    val = tw_r["val"].copy()
+    if poison:
+        col[pad] = poison_cols(col.shape, nt * 128)[pad]
+        val[pad] = np.nan
+    else:
+        col[pad] = 0
+        val[pad] = 0.0
+    dev = (torch.from_numpy(tw["count"]).to(device),
+           torch.from_numpy(col.astype(np.int16)).to(device),
+           to_storage(val, dtype).to(device))
     return tw_r, dev
+
+
+def poisoned_twell(tw_mod, T: int, d_ff: int, W: int, dtype, device):
+    """An empty TwELL for a GPU call to fill: counts 0, every slot NaN with an
+    in-range column; the call must overwrite what it defines and nothing it
+    leaves unspecified may matter downstream."""
+    nt = d_ff // 128
+    col = torch.from_numpy(poison_cols((T, nt, W), d_ff).astype(np.int16)).to(device)
+    val = torch.full((T, nt, W), float("nan"), dtype=dtype, device=device)
+    return tw_mod.Twell(torch.zeros((T, nt), dtype=torch.int32, device=device), col, val)
+
+
+def poisoned_hybrid(tw_mod, T: int, d_ff: int, K: int, max_ovf: int, dtype, device):
+    """An empty hybrid for twell_to_hybrid to fill, every unspecified part
+    poisoned: ELL values NaN with in-range columns, backup rows NaN, backup
+    row ids in range."""
+    col = torch.from_numpy(poison_cols((T, K), d_ff, 98).astype(np.int16)).to(device)
+    return tw_mod.Hybrid(
+        torch.zeros(T, dtype=torch.int32, device=device),
+        torch.zeros(T, dtype=torch.int32, device=device), col,
+        torch.full((T, K), float("nan"), dtype=dtype, device=device),
+        torch.from_numpy(np.random.default_rng(97).integers(0, max(T, 1), max_ovf)
+                         .astype(np.int32)).to(device),
+        torch.full((max_ovf, d_ff), float("nan"), dtype=dtype, device=device),
+        torch.zeros(1, dtype=torch.int32, device=device))
+
+
+# ---- sums of absolute terms (the fp32 rule's mag), from the oracle itself
+def gate_mag(orc, x, wg_t) -> np.ndarray:
+    """sum_k |x[t, k] wg_t[i, k]| for every (t, i)."""
+    return orc.gate(np.abs(f64(x)), np.abs(f64(wg_t)))
+
+
+def ffn_twell_mag(orc, x, tw: dict, wu_t, wd) -> np.ndarray:
+    """The fused forward's sums of absolute terms over a TwELL's entries."""
+    ta = dict(tw)
+    ta["val"] = np.abs(f64(tw["val"]))
+    return orc.ffn_twell(np.abs(f64(x)), ta, np.abs(f64(wu_t)), np.abs(f64(wd)))
+
+
+def hybrid_abs(hy: dict) -> dict:
+    ha = dict(hy)
+    ha["ell_val"] = np.abs(f64(hy["ell_val"]))
+    ha["dense"] = np.abs(f64(hy["dense"]))
+    return ha
+
+
+def ffn_hybrid_mag(orc, x, hy: dict, wu_t, wd) -> np.ndarray:
+    return orc.ffn_hybrid(np.abs(f64(x)), hybrid_abs(hy), np.abs(f64(wu_t)), np.abs(f64(wd)))
+
+
+def bwd_hybrid_mag(orc, x, dy, hy: dict, wg_t, wu_t, wd, l1: float = 0.0):
+    """(dx, dwg_t, dwu_t, dwd) sums of absolute terms on a hybrid's pattern."""
+    A = lambda a: np.abs(f64(a))
+    return orc.bwd_hybrid(A(x), A(dy), hybrid_abs(hy), A(wg_t), A(wu_t), A(wd), l1=abs(l1))
+
+
+def forward_e2e_bounds(orc, x, wg_t, wu_t, wd, W: int):
+    """Bounds for y of the GPU's own gate + pack + forward against the oracle's
+    forward over the oracle's TwELL (W slots). Returns (mag, extra):
+      mag   the forward's sums of absolute terms with each stored h replaced
+            by its gate's sum of absolute terms (which bounds h and the
+            rounding of h on the GPU);
+      extra for entries whose pre-activation lies in the |g| < 1e-3 band (the
+            GPU may store them or not): sum over such entries of
+            2e-3 * sum_k |x wu_t| * |wd|, what storing one can add."""
+    g = orc.gate(f64(x), f64(wg_t))
+    gm = gate_mag(orc, x, wg_t)
+    tw = orc.twell_pack(g, W=W)
+    tm = orc.twell_pack(np.where(g > 0, gm, 0.0), W=W)  # same pattern, val = mag
+    mag = ffn_twell_mag(orc, x, tm, wu_t, wd)
+    band = orc.twell_pack(np.where(np.abs(g) < BAND, 2 * BAND, 0.0), W=128)
+    extra = ffn_twell_mag(orc, x, band, wu_t, wd)
+    assert np.array_equal(tm["count"], tw["count"])
+    return mag, extra
 
 
 def hybrid_to_numpy(hy) -> dict:

@@ -178,3 +178,89 @@ def test_few_token_ffn_workspace(L):
     """twell_ffn_fwd on few tokens keeps one float per TwELL slot."""
     for T, dff, W in ((1, 6144, 32), (64, 256, 128), (7, 1024, 8)):
         assert L.twell_fwd_workspace_bytes(tw.TWELL_BF16, T, 2304, dff, W) == T * (dff // 128) * W * 4
+
+
+def test_bwd_rejects_32bit_slot_overflow(L):
+    """T * K past 2^31 - 1 (ELL slot numbers are 32-bit) is refused on the host."""
+    big = hybrid_c(T=1 << 20, d_ff=4096, K=4096)   # 2^32 slots
+    assert L.hybrid_bwd_workspace_bytes(tw.TWELL_BF16, 1 << 20, 64, 4096, 4096, 4) == 0
+    assert L.hybrid_ffn_bwd(tw.TWELL_BF16, FAKE, FAKE, ctypes.byref(big), FAKE, FAKE, FAKE, 64,
+                            0.0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None, None, None) == -2
+    assert L.twell_to_hybrid(ctypes.byref(twell_c(T=1 << 20, d_ff=4096)), ctypes.byref(big),
+                             None, None, None) == -2
+
+
+# ---- the Python wrappers check every tensor before the C-ABI sees a pointer.
+# Host tensors are enough here: shape, dtype and layout are checked first, and
+# a well-formed call on host tensors is refused for its device, so no call
+# ever reaches the library.
+import torch  # noqa: E402
+
+BF = torch.bfloat16
+
+
+def _t(*shape, dtype=BF):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _raises(match, fn, *a, **k):
+    with pytest.raises(tw.TwellError, match=match):
+        fn(*a, **k)
+
+
+def test_wrapper_gate_pack_checks():
+    x, wg = _t(8, 64), _t(256, 64)
+    _raises("wg_t: shape", tw.gate_pack, x, _t(256, 128))
+    _raises("wg_t: dtype", tw.gate_pack, x, _t(256, 64, dtype=torch.float32))
+    _raises("contiguous", tw.gate_pack, x, _t(64, 256).t())          # a transposed view
+    _raises("x: expected", tw.gate_pack, _t(8), wg)
+    out = tw.empty_twell(9, 256, 32, BF, "cpu")
+    _raises("twell.count: shape", tw.gate_pack, x, wg, out=out)      # T mismatch
+    out = tw.empty_twell(8, 384, 32, BF, "cpu")
+    _raises("d_ff", tw.gate_pack, x, wg, out=out)
+    _raises("GPU only", tw.gate_pack, x, wg)                         # right shapes, host memory
+
+
+def test_wrapper_ffn_fwd_checks():
+    x = _t(8, 64)
+    t = tw.empty_twell(8, 256, 32, BF, "cpu")
+    w = _t(256, 64)
+    _raises("wu_t: shape", tw.ffn_fwd, x, t, _t(128, 64), w)
+    _raises("wd: shape", tw.ffn_fwd, x, t, w, _t(256, 32))
+    _raises("y: shape", tw.ffn_fwd, x, t, w, w, y=torch.zeros(7, 64))
+    _raises("y: dtype", tw.ffn_fwd, x, t, w, w, y=_t(8, 64))
+    _raises("twell.val: dtype", tw.ffn_fwd, x,
+            tw.Twell(t.count, t.col, t.val.float()), w, w)
+    _raises("GPU only", tw.ffn_fwd, x, t, w, w)
+
+
+def test_wrapper_decode_checks():
+    x, w = _t(65, 64), _t(256, 64)
+    _raises("at most 64", tw.decode_fwd, x, w, w, w)
+    _raises("wu_t: shape", tw.decode_fwd, x[:4], w, _t(256, 128), w)
+    _raises("GPU only", tw.decode_fwd, x[:4].contiguous(), w, w, w)
+
+
+def test_wrapper_hybrid_checks():
+    T, dff, K, mo = 8, 256, 16, 4
+    t = tw.empty_twell(T, dff, 32, BF, "cpu")
+    hy = tw.empty_hybrid(T, dff, K, mo, BF, "cpu")
+    _raises("K, max_ovf", tw.to_hybrid, t, K + 1, mo, out=hy)
+    _raises("hybrid.ell_val: dtype", tw.to_hybrid, t, K, mo,
+            out=tw.Hybrid(hy.row_nnz, hy.row_slot, hy.ell_col, hy.ell_val.float(), hy.ovf_rows,
+                          hy.dense, hy.n_ovf))
+    _raises("GPU only", tw.to_hybrid, t, K, mo, out=hy)
+    x, w = _t(T, 64), _t(dff, 64)
+    _raises("wu_t: shape", tw.hybrid_fwd, x, hy, _t(dff, 128), w)
+    _raises("hybrid.row_nnz: shape", tw.hybrid_fwd, _t(T + 1, 64), hy, w, w)
+    _raises("GPU only", tw.hybrid_fwd, x, hy, w, w)
+    f = dict(dtype=torch.float32)
+    good = (torch.zeros(T, 64, **f),) + tuple(torch.zeros(dff, 64, **f) for _ in range(3))
+    _raises("dy: shape", tw.ffn_bwd, x, _t(T, 128), hy, w, w, w)
+    _raises("wg_t: shape", tw.ffn_bwd, x, x, hy, _t(dff + 128, 64), w, w)
+    _raises("dwd: shape", tw.ffn_bwd, x, x, hy, w, w, w,
+            out=good[:3] + (torch.zeros(dff, 32, **f),))
+    _raises("dx: dtype", tw.ffn_bwd, x, x, hy, w, w, w, out=(_t(T, 64),) + good[1:])
+    _raises("workspace", tw.ffn_bwd, x, x, hy, w, w, w, out=good,
+            workspace=torch.zeros(4, dtype=torch.float32))
+    _raises("GPU only", tw.ffn_bwd, x, x, hy, w, w, w, out=good)

@@ -11,7 +11,8 @@ import torch
 
 from activation_sparse_ffn_gemm_amd import _lib as tw
 from activation_sparse_ffn_gemm_amd import synth
-from helpers import assert_close, f64, oracle_twell_for_gpu, to_storage
+from helpers import (assert_close, bwd_hybrid_mag, f64, oracle_twell_for_gpu, poison_cols,
+                     poisoned_hybrid, poisoned_twell, to_storage)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -31,16 +32,28 @@ def oracle_hybrid(orc, d, dtype, K, max_ovf, rows=None):
 
 
 def upload_hybrid(ref: dict, dtype: str) -> tw.Hybrid:
+    """The oracle's hybrid on the GPU, its unspecified parts poisoned: ELL
+    slots past a row's length (all slots of backup rows) get NaN values and
+    in-range columns, backup rows past n_ovf NaN, their row ids in range."""
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    mo = ref["max_ovf"]
+    mo, T, K, dff = ref["max_ovf"], ref["row_nnz"].shape[0], ref["K"], ref["d_ff"]
+    ell_len = np.where(ref["row_slot"] < 0, ref["row_nnz"], 0)
+    pad = np.arange(K)[None, :] >= ell_len[:, None]
+    col = np.where(pad, poison_cols((T, K), dff, 96), ref["ell_col"]).astype(np.int16)
+    val = np.where(pad, np.nan, ref["ell_val"])
+    n = min(ref["n_ovf"], mo)
+    rows = ref["ovf_rows"][:mo].copy()
+    rows[n:] = np.random.default_rng(95).integers(0, max(T, 1), mo - n)
+    dense = ref["dense"][:mo].copy()
+    dense[n:] = np.nan
     return tw.Hybrid(
         torch.from_numpy(ref["row_nnz"].copy()).to(DEV),
         torch.from_numpy(ref["row_slot"].copy()).to(DEV),
-        torch.from_numpy(np.maximum(ref["ell_col"], 0).astype(np.int16)).to(DEV),
-        torch.from_numpy(ref["ell_val"]).to(tdt).to(DEV),
-        torch.from_numpy(ref["ovf_rows"][:mo].copy()).to(DEV) if mo else
+        torch.from_numpy(col).to(DEV),
+        torch.from_numpy(val).to(tdt).to(DEV),
+        torch.from_numpy(rows.astype(np.int32)).to(DEV) if mo else
         torch.zeros(0, dtype=torch.int32, device=DEV),
-        torch.from_numpy(ref["dense"][:mo]).to(tdt).to(DEV).reshape(mo, ref["d_ff"]),
+        torch.from_numpy(dense).to(tdt).to(DEV).reshape(mo, dff),
         torch.tensor([ref["n_ovf"]], dtype=torch.int32, device=DEV))
 
 
@@ -95,8 +108,9 @@ def test_bwd_gaussian(orc, w):
     ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
     got = run_bwd(d, upload_hybrid(ref, w.dtype), w.dtype)
     want = oracle_bwd(orc, d, ref)
-    for n, a, b in zip(NAMES, got, want):
-        assert_close(a, b, w.dtype, n)
+    mags = bwd_hybrid_mag(orc, d["x"], d["dy"], ref, d["wg_t"], d["wu_t"], d["wd"])
+    for n, a, b, m in zip(NAMES, got, want, mags):
+        assert_close(a, b, w.dtype, n, mag=m)
 
 
 def test_bwd_training_layer_full(orc):
@@ -153,8 +167,8 @@ def test_backward_end_to_end_integer(orc):
     d = synth.make_integer_inputs(384, 256, 768, "bf16", 0.02, with_dy=True, skew_rows=19)
     ref = oracle_hybrid(orc, d, "bf16", 48, 32)
     x, wg = d["x"].to(DEV), d["wg_t"].to(DEV)
-    t = tw.gate_pack(x, wg)
-    hy = tw.to_hybrid(t, 48, 32)
+    t = tw.gate_pack(x, wg, out=poisoned_twell(tw, 384, 768, 128, torch.bfloat16, DEV))
+    hy = tw.to_hybrid(t, 48, 32, out=poisoned_hybrid(tw, 384, 768, 48, 32, torch.bfloat16, DEV))
     got = run_bwd(d, hy, "bf16")
     for n, a, b in zip(NAMES, got, oracle_bwd(orc, d, ref)):
         assert np.array_equal(f64(a), b), n

@@ -1,5 +1,5 @@
-"""GPU parity of twell_decode_fwd (the whole layer for few tokens in one
-cooperative launch) against the oracle, through the C-ABI: its TwELL output
+"""GPU parity of twell_decode_fwd (the whole layer for few tokens in one call:
+three launches) against the oracle, through the C-ABI: its TwELL output
 against the oracle's pre-activations, its y against the oracle's forward."""
 import numpy as np
 import pytest
@@ -7,7 +7,8 @@ import torch
 
 from activation_sparse_ffn_gemm_amd import _lib as tw
 from activation_sparse_ffn_gemm_amd import synth
-from helpers import assert_close, assert_twell_matches, f64, oracle_twell_for_gpu
+from helpers import (assert_close, assert_twell_matches, f64, forward_e2e_bounds, gate_mag,
+                     oracle_twell_for_gpu, poisoned_twell)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -20,7 +21,8 @@ def announce(*a):
 def run_decode(d, width, status_ok=True):
     x, wg, wu, wd = (d[k].to(DEV) for k in ("x", "wg_t", "wu_t", "wd"))
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out, y = tw.decode_fwd(x, wg, wu, wd, width=width, status=st)
+    out, y = tw.decode_fwd(x, wg, wu, wd, width=width, status=st,
+                           out=poisoned_twell(tw, x.shape[0], wg.shape[0], width, x.dtype, DEV))
     torch.cuda.synchronize()
     if status_ok:
         assert int(st.item()) == 0
@@ -61,8 +63,12 @@ def test_decode_gaussian(orc, w):
     d = synth.make_inputs(w)
     g, y_ref = oracle_forward(orc, d, w.dtype, w.width)
     out, y, _ = run_decode(d, w.width)
-    assert_twell_matches(out, g, w.dtype, w.width)
-    assert_close(y, y_ref, w.dtype, "y")
+    f32 = w.dtype == "f32"
+    assert_twell_matches(out, g, w.dtype, w.width,
+                         g_mag=gate_mag(orc, d["x"], d["wg_t"]) if f32 else None)
+    mag, extra = (forward_e2e_bounds(orc, d["x"], d["wg_t"], d["wu_t"], d["wd"], w.width)
+                  if f32 else (None, None))
+    assert_close(y, y_ref, w.dtype, "y", mag=mag, extra=extra)
 
 
 def test_decode_agrees_with_two_calls():

@@ -7,7 +7,8 @@ import torch
 from activation_sparse_ffn_gemm_amd import _lib as tw
 from activation_sparse_ffn_gemm_amd import synth
 from helpers import (assert_close, assert_hybrid_equal, assert_twell_matches, f64,
-                     hybrid_to_numpy, oracle_twell_for_gpu, to_storage)
+                     ffn_twell_mag, forward_e2e_bounds, gate_mag, hybrid_to_numpy,
+                     oracle_twell_for_gpu, poisoned_hybrid, poisoned_twell, to_storage)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -61,7 +62,7 @@ def test_gate_pack_gaussian(orc, w):
     out = tw.gate_pack(x, wg, width=w.width, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    assert_twell_matches(out, g, w.dtype, w.width)
+    assert_twell_matches(out, g, w.dtype, w.width, g_mag=gate_mag(orc, d["x"], d["wg_t"]))
 
 
 def test_gate_pack_1p5b_sampled_rows(orc):
@@ -143,7 +144,7 @@ def _fwd_on_oracle_twell(orc, d, dtype, W):
     x, wu, wd = upload(d, ("x", "wu_t", "wd"))
     y = tw.ffn_fwd(x, tw.Twell(cnt, col, val), wu, wd)
     torch.cuda.synchronize()
-    return y, y_ref, g
+    return y, y_ref, g, tw_r
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -158,7 +159,7 @@ def test_ffn_fwd_integer_exact(orc, dtype, T, dm, dff):
         pytest.skip("fp32 limit is d_model <= 2048")
     announce("ffn_fwd int", dtype, T, dm, dff)
     d = synth.make_integer_inputs(T, dm, dff, dtype, 0.05)
-    y, y_ref, _ = _fwd_on_oracle_twell(orc, d, dtype, 128)
+    y, y_ref, _, _ = _fwd_on_oracle_twell(orc, d, dtype, 128)
     assert np.array_equal(f64(y), y_ref)
 
 
@@ -172,7 +173,7 @@ def test_ffn_fwd_narrow_width_exact(orc, dtype, T, dm, dff, W):
     tile, which must never be used. 1029 tokens take the two-pass path."""
     announce("ffn_fwd narrow W", dtype, T, dm, dff, W)
     d = synth.make_integer_inputs(T, dm, dff, dtype, 0.05)
-    y, y_ref, g = _fwd_on_oracle_twell(orc, d, dtype, W)
+    y, y_ref, g, _ = _fwd_on_oracle_twell(orc, d, dtype, W)
     assert orc.twell_pack(g, W=W)["overflow"]
     assert np.array_equal(f64(y), y_ref)
 
@@ -182,8 +183,8 @@ def test_ffn_fwd_narrow_width_exact(orc, dtype, T, dm, dff, W):
 def test_ffn_fwd_on_oracle_twell(orc, w):
     announce("ffn_fwd on oracle TwELL", w.name, w.T)
     d = synth.make_inputs(w)
-    y, y_ref, _ = _fwd_on_oracle_twell(orc, d, w.dtype, w.width)
-    assert_close(y, y_ref, w.dtype, "y")
+    y, y_ref, _, tw_r = _fwd_on_oracle_twell(orc, d, w.dtype, w.width)
+    assert_close(y, y_ref, w.dtype, "y", mag=ffn_twell_mag(orc, d["x"], tw_r, d["wu_t"], d["wd"]))
 
 
 @pytest.mark.parametrize("T", [8, 300])
@@ -213,11 +214,14 @@ def test_forward_end_to_end(orc, w):
     y_ref = orc.ffn_twell(x64, tw_r, f64(d["wu_t"]), f64(d["wd"]))
     x, wg, wu, wd = upload(d)
     st = status_word()
-    t = tw.gate_pack(x, wg, width=w.width, status=st)
+    t = tw.gate_pack(x, wg, width=w.width, status=st,
+                     out=poisoned_twell(tw, w.T, w.d_ff, w.width, x.dtype, DEV))
     y = tw.ffn_fwd(x, t, wu, wd, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    assert_close(y, y_ref, w.dtype, "y")
+    mag, extra = (forward_e2e_bounds(orc, d["x"], d["wg_t"], d["wu_t"], d["wd"], w.width)
+                  if w.dtype == "f32" else (None, None))
+    assert_close(y, y_ref, w.dtype, "y", mag=mag, extra=extra)
 
 
 def test_forward_1p5b_sweep_sampled(orc):
@@ -230,7 +234,8 @@ def test_forward_1p5b_sweep_sampled(orc):
         d = synth.make_inputs(w)
         x, wg, wu, wd = upload(d)
         st = status_word()
-        t = tw.gate_pack(x, wg, width=w.width, status=st)
+        t = tw.gate_pack(x, wg, width=w.width, status=st,
+                         out=poisoned_twell(tw, w.T, w.d_ff, w.width, x.dtype, DEV))
         y = tw.ffn_fwd(x, t, wu, wd)
         torch.cuda.synchronize()
         assert int(st.item()) == 0
@@ -255,7 +260,8 @@ def test_to_hybrid_on_oracle_twell_exact(orc, dtype):
         tw_r, (cnt, col, val) = oracle_twell_for_gpu(orc, g, 128, dtype, DEV)
         ref = orc.to_hybrid(tw_r, K, max_ovf)
         st = status_word()
-        hy = tw.to_hybrid(tw.Twell(cnt, col, val), K, max_ovf, status=st)
+        hy = tw.to_hybrid(tw.Twell(cnt, col, val), K, max_ovf, status=st,
+                          out=poisoned_hybrid(tw, 300, 640, K, max_ovf, val.dtype, DEV))
         torch.cuda.synchronize()
         assert bool(int(st.item()) & tw.DEV_OVF_CAPACITY) == ref["capacity_exceeded"]
         assert_hybrid_equal(hybrid_to_numpy(hy), ref)
@@ -288,8 +294,8 @@ def test_to_hybrid_end_to_end_integer(orc):
     tw_r, _ = oracle_twell_for_gpu(orc, g, 128, "bf16", "cpu")
     ref = orc.to_hybrid(tw_r, 40, 32)
     x, wg = upload(d, ("x", "wg_t"))
-    t = tw.gate_pack(x, wg)
-    hy = tw.to_hybrid(t, 40, 32)
+    t = tw.gate_pack(x, wg, out=poisoned_twell(tw, 257, 512, 128, x.dtype, DEV))
+    hy = tw.to_hybrid(t, 40, 32, out=poisoned_hybrid(tw, 257, 512, 40, 32, x.dtype, DEV))
     torch.cuda.synchronize()
     assert_hybrid_equal(hybrid_to_numpy(hy), ref)
     assert ref["n_ovf"] == 13

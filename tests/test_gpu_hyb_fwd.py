@@ -10,7 +10,7 @@ import torch
 
 from activation_sparse_ffn_gemm_amd import _lib as tw
 from activation_sparse_ffn_gemm_amd import synth
-from helpers import assert_close, f64
+from helpers import assert_close, f64, ffn_hybrid_mag, poisoned_hybrid, poisoned_twell
 from test_gpu_bwd import oracle_hybrid, upload_hybrid
 
 pytestmark = pytest.mark.gpu
@@ -62,7 +62,9 @@ def test_hybrid_fwd_gaussian(orc, w):
     d = synth.make_inputs(w)
     ref = oracle_hybrid(orc, d, w.dtype, w.K, w.max_ovf)
     y = run_fwd(d, upload_hybrid(ref, w.dtype))
-    assert_close(y, orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"])), w.dtype, "y")
+    mag = ffn_hybrid_mag(orc, d["x"], ref, d["wu_t"], d["wd"])
+    assert_close(y, orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"])), w.dtype, "y",
+                 mag=mag)
 
 
 def test_hybrid_fwd_training_layer_full(orc):
@@ -86,9 +88,11 @@ def test_hybrid_fwd_agrees_with_twell_fwd():
     d = synth.make_inputs(w)
     x, wg, wu, wd = (d[k].to(DEV) for k in ("x", "wg_t", "wu_t", "wd"))
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
-    t = tw.gate_pack(x, wg, width=w.width, status=st)
+    t = tw.gate_pack(x, wg, width=w.width, status=st,
+                     out=poisoned_twell(tw, w.T, w.d_ff, w.width, torch.bfloat16, DEV))
     y_tw = tw.ffn_fwd(x, t, wu, wd, status=st)
-    hy = tw.to_hybrid(t, w.K, w.max_ovf, status=st)
+    hy = tw.to_hybrid(t, w.K, w.max_ovf, status=st,
+                      out=poisoned_hybrid(tw, w.T, w.d_ff, w.K, w.max_ovf, torch.bfloat16, DEV))
     y_hy = tw.hybrid_fwd(x, hy, wu, wd, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and int(hy.n_ovf.item()) > 0
