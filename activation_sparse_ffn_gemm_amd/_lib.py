@@ -24,7 +24,8 @@ DEV_TILE_OVERFLOW, DEV_OVF_CAPACITY, DEV_BAD_INDEX = 1, 2, 4
 EXPORTS = ("twell_gate_pack", "twell_gate_workspace_bytes", "twell_ffn_fwd", "twell_fwd_workspace_bytes", "twell_decode_fwd",
            "twell_decode_workspace_bytes", "twell_to_hybrid", "hybrid_ffn_fwd",
            "hybrid_fwd_workspace_bytes", "hybrid_ffn_bwd", "hybrid_bwd_workspace_bytes",
-           "twell_status_str")
+           "twell_status_str", "twell_decode_fwd_noalloc")
+STATIC_SCRATCH_BYTES = 12 << 20  # twell_decode_fwd_noalloc's scratch per GPU
 DECODE_T = 64  # most tokens twell_decode_fwd takes (few-token kernels up to here)
 
 c_i32, c_sz, c_p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
@@ -108,6 +109,8 @@ def load() -> ctypes.CDLL:
     L.twell_fwd_workspace_bytes.restype = S
     L.twell_decode_fwd.argtypes = [ctypes.c_int, P, P, P, P, I, ctypes.POINTER(TwellC), P, P,
                                    S, P, P, P]
+    L.twell_decode_fwd_noalloc.argtypes = [ctypes.c_int, P, P, P, P, I,
+                                           ctypes.POINTER(TwellC), P, P, P, P]
     L.twell_decode_workspace_bytes.argtypes = [ctypes.c_int, I, I, I, I]
     L.twell_decode_workspace_bytes.restype = S
     L.twell_to_hybrid.argtypes = [ctypes.POINTER(TwellC), ctypes.POINTER(HybridC), P, P, P]
@@ -122,7 +125,7 @@ def load() -> ctypes.CDLL:
     L.twell_status_str.argtypes = [ctypes.c_int]
     L.twell_status_str.restype = ctypes.c_char_p
     for f in ("twell_gate_pack", "twell_ffn_fwd", "twell_decode_fwd", "twell_to_hybrid",
-              "hybrid_ffn_fwd", "hybrid_ffn_bwd"):
+              "hybrid_ffn_fwd", "hybrid_ffn_bwd", "twell_decode_fwd_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -431,6 +434,34 @@ def decode_fwd(x, wg_t, wu_t, wd, width=TILE_C, out: Twell | None = None, y=None
                                    ctypes.byref(c), _ptr(y), _ptr(workspace), nbytes,
                                    _ptr(status), _timing(timing), _stream(x.device)),
            "twell_decode_fwd")
+    return out, y
+
+
+def decode_fwd_noalloc(x, wg_t, wu_t, wd, out: Twell, y, status=None,
+                       timing: KernelTimer | None = None):
+    """decode_fwd for callers that cannot allocate: the caller passes the
+    outputs (out, y), the library's static per-GPU scratch replaces the
+    workspace, and nothing is allocated. Overlapping calls on one GPU race."""
+    T, dm = _x2(x)
+    _req(x, "x", (T, dm), x.dtype)
+    if not isinstance(wg_t, torch.Tensor) or wg_t.dim() != 2:
+        raise TwellError("wg_t: expected a [d_ff][d_model] tensor")
+    d_ff = wg_t.shape[0]
+    _check_weights(d_ff, dm, x.dtype, wg_t=wg_t, wu_t=wu_t, wd=wd)
+    if T > DECODE_T:
+        raise TwellError(f"decode_fwd_noalloc takes at most {DECODE_T} tokens, got {T}")
+    _check_twell(out, T, x.dtype)
+    if out.d_ff != d_ff:
+        raise TwellError(f"out: d_ff {out.d_ff}, wg_t has {d_ff} rows")
+    _req(y, "y", (T, dm), torch.float32)
+    dev = _on_gpu(("x", x), ("wg_t", wg_t), ("wu_t", wu_t), ("wd", wd), *_twell_tensors(out),
+                  ("y", y), ("status", status))
+    _status(status, dev)
+    c = out.c()
+    _check(load().twell_decode_fwd_noalloc(_dt(x), _ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), dm,
+                                           ctypes.byref(c), _ptr(y), _ptr(status),
+                                           _timing(timing), _stream(x.device)),
+           "twell_decode_fwd_noalloc")
     return out, y
 
 

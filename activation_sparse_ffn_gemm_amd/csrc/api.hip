@@ -87,6 +87,28 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_E_HIP; }
 
 } // namespace
 
+// Every argument check of twell_decode_fwd except the workspace's (shared
+// with twell_decode_fwd_noalloc, whose scratch is the library's own).
+int check_decode_args(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
+                      const void *wd, int32_t d_model, const twell_t *out, const float *y)
+{
+    if (!dtype_ok(dt))
+        return TWELL_E_DTYPE;
+    if (!wg_t || !wu_t || !wd || !out)
+        return TWELL_E_NULL;
+    if (int rc = check_twell(out, dt))
+        return rc;
+    if (out->T > 0 && (!x || !y))
+        return TWELL_E_NULL;
+    if (int rc = check_dm(dt, d_model))
+        return rc;
+    if (out->T > TWELL_DECODE_T)
+        return TWELL_E_SHAPE;
+    if (!a16(x) || !a16(wg_t) || !a16(wu_t) || !a16(wd) || !a16(y))
+        return TWELL_E_ALIGN;
+    return TWELL_OK;
+}
+
 extern "C" {
 
 const char *twell_status_str(int code)
@@ -99,6 +121,7 @@ const char *twell_status_str(int code)
     case TWELL_E_ALIGN: return "a pointer is not 16-byte aligned";
     case TWELL_E_WORKSPACE: return "workspace too small";
     case TWELL_E_HIP: return "HIP launch failed";
+    case TWELL_E_SCRATCH: return "the call needs more scratch than the static buffer holds";
     default: return "unknown status";
     }
 }
@@ -187,20 +210,8 @@ int twell_decode_fwd(twell_dtype dt, const void *x, const void *wg_t, const void
                      void *workspace, size_t workspace_bytes, int32_t *dev_status,
                      twell_timing_t *timing, void *stream)
 {
-    if (!dtype_ok(dt))
-        return TWELL_E_DTYPE;
-    if (!wg_t || !wu_t || !wd || !out)
-        return TWELL_E_NULL;
-    if (int rc = check_twell(out, dt))
+    if (int rc = check_decode_args(dt, x, wg_t, wu_t, wd, d_model, out, y))
         return rc;
-    if (out->T > 0 && (!x || !y))
-        return TWELL_E_NULL;
-    if (int rc = check_dm(dt, d_model))
-        return rc;
-    if (out->T > TWELL_DECODE_T)
-        return TWELL_E_SHAPE;
-    if (!a16(x) || !a16(wg_t) || !a16(wu_t) || !a16(wd) || !a16(y))
-        return TWELL_E_ALIGN;
     const size_t need =
         twell_decode_workspace_bytes(dt, out->T, d_model, out->d_ff, out->width);
     if (workspace_bytes < need || (need && !workspace))

@@ -60,7 +60,8 @@ enum {
     TWELL_E_DTYPE = -3,     /* unsupported element type */
     TWELL_E_ALIGN = -4,     /* a pointer is not 16-byte aligned */
     TWELL_E_WORKSPACE = -5, /* workspace smaller than the *_workspace_bytes figure */
-    TWELL_E_HIP = -6        /* the HIP runtime rejected a launch */
+    TWELL_E_HIP = -6,       /* the HIP runtime rejected a launch */
+    TWELL_E_SCRATCH = -7    /* more scratch needed than TWELL_STATIC_SCRATCH_BYTES */
 };
 
 /* device status bits */
@@ -204,6 +205,26 @@ int twell_decode_fwd(twell_dtype dt, const void *x, const void *wg_t, const void
 /* Workspace bytes twell_decode_fwd needs (0 on invalid arguments). */
 size_t twell_decode_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                     int32_t width);
+
+/*
+ * twell_decode_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, arguments and results, with the scratch taken from a
+ * static device array of TWELL_STATIC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends. Nothing is allocated,
+ * freed or synchronised. A call whose twell_decode_workspace_bytes(...)
+ * exceeds the array returns TWELL_E_SCRATCH and launches nothing: the 2B
+ * decode layer (d_model 2304, d_ff 6144) needs at most 9.4 MB for T <= 64,
+ * the largest shapes (d_model 4096, d_ff 32768, width 128) need 16 MiB.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from different threads) race and must be
+ * ordered by the caller.
+ * Errors: those of twell_decode_fwd except WORKSPACE, plus SCRATCH.
+ */
+#define TWELL_STATIC_SCRATCH_BYTES ((size_t)12 << 20)
+int twell_decode_fwd_noalloc(twell_dtype dt, const void *x, const void *wg_t, const void *wu_t,
+                             const void *wd, int32_t d_model, const twell_t *out, float *y,
+                             int32_t *dev_status, twell_timing_t *timing, void *stream);
 
 /*
  * TwELL -> hybrid conversion (section 2.B.3 of the summary page: a dedicated

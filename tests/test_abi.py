@@ -264,3 +264,22 @@ def test_wrapper_hybrid_checks():
     _raises("workspace", tw.ffn_bwd, x, x, hy, w, w, w, out=good,
             workspace=torch.zeros(4, dtype=torch.float32))
     _raises("GPU only", tw.ffn_bwd, x, x, hy, w, w, w, out=good)
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode call checks its arguments as twell_decode_fwd
+    does and refuses, on the host, a call needing more than the static
+    scratch."""
+    f = lambda tt, dm=64, y=FAKE, x=FAKE: L.twell_decode_fwd_noalloc(
+        tw.TWELL_BF16, x, FAKE, FAKE, FAKE, dm, ctypes.byref(tt), y, None, None, None)
+    assert f(twell_c(), y=0) == -1
+    assert f(twell_c(), dm=100) == -2
+    assert f(twell_c(T=65)) == -2
+    assert f(twell_c(), y=FAKE + 4) == -4
+    big = twell_c(T=64, d_ff=32768, width=128)
+    assert L.twell_decode_workspace_bytes(tw.TWELL_BF16, 64, 4096, 32768, 128) > tw.STATIC_SCRATCH_BYTES
+    for T in (1, 8, 32, 64):   # the 2B decode layer fits
+        assert L.twell_decode_workspace_bytes(tw.TWELL_BF16, T, 2304, 6144, 128) <= tw.STATIC_SCRATCH_BYTES
+    assert f(big, dm=4096) == -7
+    assert b"scratch" in L.twell_status_str(-7)
+    assert f(twell_c(T=0, ptr=0), x=0, y=0) == 0   # T == 0: nothing to do
