@@ -10,16 +10,21 @@
 // Backward, with u = x_O W_u and da = dy_O W_d^T:
 //   a = h_O u,  du = da h_O,  dg = da u + l1 where h_O != 0, else 0
 //   dx_O = du W_u^T + dg W_g^T
-//   dW_d += a^T dy_O,  dW_u += du^T x_O,  dW_g += dg^T x_O
+//   dW_d = a^T dy_O,  dW_u = du^T x_O,  dW_g = dg^T x_O  (the ELL rows' share
+//   is added by the neuron pass that runs after them)
 //
-// Every product runs on the NT main loop (both operands K-contiguous), so
-// operands whose contraction index is their row index get a transposed copy
-// first: W_u, W_g and W_d as [d_model][d_ff], x_O and dy_O as
-// [d_model][rows], and the intermediates a, du, dg are written by the u/da
-// epilogue both as [rows][d_ff] (for dx) and as [d_ff][rows] (for dW). For
-// bf16 inputs a float32 intermediate v is stored as two bf16, hi = bf16(v)
-// and lo = bf16(v - hi), and a product over it runs over both halves (about
-// 16 significant bits); float32 inputs keep one float32 array.
+// Every operand is read as it is stored. Products over K-contiguous rows
+// (u = x_O W_u and da = dy_O W_d^T: x, dy, wu_t and wd rows all run along
+// d_model) take the shared main loop; the others take its mixed-layout form
+// (ntgemm.hpp), which reads an operand stored with the contraction index as
+// its row index straight from that layout through gfx950's transposing LDS
+// reads: W_d in y_O = A W_d, W_u and W_g in dx_O, and both operands of the
+// dW products (a, du, dg as [rows][d_ff], and x_O, dy_O as [rows][d_model],
+// the latter gathered once by extra workgroups of the ELL masks launch). No
+// transposed copy of any weight or activation is made. For bf16 inputs a
+// float32 intermediate v is stored as two bf16, hi = bf16(v) and
+// lo = bf16(v - hi), and a product over it runs over both halves (about 16
+// significant bits); float32 inputs keep one float32 array.
 //
 // y_O and dx_O have few rows and a long K (d_ff, or 2-4 segments of it): K is
 // split over S workgroups per tile, each writing a float32 partial; the ELL
@@ -27,9 +32,8 @@
 // row's S partials in order and store the row (see BkPart).
 // Row counts are device values: workgroups whose rows all lie past n_ovf
 // return at once, and the grids are sized for the capacity max_ovf. Work
-// without an ordering between its parts shares a launch (the u/da tiles with
-// the transposes; the dx tiles with the dW tiles), so that a layer without
-// backup rows pays few launches.
+// without an ordering between its parts shares a launch (the dx tiles with
+// the dW tiles), so that a layer without backup rows pays few launches.
 #include "ntgemm.hpp"
 #include "backup.hpp"
 
@@ -40,22 +44,27 @@ namespace {
 // the split-K row x weight products and the dW products take 128-byte steps,
 // two resident (one barrier per four MFMA groups).
 using CU = ng::Cfg<128, 128, 2, 2>;
-using CW = ng::Cfg<128, 128, 2, 2, 2, 128>;
-static_assert(CU::NT == CW::NT && CU::LDS == CW::LDS, "the kernels size LDS and blocks once");
-constexpr int TILE = 128;
+// the split-K row x weight products and the dW products: 256 x 256 tiles,
+// eight waves of 128 x 64, 128-byte K steps, two resident (the gate's shape;
+// measured on the 1.5B skewed layer's products against 128 x 128 tiles of
+// four waves: y_O 49 -> 35 us, dx_O 71 -> 56 us, dW alike)
+using CW = ng::Cfg<256, 256, 2, 4, 2, 128>;
+constexpr int TILE = 128;  // u/da tiles
+constexpr int WT = 256;    // split-K and dW tiles
+
+template <int DT> using Store = typename elem<DT>::storage;
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
-int pad_rows(int max_ovf) { return (max_ovf + TILE - 1) / TILE * TILE; }
+int pad_rows(int max_ovf) { return (max_ovf + WT - 1) / WT * WT; }
 
-// K split of the y_O / dx_O products: a tile of 128 rows gives one
-// workgroup of four waves per CU far too little to overlap (about a third of
-// the MFMA rate, measured); aim at 2048 workgroups over the capacity's tiles
-// (several per CU when about half the capacity is used), at most 16 splits,
-// at least 16 K steps each.
+// K split of the y_O / dx_O products: few row tiles give one workgroup per
+// CU far too little to overlap; aim at 512 workgroups over the capacity's
+// tiles (two per CU when about half the capacity is used; tiles wholly past
+// n_ovf return at once), at most 16 splits, at least 16 K steps each.
 int split_k(int R, int dm, int nk)
 {
-    const int tiles = (R / TILE) * ((dm + TILE - 1) / TILE);
-    int S = std::max(1, 2048 / std::max(tiles, 1));
+    const int tiles = (R / WT) * ((dm + WT - 1) / WT);
+    int S = std::max(1, 512 / std::max(tiles, 1));
     S = std::min(S, 16);
     S = std::min(S, std::max(1, nk / 16));
     return S;
@@ -69,8 +78,7 @@ DEVI int n_rows(const int32_t *n_ovf_p, int max_ovf) { return min(*n_ovf_p, max_
 //   fwd (BWD = false): the groups sum the two halves of K of u; epilogue
 //                      A = h u -> a [R][dff] (hi, lo)
 //   bwd (BWD = true):  group 0 runs u = x_O W_u, group 1 da = dy_O W_d^T;
-//                      epilogue du, dg -> [R][dff] (hi, lo each) and
-//                      a, du, dg -> [dff][R] (hi, lo each)
+//                      epilogue a, du, dg -> [R][dff] (hi, lo each)
 // Each wave's sub-tile has two 32-row block rows (mi = 0, 1): group g runs
 // the epilogue of block row g, so the groups swap the other block row's
 // accumulators through LDS first (in the forward u = first half + second
@@ -90,14 +98,14 @@ template <int DT, bool BWD>
 DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                   const int32_t *__restrict__ ovf_rows, int n, const uint8_t *__restrict__ wu,
                   const uint8_t *__restrict__ wd, int dm, int dff, int R,
-                  const void *__restrict__ dense, float l1, void *__restrict__ inter,
-                  void *__restrict__ inter_t, int bx, int by, uint8_t *L)
+                  const void *__restrict__ dense, float l1, void *__restrict__ inter, int bx,
+                  int by, uint8_t *L)
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1; // arrays per intermediate
     constexpr int NI = CU::NI;
-    constexpr int P = TILE * esz + 16;          // row pitch (bytes) of the transposed tile in LDS
+    constexpr int P = TILE * esz + 16;          // row pitch (bytes) of a staged tile in LDS
     const int m0 = by * TILE, i0 = bx * TILE;
     if (m0 >= n)
         return;
@@ -182,17 +190,18 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     constexpr int PLANE = TILE * P;
     constexpr int CPR = TILE * esz / 16; // 16-byte chunks per tile row
     {
-        // A (fwd) or du and dg (bwd) as [R][dff] (planes hi, lo of each for
+        // A (fwd) or a, du and dg (bwd) as [R][dff] (planes hi, lo of each for
         // bf16): each plane's tile goes through LDS as [m][i], then the
         // workgroup stores it along i, 16 bytes per lane. QR planes per round.
-        constexpr int NR = (BWD ? 2 : 1) * NH;
-        constexpr int QR = ud_lds<DT>() / PLANE >= 2 ? 2 : 1;
+        constexpr int NR = (BWD ? 3 : 1) * NH;
+        constexpr int FIT = ud_lds<DT>() / PLANE;
+        constexpr int QR = FIT >= 3 && NR % 3 == 0 ? 3 : (FIT >= 2 && NR % 2 == 0 ? 2 : 1);
         static_assert(NR % QR == 0 && QR * PLANE <= ud_lds<DT>(), "LDS rounds");
 #pragma unroll 1
         for (int qb = 0; qb < NR; qb += QR) {
 #pragma unroll
             for (int qq = 0; qq < QR; ++qq) {
-                const int q = qb + qq, which = q / NH, part = q % NH; // bwd: du, dg
+                const int q = qb + qq, which = q / NH, part = q % NH; // bwd: a, du, dg
                 uint8_t *Lq = L + qq * PLANE;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
@@ -200,7 +209,9 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                     for (int e = 0; e < 16; ++e) {
                         const int r = ng::acc_row<CU>(wm, mi, e, lane);
                         const int c = ng::acc_col<CU>(wn, ni, lane);
-                        const float v = !BWD ? own[ni][e] : (which == 0 ? oth[ni][e] : hv[ni][e]);
+                        const float v = !BWD || which == 0
+                                            ? own[ni][e]
+                                            : (which == 1 ? oth[ni][e] : hv[ni][e]);
                         if constexpr (DT == TWELL_BF16) {
                             const uint16_t hi = f32_to_bf16(v);
                             *(uint16_t *)(Lq + r * P + c * 2) =
@@ -224,90 +235,39 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
             __syncthreads();
         }
     }
-    if constexpr (BWD) {
-        // Transposed copies [dff][R] of a, du, dg (hi and lo halves for bf16):
-        // each half goes through LDS as [i][m] (both groups' block rows), then
-        // the workgroup stores it along m, 16 bytes per lane. QB halves share
-        // one LDS round (three for bf16: two rounds instead of six).
-        constexpr int QB = ud_lds<DT>() / PLANE >= 3 ? 3 : 1;
-        static_assert((3 * NH) % QB == 0 && QB * PLANE <= ud_lds<DT>(), "LDS rounds");
-#pragma unroll 1
-        for (int qb = 0; qb < 3 * NH; qb += QB) {
-#pragma unroll
-            for (int qq = 0; qq < QB; ++qq) {
-                const int q = qb + qq; // (a, du, dg) x (hi, lo)
-                const int which = q / NH, part = q % NH;
-                uint8_t *Lq = L + qq * PLANE;
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) { // rows 8g + 4 half .. + 3: contiguous in m
-                        const int r = ng::acc_row<CU>(wm, mi, 4 * g, lane);
-                        const int c = ng::acc_col<CU>(wn, ni, lane);
-                        uint8_t *dst = Lq + c * P + r * esz;
-                        float v[4];
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const int e = 4 * g + k;
-                            v[k] = which == 0 ? own[ni][e] : (which == 1 ? oth[ni][e] : hv[ni][e]);
-                        }
-                        if constexpr (DT == TWELL_BF16) {
-                            uint16_t hw[4];
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                const uint16_t hi = f32_to_bf16(v[k]);
-                                hw[k] = part == 0 ? hi : f32_to_bf16(v[k] - bf16_to_f32(hi));
-                            }
-                            *(uint2 *)dst = make_uint2(hw[0] | ((uint32_t)hw[1] << 16),
-                                                       hw[2] | ((uint32_t)hw[3] << 16));
-                        } else {
-                            *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
-                        }
-                    }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int qq = 0; qq < QB; ++qq) {
-                uint8_t *tbase = (uint8_t *)inter_t + (size_t)(qb + qq) * plane * esz;
-                const uint8_t *Lq = L + qq * PLANE;
-                for (int t = threadIdx.x; t < TILE * CPR; t += UD_NT) {
-                    const int c = t / CPR, ch = t % CPR;
-                    *(uint4 *)(tbase + ((size_t)(i0 + c) * R + m0) * esz + ch * 16) =
-                        *(const uint4 *)(Lq + c * P + ch * 16);
-                }
-            }
-            __syncthreads();
-        }
-    }
 }
 
-// One tile of partial rows x weights^T over a K split: part[sp][m][d] = sum
-// over the split's K steps of a_q[m][.] . w_q[d][.], for NSEG segments of d_ff
-// each. Segment q reads A array q (arrays `R dff` elements apart) and B array
-// q >> BSHIFT (arrays `dm dff` elements apart).
+// One tile of partial rows x weights over a K split: part[sp][m][d] = sum
+// over the split's K steps of a_q[m][.] . w_q[.][d], for NSEG segments of
+// d_ff each. Segment q reads A array q (arrays `R dff` elements apart, K
+// along their rows) and weight matrix w0 (q >> BSHIFT == 0) or w1, stored
+// [d_ff][d_model], i.e. K-major: read through the transposing LDS loads.
 template <int DT, int NSEG, int BSHIFT>
-DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ wt, int n, int dm,
-                     int dff, int R, int S, float *__restrict__ part, int bx, int by, int sp,
-                     uint8_t *L)
+DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ w0,
+                     const uint8_t *__restrict__ w1, int n, int dm, int dff, int R, int S,
+                     float *__restrict__ part, int bx, int by, int sp, uint8_t *L)
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
-    const int m0 = by * TILE, d0 = bx * TILE;
+    constexpr int KS = CW::ROWB / esz; // K per step
+    const int m0 = by * WT, d0 = bx * WT;
     if (m0 >= n)
         return;
     const size_t rowbytes = (size_t)dff * esz, plane = (size_t)R * dff * esz,
-                 wplane = (size_t)dm * dff * esz;
-    const int spseg = (int)(rowbytes / CW::ROWB), nk = NSEG * spseg;
+                 wrow = (size_t)dm * esz;
+    const int spseg = dff / KS, nk = NSEG * spseg;
     const int kt0 = (int)((long)nk * sp / S), kt1 = (int)((long)nk * (sp + 1) / S);
+    auto rowa = [&](int r) { return a + (size_t)(m0 + r) * rowbytes; };
+    auto rowb = [&](int r) { return w0 + (size_t)r * wrow + (size_t)d0 * esz; };
+    const ptrdiff_t w01 = w1 - w0;
     auto off = [&](int kt) {
         const int q = kt / spseg, kk = kt % spseg;
         return ng::StepOff{q * plane + (size_t)kk * CW::ROWB,
-                           (q >> BSHIFT) * wplane + (size_t)kk * CW::ROWB};
+                           (size_t)((q >> BSHIFT) ? w01 : 0) + (size_t)kk * KS * wrow};
     };
-    auto rowa = [&](int r) { return a + (size_t)(m0 + r) * rowbytes; };
-    auto rowb = [&](int r) { return wt + (size_t)min(d0 + r, dm - 1) * rowbytes; };
     ng::Acc<CW> acc;
-    ng::mainloop<CW, DT>(L, rowa, rowb, off, kt0, kt1, acc);
+    ng::mainloop_mixed<CW, DT, ng::KC, ng::KM>(L, rowa, rowb, off, kt0, kt1, acc, 1 << 30,
+                                               dm - d0);
     const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
     float *p = part + (size_t)sp * R * dm;
 #pragma unroll
@@ -325,49 +285,40 @@ DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ 
             }
 }
 
-// One tile of dW[i][d] += sum_m it[i][m] xt[d][m] over the backup rows, z = 0,
-// 1, 2: (dW_d, a, dy), (dW_u, du, x), (dW_g, dg, x); hi and lo segments for bf16.
+// One tile of dW[i][d] = sum_m it[m][i] xo[m][d] over the backup rows, z = 0,
+// 1, 2: (dW_d, a, dy_O), (dW_u, du, x_O), (dW_g, dg, x_O); hi and lo segments
+// for bf16. Both operands run along the rows m, the contraction index: both
+// are read K-major. Rows at or past n hold zeros in both (the u/da epilogue
+// stores its whole tiles, the gather zero rows), so whole K steps are safe.
 template <int DT>
-DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt, int n, int dm,
+DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xo, int n, int dm,
                   int dff, int R, float *__restrict__ dwd, float *__restrict__ dwu,
                   float *__restrict__ dwg, int bx, int by, int z, uint8_t *L)
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    constexpr int KE = CW::ROWB / esz; // rows per K step
+    constexpr int KS = CW::ROWB / esz; // rows per K step
     if (n <= 0)
         return;
-    const int d0 = bx * TILE, i0 = by * TILE;
-    const size_t rowbytes = (size_t)R * esz, plane = (size_t)dff * R * esz;
-    const uint8_t *ta = it + (size_t)z * NH * plane;                  // a / du / dg, hi first
-    const uint8_t *tx = xt + (size_t)(z == 0 ? 1 : 0) * dm * rowbytes; // dy or x
+    const int d0 = bx * WT, i0 = by * WT;
+    const size_t plane = (size_t)R * dff * esz, irow = (size_t)dff * esz,
+                 xrow = (size_t)dm * esz;
+    const uint8_t *ta = it + (size_t)z * NH * plane;             // a / du / dg, hi first
+    const uint8_t *tx = xo + (size_t)(z == 0 ? 1 : 0) * R * xrow; // dy_O or x_O
     float *out = z == 0 ? dwd : (z == 1 ? dwu : dwg);
-    const int spseg = (n + KE - 1) / KE, nk = NH * spseg;
+    const int spseg = (n + KS - 1) / KS, nk = NH * spseg;
+    auto rowa = [&](int r) { return ta + (size_t)r * irow + (size_t)i0 * esz; };
+    auto rowb = [&](int r) { return tx + (size_t)r * xrow + (size_t)d0 * esz; };
     auto off = [&](int kt) {
         const int q = kt / spseg, kk = kt % spseg;
-        return ng::StepOff{q * plane + (size_t)kk * CW::ROWB, (size_t)kk * CW::ROWB};
+        return ng::StepOff{q * plane + (size_t)kk * KS * irow, (size_t)kk * KS * xrow};
     };
-    auto rowa = [&](int r) { return ta + (size_t)(i0 + r) * rowbytes; };
-    auto rowb = [&](int r) { return tx + (size_t)min(d0 + r, dm - 1) * rowbytes; };
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
-    // all of this lane's current dW values, requested before the K loop (they
-    // do not depend on it): their latency overlaps the loop's first loads
-    float cur[CW::MI][CW::NI][16];
-#pragma unroll
-    for (int mi = 0; mi < CW::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < CW::NI; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int i = i0 + ng::acc_row<CW>(wm, mi, e, lane);
-                const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
-                // unconditional load (column clamped into the row), then select
-                const float v = out[(size_t)i * dm + min(d, dm - 1)];
-                cur[mi][ni][e] = d < dm ? v : 0.f;
-            }
     ng::Acc<CW> acc;
-    ng::mainloop<CW, DT>(L, rowa, rowb, off, 0, nk, acc);
+    ng::mainloop_mixed<CW, DT, ng::KM, ng::KM>(L, rowa, rowb, off, 0, nk, acc, dff - i0, dm - d0);
+    // the tile is the backup rows' share of dW, written whole: the ELL rows'
+    // share is added to it by the neuron pass, which runs next
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
 #pragma unroll
     for (int mi = 0; mi < CW::MI; ++mi)
 #pragma unroll
@@ -376,65 +327,59 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xt
             for (int e = 0; e < 16; ++e) {
                 const int i = i0 + ng::acc_row<CW>(wm, mi, e, lane);
                 const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
-                if (d < dm)
-                    out[(size_t)i * dm + d] = cur[mi][ni][e] + acc.v[mi][ni][e];
+                if (i < dff && d < dm)
+                    out[(size_t)i * dm + d] = acc.v[mi][ni][e];
             }
 }
 
 // ---------------------------------------------------------------- kernels
-// forward: the A tiles, then (other workgroups) the W_d transpose
 template <int DT>
 __global__ __launch_bounds__(UD_NT, 1) void bk_a_kernel(
     const uint8_t *__restrict__ x, const int32_t *__restrict__ ovf_rows,
-    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
-    const uint8_t *__restrict__ wd, int dm, int dff, int R, const void *__restrict__ dense,
-    void *__restrict__ inter, void *__restrict__ wdt, int n_a)
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu, int dm,
+    int dff, int R, const void *__restrict__ dense, void *__restrict__ inter)
 {
     __shared__ __attribute__((aligned(16))) uint8_t L[ud_lds<DT>()];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
     const int b = blockIdx.x, nx = dff / TILE;
-    if (b < n_a)
-        ud_tile<DT, false>(x, nullptr, ovf_rows, n, wu, nullptr, dm, dff, R, dense, 0.f, inter,
-                           nullptr, b % nx, b / nx, L);
-    else
-        weight_t_tile<DT, UD_NT>(wd, wdt, dm, dff, b - n_a, L);
+    ud_tile<DT, false>(x, nullptr, ovf_rows, n, wu, nullptr, dm, dff, R, dense, 0.f, inter,
+                       b % nx, b / nx, L);
 }
 
-// backward: the u/da tiles (the transposes run beside the ELL masks)
 template <int DT>
 __global__ __launch_bounds__(UD_NT, 1) void bk_ud_kernel(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd, int dm, int dff, int R,
-    const void *__restrict__ dense, float l1, void *__restrict__ inter, void *__restrict__ inter_t)
+    const void *__restrict__ dense, float l1, void *__restrict__ inter)
 {
     __shared__ __attribute__((aligned(16))) uint8_t L[ud_lds<DT>()];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
     const int b = blockIdx.x, nx = dff / TILE;
-    ud_tile<DT, true>(x, dy, ovf_rows, n, wu, wd, dm, dff, R, dense, l1, inter, inter_t, b % nx,
-                      b / nx, L);
+    ud_tile<DT, true>(x, dy, ovf_rows, n, wu, wd, dm, dff, R, dense, l1, inter, b % nx, b / nx,
+                      L);
 }
 
 template <int DT, int NH>
-__global__ __launch_bounds__(CW::NT, 2) void bk_y_kernel(
-    const uint8_t *__restrict__ a, const uint8_t *__restrict__ wdt,
+__global__ __launch_bounds__(CW::NT, 1) void bk_y_kernel(
+    const uint8_t *__restrict__ a, const uint8_t *__restrict__ wd,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
     float *__restrict__ part)
 {
     __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
-    rowsw_tile<DT, NH, 4>(a, wdt, n_rows(n_ovf_p, max_ovf), dm, dff, R, S, part, blockIdx.x,
+    rowsw_tile<DT, NH, 4>(a, wd, wd, n_rows(n_ovf_p, max_ovf), dm, dff, R, S, part, blockIdx.x,
                           blockIdx.y, blockIdx.z, L);
 }
 
 // backward: the dx_O tiles (K split), then the dW tiles
 template <int DT>
-__global__ __launch_bounds__(CW::NT, 2) void bk_dxdw_kernel(
-    const uint8_t *__restrict__ inter, const uint8_t *__restrict__ wt,
-    const uint8_t *__restrict__ inter_t, const uint8_t *__restrict__ xt,
+__global__ __launch_bounds__(CW::NT, 1) void bk_dxdw_kernel(
+    const uint8_t *__restrict__ inter, const uint8_t *__restrict__ wu,
+    const uint8_t *__restrict__ wg, const uint8_t *__restrict__ xo,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
     float *__restrict__ part, float *__restrict__ dwd, float *__restrict__ dwu,
     float *__restrict__ dwg, int n_dx)
@@ -445,34 +390,32 @@ __global__ __launch_bounds__(CW::NT, 2) void bk_dxdw_kernel(
     if (n <= 0)
         return;
     int b = blockIdx.x;
-    const int nd = (dm + TILE - 1) / TILE;
+    const int nd = (dm + WT - 1) / WT;
     if (b < n_dx) {
-        // segments (du hi, du lo, dg hi, dg lo) against (W_u^T, W_u^T, W_g^T,
-        // W_g^T), or (du, dg) against (W_u^T, W_g^T)
-        const int mt = R / TILE;
-        rowsw_tile<DT, 2 * NH, NH == 2 ? 1 : 0>(inter, wt, n, dm, dff, R, S, part, b % nd,
-                                                 (b / nd) % mt, b / (nd * mt), L);
+        // segments (du hi, du lo, dg hi, dg lo) against (W_u, W_u, W_g, W_g),
+        // or (du, dg) against (W_u, W_g); du is plane NH of inter (after a)
+        const int mt = R / WT;
+        const size_t plane = (size_t)R * dff * sizeof(Store<DT>);
+        rowsw_tile<DT, 2 * NH, NH == 2 ? 1 : 0>(inter + NH * plane, wu, wg, n, dm, dff, R, S,
+                                                 part, b % nd, (b / nd) % mt, b / (nd * mt), L);
         return;
     }
     b -= n_dx;
-    const int ni = dff / TILE;
-    dw_tile<DT>(inter_t, xt, n, dm, dff, R, dwd, dwu, dwg, b % nd, (b / nd) % ni, b / (nd * ni),
-                L);
+    const int ni = (dff + WT - 1) / WT;
+    dw_tile<DT>(inter, xo, n, dm, dff, R, dwd, dwu, dwg, b % nd, (b / nd) % ni, b / (nd * ni), L);
 }
 
 } // namespace
 
 // ---------------------------------------------------------------- host side
 struct BkLayout {
-    size_t inter, inter_t, xt, wt, part, total;
+    size_t inter, xo, part, total;
     int R, S;
 };
 
 // Workspace of the backup products, bytes from `base`:
-//   inter   [NI][R][dff]  fwd: a (hi, lo); bwd: du, dg (hi, lo each)
-//   inter_t [3][NH][dff][R] bwd only: a, du, dg transposed
-//   xt      [2][dm][R]      bwd only: x_O, dy_O transposed
-//   wt      fwd: W_d^T; bwd: W_u^T, W_g^T ([dm][dff] each)
+//   inter   fwd: A (hi, lo) [NH][R][dff]; bwd: a, du, dg (hi, lo each) [3][NH][R][dff]
+//   xo      bwd only: x_O, dy_O gathered, [2][R][dm]
 //   part    [S][R][dm] float32 partials of y_O / dx_O
 BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
 {
@@ -482,11 +425,9 @@ BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
     const int nseg = (int)(bwd ? 2 * nh : nh);
     L.S = split_k(L.R, dm, nseg * (int)(dff * esz / CW::ROWB));
     size_t o = 0;
-    L.inter = o;   o += up256((bwd ? 2 : 1) * nh * L.R * dff * esz);
-    L.inter_t = o; o += bwd ? up256(3 * nh * L.R * dff * esz) : 0;
-    L.xt = o;      o += bwd ? up256(2 * (size_t)dm * L.R * esz) : 0;
-    L.wt = o;      o += up256((bwd ? 2 : 1) * (size_t)dm * dff * esz);
-    L.part = o;    o += up256((size_t)L.S * L.R * dm * 4);
+    L.inter = o; o += up256((bwd ? 3 : 1) * nh * L.R * dff * esz);
+    L.xo = o;    o += bwd ? up256(2 * (size_t)L.R * dm * esz) : 0;
+    L.part = o;  o += up256((size_t)L.S * L.R * dm * 4);
     L.total = max_ovf > 0 ? o : 0;
     return L;
 }
@@ -498,16 +439,15 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, false);
     const int n_a = (dff / TILE) * (L.R / TILE);
-    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a + (dm / TT) * (dff / TT)), dim3(UD_NT),
-                       0, s, (const uint8_t *)x, h->ovf_rows, h->n_ovf, h->max_ovf,
-                       (const uint8_t *)wu, (const uint8_t *)wd, dm, dff, L.R, h->dense,
-                       (void *)(ws + L.inter), (void *)(ws + L.wt), n_a);
+    hipLaunchKernelGGL((bk_a_kernel<DT>), dim3(n_a), dim3(UD_NT), 0, s, (const uint8_t *)x,
+                       h->ovf_rows, h->n_ovf, h->max_ovf, (const uint8_t *)wu, dm, dff, L.R,
+                       h->dense, (void *)(ws + L.inter));
     tm.mark("bk_a_kernel");
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + TILE - 1) / TILE, L.R / TILE, L.S),
-                       dim3(CW::NT), 0, s,
-                       (const uint8_t *)(ws + L.inter), (const uint8_t *)(ws + L.wt), h->n_ovf,
-                       h->max_ovf, dm, dff, L.R, L.S, (float *)(ws + L.part));
+    hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + WT - 1) / WT, L.R / WT, L.S),
+                       dim3(CW::NT), 0, s, (const uint8_t *)(ws + L.inter),
+                       (const uint8_t *)wd, h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
+                       (float *)(ws + L.part));
     tm.mark("bk_y_kernel");
 }
 
@@ -521,23 +461,22 @@ void bk_ud_dt(const void *x, const void *dy, const hybrid_t *h, const void *wu, 
     hipLaunchKernelGGL((bk_ud_kernel<DT>), dim3(n_ud), dim3(UD_NT), 0, s,
                        (const uint8_t *)x, (const uint8_t *)dy, h->ovf_rows, h->n_ovf, h->max_ovf,
                        (const uint8_t *)wu, (const uint8_t *)wd, dm, dff, L.R, h->dense, l1,
-                       (void *)(ws + L.inter), (void *)(ws + L.inter_t));
+                       (void *)(ws + L.inter));
     tm.mark("bk_ud_kernel");
 }
 
 template <int DT>
-void bk_dxdw_dt(const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu, float *dwg,
-                uint8_t *ws, Timer &tm, hipStream_t s)
+void bk_dxdw_dt(const hybrid_t *h, const void *wu, const void *wg, int dm, float *dx, float *dwd,
+                float *dwu, float *dwg, uint8_t *ws, Timer &tm, hipStream_t s)
 {
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
-    const int nd = (dm + TILE - 1) / TILE;
-    const int n_dx = nd * (L.R / TILE) * L.S, n_dw = nd * (dff / TILE) * 3;
+    const int nd = (dm + WT - 1) / WT;
+    const int n_dx = nd * (L.R / WT) * L.S, n_dw = nd * ((dff + WT - 1) / WT) * 3;
     hipLaunchKernelGGL((bk_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(CW::NT), 0, s,
-                       (const uint8_t *)(ws + L.inter), (const uint8_t *)(ws + L.wt),
-                       (const uint8_t *)(ws + L.inter_t), (const uint8_t *)(ws + L.xt), h->n_ovf,
-                       h->max_ovf, dm, dff, L.R, L.S, (float *)(ws + L.part), dwd, dwu, dwg,
-                       n_dx);
+                       (const uint8_t *)(ws + L.inter), (const uint8_t *)wu, (const uint8_t *)wg,
+                       (const uint8_t *)(ws + L.xo), h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
+                       (float *)(ws + L.part), dwd, dwu, dwg, n_dx);
     tm.mark("bk_dxdw_kernel");
 }
 
@@ -552,6 +491,14 @@ BkPart bk_part(int dt, int dm, int dff, int max_ovf, bool bwd, const void *ws)
 size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd)
 {
     return bk_layout(dt, dm, dff, max_ovf, bwd).total;
+}
+
+BkGather bk_gather(int dt, int dm, int dff, int max_ovf, void *ws)
+{
+    if (max_ovf <= 0)
+        return BkGather{nullptr, 0, 0};
+    const BkLayout L = bk_layout(dt, dm, dff, max_ovf, true);
+    return BkGather{(uint8_t *)ws + L.xo, L.R, bk_gather_blocks(L.R)};
 }
 
 void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
@@ -577,22 +524,14 @@ void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t 
         bk_ud_dt<TWELL_F32>(x, dy, h, wu, wd, dm, l1, (uint8_t *)ws, tm, s);
 }
 
-BkXpose bk_xpose(int dt, int dm, int dff, int max_ovf, void *ws)
-{
-    if (max_ovf <= 0)
-        return BkXpose{nullptr, nullptr, 0, 0};
-    const BkLayout L = bk_layout(dt, dm, dff, max_ovf, true);
-    return BkXpose{(uint8_t *)ws + L.wt, (uint8_t *)ws + L.xt, L.R,
-                   bk_xpose_blocks(dm, dff, L.R)};
-}
-
-void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
-                    float *dwg, void *ws, Timer &tm, hipStream_t s)
+void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, const void *wu, const void *wg, int dm,
+                    float *dx, float *dwd, float *dwu, float *dwg, void *ws, Timer &tm,
+                    hipStream_t s)
 {
     if (h->max_ovf <= 0 || h->T <= 0)
         return;
     if (dt == TWELL_BF16)
-        bk_dxdw_dt<TWELL_BF16>(h, dm, dx, dwd, dwu, dwg, (uint8_t *)ws, tm, s);
+        bk_dxdw_dt<TWELL_BF16>(h, wu, wg, dm, dx, dwd, dwu, dwg, (uint8_t *)ws, tm, s);
     else
-        bk_dxdw_dt<TWELL_F32>(h, dm, dx, dwd, dwu, dwg, (uint8_t *)ws, tm, s);
+        bk_dxdw_dt<TWELL_F32>(h, wu, wg, dm, dx, dwd, dwu, dwg, (uint8_t *)ws, tm, s);
 }

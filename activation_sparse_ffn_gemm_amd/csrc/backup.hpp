@@ -19,8 +19,9 @@ void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void 
 void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
                   const void *wu, const void *wd, int dm, float l1, void *ws, Timer &tm,
                   hipStream_t s);
-void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, int dm, float *dx, float *dwd, float *dwu,
-                    float *dwg, void *ws, Timer &tm, hipStream_t s);
+void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, const void *wu, const void *wg, int dm,
+                    float *dx, float *dwd, float *dwu, float *dwg, void *ws, Timer &tm,
+                    hipStream_t s);
 
 // Row `slot` of the backup: words [base, min(base + 64 NW, end, ndw)) of a
 // d_model row (EPW floats each, lane l owning words base + 64 c + l) of sum
@@ -67,94 +68,39 @@ DEVI void bk_finish_row(const BkPart &bp, int slot, int ndw, int base, int end, 
     }
 }
 
-// ---- transposed copies for the backward's backup products, made by extra
-// workgroups of an earlier launch (the ELL masks) at full occupancy.
-constexpr int TT = 64; // transpose tile (elements per side)
-template <int DT> using Store = typename elem<DT>::storage;
-
-
-// One TT x TT tile of out[c][r] = in[src(r)][c] for c < cols and r < rows_out,
-// src(r) = r, or gather[r] for r < n_valid and a zero row past it (gather
-// non-null). NTH threads; lds: TT x (TT + 8) elements.
-template <typename T, int NTH = 256>
-DEVI void transpose_tile(const T *__restrict__ in, T *__restrict__ out, int cols, int rows_out,
-                         const int32_t *__restrict__ gather, int n_valid, int bx, int by,
-                         uint8_t *lds)
-{
-    constexpr int V = 16 / sizeof(T), TP = TT + 8; // elements per 16-byte chunk, LDS pitch
-    T(*tile)[TP] = (T(*)[TP])lds;
-    const int c0 = bx * TT, r0 = by * TT, tid = threadIdx.x;
-    if (gather && r0 >= (n_valid + TT - 1) / TT * TT)
-        return; // never read: the products stop at the padded row count
-    constexpr int CPR = TT / V; // chunks per tile row
-    for (int q = tid; q < TT * CPR; q += NTH) {
-        const int r = q / CPR, cc = q % CPR, gr = r0 + r, gc = c0 + cc * V;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (gr < n_valid && gc < cols) {
-            const int sr = gather ? gather[gr] : gr;
-            v = *(const uint4 *)(in + (size_t)sr * cols + gc);
-        }
-        const T *e = (const T *)&v;
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            tile[r][cc * V + k] = e[k];
-    }
-    __syncthreads();
-    for (int q = tid; q < TT * CPR; q += NTH) {
-        const int c = q / CPR, rc = q % CPR, gc = c0 + c, gr = r0 + rc * V;
-        if (gc >= cols || gr >= rows_out)
-            continue;
-        T e[V];
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            e[k] = tile[rc * V + k][c];
-        *(uint4 *)(out + (size_t)gc * rows_out + gr) = *(const uint4 *)e;
-    }
-    __syncthreads(); // lds is reused by the workgroup's next tile
-}
-
-// Tiles of a weight transpose [dff][dm] -> [dm][dff]
-DEVI int wt_tiles(int dm, int dff) { return (dm / TT) * (dff / TT); }
-template <int DT, int NTH = 256>
-DEVI void weight_t_tile(const void *w, void *wt, int dm, int dff, int b, uint8_t *lds)
-{
-    const int nx = dm / TT;
-    transpose_tile<Store<DT>, NTH>((const Store<DT> *)w, (Store<DT> *)wt, dm, dff, nullptr, dff,
-                                   b % nx, b / nx, lds);
-}
-
-
-// Where the backward's transposed copies go: W_u^T, W_g^T ([dm][dff] each) at
-// wt; x_O^T, dy_O^T ([dm][R] each) at xt; `blocks` workgroups make them.
-struct BkXpose {
-    uint8_t *wt, *xt;
+// ---- the backup rows' x and dy rows gathered into xo [2][R][d_model] (x_O,
+// then dy_O; rows at or past n_ovf zero) by extra workgroups of an earlier
+// launch (the ELL masks): the dW products take them, K-major, as the operand
+// contracted over the rows.
+struct BkGather {
+    uint8_t *xo;
     int R, blocks;
 };
-BkXpose bk_xpose(int dt, int dm, int dff, int max_ovf, void *ws);
-inline int bk_xpose_blocks(int dm, int dff, int R)
-{
-    return 2 * (dm / TT) * (dff / TT) + 2 * (dm / TT) * (R / TT);
-}
+BkGather bk_gather(int dt, int dm, int dff, int max_ovf, void *ws);
+constexpr int GROWS = 4; // rows per workgroup of the gather
+inline int bk_gather_blocks(int R) { return 2 * R / GROWS; }
 
-// Block b (< bk_xpose_blocks) of those copies; lds: TT x (TT + 8) elements.
-// Nothing is copied when the hybrid holds no backup rows.
-template <int DT>
-DEVI void bk_xpose_block(int b, const BkXpose &xp, const uint8_t *x, const uint8_t *dy,
-                         const uint8_t *wu, const uint8_t *wg, const int32_t *ovf_rows,
-                         const int32_t *n_ovf_p, int max_ovf, int dm, int dff, uint8_t *lds)
+// Block b (< bk_gather_blocks) of the gather, NTH threads, 16 bytes per lane.
+// Nothing is written when the hybrid holds no backup rows.
+template <int DT, int NTH>
+DEVI void bk_gather_block(int b, const BkGather &g, const uint8_t *__restrict__ x,
+                          const uint8_t *__restrict__ dy, const int32_t *__restrict__ ovf_rows,
+                          const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm)
 {
-    using T = Store<DT>;
+    constexpr int esz = sizeof(typename elem<DT>::storage);
     const int n = min(*n_ovf_p, max_ovf);
     if (n <= 0)
         return;
-    const int nw = (dm / TT) * (dff / TT);
-    if (b < 2 * nw) { // W_u^T, W_g^T
-        const int z = b / nw;
-        weight_t_tile<DT>(z ? wg : wu, (T *)xp.wt + (size_t)z * dm * dff, dm, dff, b % nw, lds);
-        return;
+    const int per = g.R / GROWS, z = b / per, r0 = (b % per) * GROWS;
+    const size_t rowb = (size_t)dm * esz;
+    const int c16 = (int)(rowb / 16); // d_model % 64 == 0: whole 16-byte chunks
+    const uint8_t *src = z ? dy : x;
+    uint8_t *dst = g.xo + (size_t)z * g.R * rowb;
+    for (int q = threadIdx.x; q < GROWS * c16; q += NTH) {
+        const int r = r0 + q / c16, c = q % c16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < n)
+            v = *(const uint4 *)(src + (size_t)ovf_rows[r] * rowb + (size_t)c * 16);
+        *(uint4 *)(dst + (size_t)r * rowb + (size_t)c * 16) = v;
     }
-    b -= 2 * nw; // x_O^T, dy_O^T: [dm][R]
-    const int ng = (dm / TT) * (xp.R / TT), z = b / ng, q = b % ng, gx = dm / TT;
-    transpose_tile<T>((const T *)(z ? dy : x), (T *)xp.xt + (size_t)z * dm * xp.R, dm, xp.R,
-                      ovf_rows, n, q % gx, q / gx, lds);
 }

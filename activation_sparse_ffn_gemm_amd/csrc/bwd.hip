@@ -21,7 +21,8 @@
 //      row order; per entry it gathers x[t] and dy[t] once, computes
 //      u = x[t] . wu_t[i] and da = dy[t] . wd[i], then a, du, dg, adds
 //      a dy[t], du x[t], dg x[t] to its three dW rows, and keeps du, dg for
-//      the dx pass. Every dW row is written (zero rows for unused neurons);
+//      the dx pass. Every dW row is written once (zero rows for unused
+//      neurons), added to the backup rows' share when there are backup rows;
 //   5. dx (sparse-to-dense): a wave per (row, part of d_model) sums
 //      du wu_t[i] + dg wg_t[i] over the row's entries.
 // Rows are gathered with 4-byte lanes (rows.hpp).
@@ -31,8 +32,11 @@
 //      where h is zero), launched before the ELL passes;
 //   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T as split-K partials,
 //      summed into their rows by the dx pass;
-//   8. DW:   dW += [a | du | dg]^T [dy | x | x] over the backup rows, after the
-//      neuron pass has written every dW row.
+//   8. DW:   dW = [a | du | dg]^T [dy | x | x] over the backup rows, written
+//      before the neuron pass, which adds the ELL rows' share (a two-term
+//      sum, so its value does not depend on the order of the two passes).
+// The x and dy rows of the backup rows are gathered once by extra workgroups
+// of the masks launch; no operand is transposed.
 #include "backup.hpp"
 #include "rows.hpp"
 #include "slices.hpp"
@@ -247,10 +251,13 @@ __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
     const void *__restrict__ ell_val, int T, int K, int dff, const uint8_t *__restrict__ x,
     const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd,
     int dm, float l1, float *__restrict__ coef, float *__restrict__ dwg, float *__restrict__ dwu,
-    float *__restrict__ dwd)
+    float *__restrict__ dwd, const int32_t *__restrict__ n_ovf_p, int max_ovf)
 {
     using E = elem<DT>;
     using R = Row<DT, NW>;
+    // the backup rows' dense products have written their share of dW when the
+    // hybrid holds backup rows: this pass adds the ELL rows' share to it
+    const bool add = T > 0 && max_ovf > 0 && min(*n_ovf_p, max_ovf) > 0;
     using RP = Row<DT, NWP>;
     constexpr int EPW = R::EPW;
     constexpr int PL = NWP * 64 * EPW; // elements of one part of a row
@@ -353,14 +360,24 @@ __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
                 sum.z += v.z;
                 sum.w += v.w;
             }
+            if (add) {
+                const float4 b = *(const float4 *)(o + q);
+                sum = make_float4(b.x + sum.x, b.y + sum.y, b.z + sum.z, b.w + sum.w);
+            }
             *(float4 *)(o + q) = sum;
         }
         __syncthreads();
     };
     if constexpr (S == 1) {
-        pgeo.store_f(dwd, i, ad);
-        pgeo.store_f(dwu, i, au);
-        pgeo.store_f(dwg, i, ag);
+        if (add) {
+            pgeo.add_store_f(dwd, i, ad);
+            pgeo.add_store_f(dwu, i, au);
+            pgeo.add_store_f(dwg, i, ag);
+        } else {
+            pgeo.store_f(dwd, i, ad);
+            pgeo.store_f(dwu, i, au);
+            pgeo.store_f(dwg, i, ag);
+        }
     } else {
         reduce_store(ad, dwd);
         reduce_store(au, dwu);
@@ -440,18 +457,17 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 // wg_t into the dx pass's interleaved slice-major array; the rest make the
 // backup products' transposed copies.
 constexpr int MASK_LDS = CH * 8 + BR * 4;
-constexpr int XPOSE_LDS = TT * (TT + 8) * 4;
 template <int DT>
 __global__ __launch_bounds__(NT) void mask_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, int T, int K, int dff, uint64_t *__restrict__ masks,
     int32_t *__restrict__ cnt, int n_chunk, int n_mask, int n_copy,
     const uint32_t *__restrict__ wu, const uint32_t *__restrict__ wg, uint32_t *__restrict__ wsl,
-    Slices sl, BkXpose xp, const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
+    Slices sl, BkGather bg, const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     int dm)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MASK_LDS > XPOSE_LDS ? MASK_LDS : XPOSE_LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MASK_LDS];
     int b = blockIdx.x;
     if (b < n_mask) {
         ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk,
@@ -463,8 +479,7 @@ __global__ __launch_bounds__(NT) void mask_kernel(
         copy_slices_rows<2, NT>(b, wu, wg, wsl, dff, sl);
         return;
     }
-    bk_xpose_block<DT>(b - n_copy, xp, x, dy, (const uint8_t *)wu, (const uint8_t *)wg, ovf_rows,
-                       n_ovf_p, max_ovf, dm, dff, lds);
+    bk_gather_block<DT, NT>(b - n_copy, bg, x, dy, ovf_rows, n_ovf_p, max_ovf, dm);
 }
 
 // ------------------------------------------------------------ 5'. dx, XCD-local
@@ -604,11 +619,11 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     if (T > 0) {
         const int n_chunk = (dff + CH - 1) / CH, n_mask = L.nblk * n_chunk;
         const int n_copy = L.split ? copy_groups(dff) : 0;
-        const BkXpose xp = bk_xpose(DT, dm, dff, h->max_ovf, ws + L.backup);
-        hipLaunchKernelGGL((mask_kernel<DT>), dim3(n_mask + n_copy + xp.blocks), dim3(NT), 0, s,
+        const BkGather bg = bk_gather(DT, dm, dff, h->max_ovf, ws + L.backup);
+        hipLaunchKernelGGL((mask_kernel<DT>), dim3(n_mask + n_copy + bg.blocks), dim3(NT), 0, s,
                            h->row_nnz, h->row_slot, h->ell_col, T, K, dff, masks, cnt, n_chunk,
                            n_mask, n_copy, (const uint32_t *)wu, (const uint32_t *)wg, wsl, sl,
-                           xp, xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf, dm);
+                           bg, xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf, dm);
         tm.mark("mask_kernel");
     }
     launch_bk_ud((twell_dtype)DT, x, dy, h, wu, wd, dm, l1, ws + L.backup, tm, s);
@@ -623,13 +638,13 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                            status);
         tm.mark("csc_fill_kernel");
     }
+    // the backup rows' dW products write dW (the neuron pass adds the ELL
+    // rows' share to it); their dx partials are summed by the dx pass
+    launch_bk_dxdw((twell_dtype)DT, h, wu, wg, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
     hipLaunchKernelGGL((bwd_neuron_kernel<DT, NW, NWN, GN, NSPLIT>), dim3(dff, NW / NWN),
                        dim3(64 * NSPLIT), 0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
-                       (const uint8_t *)wd, dm, l1, coef, dwg, dwu, dwd);
+                       (const uint8_t *)wd, dm, l1, coef, dwg, dwu, dwd, h->n_ovf, h->max_ovf);
     tm.mark("bwd_neuron_kernel");
-    // the backup rows' dW products add to the rows the neuron pass wrote; their
-    // dx partials are summed by the dx pass
-    launch_bk_dxdw((twell_dtype)DT, h, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
     if (T > 0) {
         const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, true, ws + L.backup);
         if (L.split) {

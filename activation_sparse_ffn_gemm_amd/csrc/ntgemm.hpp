@@ -234,4 +234,169 @@ DEVI void mainloop(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1, 
     __syncthreads(); // every wave is done reading the stages
 }
 
+
+// ---------------------------------------------------------------- K-major operands
+// Products whose operand is stored with the contraction index as its row
+// index ("[k][mn]": consecutive elements run along M or N) read it as it is
+// stored: the stage holds the operand's K step as KS k-rows of BX elements,
+// and the fragment reads transpose on the way out of LDS.
+//
+// gfx950's transposing LDS read of 16-bit elements (ds_read_b64_tr_b16)
+// gives, within each group of 16 lanes, lane 4q + e element e of the 8-byte
+// chunks addressed by lanes q, 4 + q, 8 + q and 12 + q (in that order; the
+// layout was measured on the part). So if lane 16G + 4j + q of a wave points
+// at k-row j, columns c0 + 16 (G & 1) + 4q .. + 3, lane l receives column
+// c0 + l % 32 at k-rows 0..3: one half of the 8 consecutive k a 32x32x16 MFMA
+// fragment takes per lane. Two reads (k-rows 0..3 and 4..7 of the lane's
+// half, k-rows 8 (l / 32) .. of the group) make the fragment.
+//
+// K-major rows of a stage are BX * esz bytes (at least 256); their 16-byte
+// chunks are XOR-swizzled with 4 (k-row % 4), so the four k-rows one read
+// touches land in four different 64-byte quarters of the 64 banks.
+enum Lay { KC = 0, KM = 1 }; // rows along K (as `mainloop` takes them), or along M/N
+
+template <int DT> DEVI uint4 frag_km(const uint8_t *X, int rb, int cb, int g, int lane);
+
+// fragment of tile columns cb .. cb + 31 for MFMA group g, from a K-major
+// region X of rows of rb bytes (bf16)
+template <> DEVI uint4 frag_km<TWELL_BF16>(const uint8_t *X, int rb, int cb, int g, int lane)
+{
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) bf16x4_t lds_b4;
+    const int G = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+    const int col = cb + 16 * (G & 1) + 4 * q; // element column of this lane's chunk
+    uint2 h[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int kr = 16 * g + 8 * (G >> 1) + 4 * r + j; // k-row; kr % 4 == j
+        const int off = kr * rb + ((((col * 2) >> 4) ^ (j << 2)) << 4) + ((col * 2) & 15);
+        const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_b4 *)(uintptr_t)(lds_u8 *)(X + off));
+        h[r] = __builtin_bit_cast(uint2, v);
+    }
+    return make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+}
+
+// float32: lane l takes column cb + l % 32 at k-rows 8g + 4 (l / 32) + 0..3
+// (the k order mma_group<TWELL_F32> expects), one 4-byte read each
+template <> DEVI uint4 frag_km<TWELL_F32>(const uint8_t *X, int rb, int cb, int g, int lane)
+{
+    const int col = cb + (lane & 31);
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int kr = 8 * g + 4 * (lane >> 5) + q;
+        v[q] = *(const uint32_t *)(X + kr * rb + ((((col * 4) >> 4) ^ ((kr & 3) << 2)) << 4) +
+                                   ((col * 4) & 15));
+    }
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// acc += A B^T over K steps [kt0, kt1) with either operand K-contiguous (KC)
+// or K-major (KM). As in `mainloop`, rowa(r) / rowb(r) give a per-row base
+// address and off(kt) the uniform byte offsets of step kt (computed once per
+// step): for a KC operand row r is tile row r (at K offset 0), for a KM
+// operand row r is the step's k-row r (the K index kt * KS + r, KS = ROWB /
+// element size) at the tile's first M (N) element, off(kt) then moving to
+// the step's first k-row. Rows outside a KC operand must repeat a valid row
+// (their outputs are dropped); K-major rows past the contraction's end must
+// read zeros in at least one operand. va / vb: columns of a K-major A / B
+// tile that lie inside the operand (a multiple of 8 elements); chunks past
+// them read the row's first chunk instead (their outputs are dropped), so no
+// read leaves the operand. One group of C::NWV waves; ends with a barrier.
+template <class C, int DT, int LA, int LB, class RowA, class RowB, class Off>
+DEVI void mainloop_mixed(uint8_t *L, RowA rowa, RowB rowb, Off off, int kt0, int kt1,
+                         Acc<C> &acc, int va = 1 << 30, int vb = 1 << 30)
+{
+    constexpr int esz = DT == TWELL_BF16 ? 2 : 4;
+    constexpr int RBA = C::BM * esz, RBB = C::BN * esz; // K-major row bytes
+    static_assert(LA == KC || (RBA >= 256 && BLK % RBA == 0), "K-major A rows");
+    static_assert(LB == KC || (RBB >= 256 && BLK % RBB == 0), "K-major B rows");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
+    const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc.v[mi][ni][e] = 0.f;
+    const int nk = kt1 - kt0;
+    if (nk <= 0)
+        return;
+    const int nb = wave < C::N_HI ? C::WB_HI : C::WB_HI - 1;
+    const int b0 = wave < C::N_HI ? wave * C::WB_HI
+                                  : C::N_HI * C::WB_HI + (wave - C::N_HI) * (C::WB_HI - 1);
+    // per block of this wave: which operand, and the address of the source
+    // chunk (at step offset 0) that the stage's swizzle puts at this lane's
+    // 16 LDS bytes
+    const uint8_t *src[C::WB_HI];
+    bool isa[C::WB_HI];
+#pragma unroll
+    for (int i = 0; i < C::WB_HI; ++i) {
+        const int b = min(b0 + i, C::NBLK - 1);
+        const int pos = b * BLK + 16 * lane; // byte in the stage
+        isa[i] = b * BLK < C::BM * C::ROWB;  // uniform
+        const int p = isa[i] ? pos : pos - C::BM * C::ROWB;
+        const bool km = isa[i] ? LA == KM : LB == KM;
+        const int rb = km ? (isa[i] ? RBA : RBB) : C::ROWB;
+        const int r = p / rb, c = (p % rb) >> 4;
+        int chunk;
+        if (km) {
+            const int sc = c ^ ((r & 3) << 2); // source chunk of this LDS chunk
+            chunk = sc * 16 / esz < (isa[i] ? va : vb) ? sc << 4 : 0;
+        } else {
+            chunk = (c ^ ((r / C::SW) % C::CPR)) << 4;
+        }
+        src[i] = (isa[i] ? rowa(r) : rowb(r)) + chunk;
+    }
+    constexpr int NST = C::NST;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8 *)L + b0 * BLK;
+    auto issue = [&](int kt) {
+        const uint32_t dst = lds0 + ((kt - kt0) % NST) * C::STAGE;
+        const StepOff o = off(kt);
+#pragma unroll
+        for (int i = 0; i < C::WB_HI; ++i)
+            if (i < nb) // uniform
+                lds_dma16(src[i] + (isa[i] ? o.a : o.b), dst + i * BLK);
+    };
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nk)
+            issue(kt0 + s);
+    for (int k = 0; k < nk; ++k) {
+        const int later = min(nk - 1, k + NST - 2) - k;
+        if (nb == C::WB_HI)
+            wait_vm_steps<C::WB_HI, NST - 2>(later);
+        else
+            wait_vm_steps<C::WB_HI - 1, NST - 2>(later);
+        __syncthreads();
+        if (k + NST - 1 < nk)
+            issue(kt0 + k + NST - 1);
+        const uint8_t *As = L + (k % NST) * C::STAGE, *Bs = As + C::BM * C::ROWB;
+#pragma unroll
+        for (int g = 0; g < C::NG; ++g) {
+            uint4 fa[C::MI], fb[C::NI];
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+                fa[mi] = LA == KM ? frag_km<DT>(As, RBA, wm * C::WM + mi * 32, g, lane)
+                                  : *(const uint4 *)(As + swz<C>(wm * C::WM + mi * 32 + l32,
+                                                                 2 * g + half));
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                fb[ni] = LB == KM ? frag_km<DT>(Bs, RBB, wn * C::WN + ni * 32, g, lane)
+                                  : *(const uint4 *)(Bs + swz<C>(wn * C::WN + ni * 32 + l32,
+                                                                 2 * g + half));
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni)
+                    mma_group<DT>(acc.v[mi][ni], fa[mi], fb[ni]);
+        }
+    }
+    __syncthreads();
+}
+
 } // namespace ng

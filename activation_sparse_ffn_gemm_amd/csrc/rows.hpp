@@ -114,6 +114,35 @@ template <int DT, int NW> struct Row {
         }
     }
 
+    // row r of a [rows][d_model] float32 matrix += f: every word's current
+    // value is requested before any is added
+    DEVI void add_store_f(float *y, int r, const float (&f)[NW][EPW]) const
+    {
+        float *p = y + (size_t)r * ndw * EPW;
+        float cur[NW][EPW];
+#pragma unroll
+        for (int c = 0; c < NW; ++c) {
+            const int w = in(c) ? word(c) : 0;
+            if constexpr (EPW == 2) {
+                const float2 v = *(const float2 *)(p + (size_t)w * 2);
+                cur[c][0] = v.x;
+                cur[c][1] = v.y;
+            } else {
+                cur[c][0] = p[w];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NW; ++c) {
+            if (!in(c))
+                continue;
+            if constexpr (EPW == 2)
+                *(float2 *)(p + (size_t)word(c) * 2) =
+                    make_float2(cur[c][0] + f[c][0], cur[c][1] + f[c][1]);
+            else
+                p[word(c)] = cur[c][0] + f[c][0];
+        }
+    }
+
     // row r of a [rows][d_model] float32 matrix
     DEVI void store_f(float *y, int r, const float (&f)[NW][EPW]) const
     {

@@ -259,11 +259,11 @@ def kernel_work(ctx):
                            "(3 GEMMs)"),
         "mask_kernel": ("hbm", 8 * T + nnz_ell * 2 + nblk * dff * 12
                         + (4 * dff * row_b if dx_split else 0)
-                        + (4 * dff * row_b + 4 * n_ovf * row_b if n_ovf > 0 else 0),
+                        + (2 * n_ovf * row_b + 2 * ctx.get("R", 0) * row_b if n_ovf > 0 else 0),
                         "row_nnz, row_slot per row, column per ELL entry read; 64-row block "
                         "mask and count per neuron written; on the same launch the slice-major "
-                        "wu_t, wg_t copy (XCD-local dx) and the backup's transposed W_u, W_g, "
-                        "x_O, dy_O (read + write)"),
+                        "wu_t, wg_t copy (XCD-local dx) and the backup rows' x, dy gathered "
+                        "(read + write, padded to whole 128-row tiles)"),
         "blk_prefix_kernel": ("hbm", nblk * dff * 12 + dff * 4,
                               "block counts read twice and rewritten as prefixes; totals"),
         "colptr_kernel": ("hbm", dff * 8 + 4, "neuron totals read, column pointers written"),
@@ -384,7 +384,8 @@ class Layer:
         if self.train:
             ell = self.hy.row_slot < 0
             out.update(n_ovf=int(self.hy.n_ovf.item()),
-                       nnz_ell=int(self.hy.row_nnz[ell].sum()))
+                       nnz_ell=int(self.hy.row_nnz[ell].sum()),
+                       R=(self.w.max_ovf + 127) // 128 * 128)
         return out
 
 
