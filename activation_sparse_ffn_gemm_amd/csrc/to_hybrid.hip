@@ -3,16 +3,17 @@
 // so rows with few nonzeros go to a compact ELL matrix and overflow rows are
 // redirected to a dense backup, through a dedicated conversion kernel).
 //
-// Two launches, all integer / copy work:
+// Three launches, all integer / copy work:
 //   1. rows:  one wave per row sums the tile counts (row_nnz) and, for a row
 //             with row_nnz <= K, concatenates its tiles into ELL row t; the
 //             tiles are in column order, so the ELL row is ascending.
-//   2. slots + dense: one workgroup per block of BLK rows counts the overflow
-//             rows before its block (a reduction over row_nnz), numbers its
-//             own overflow rows after them in row order (backup slots in
-//             ascending row order), writes row_slot, ovf_rows, and the dense
-//             backup rows (zero fill, then scatter); the last block writes
-//             n_ovf.
+//   2. slots: one thread per row; a workgroup counts the overflow rows of
+//             the blocks before its own (a reduction over row_nnz) and scans
+//             its block's flags, so backup slots follow ascending row order;
+//             writes row_slot and ovf_rows, and the last block n_ovf.
+//   3. dense: one workgroup per backup slot builds that row (zeros, then its
+//             entries) in LDS and stores it with 16-byte lanes, all backup
+//             rows at once.
 #include "common.hpp"
 
 namespace {
@@ -68,115 +69,116 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
     }
 }
 
-constexpr int BLK = 4;    // rows per workgroup of the slot/dense launch: a workgroup builds
-                          // its backup rows one after another, so blocks stay small
-constexpr int DNT = 256;  // its threads
+constexpr int SNT = 256;       // threads (and rows) per workgroup of the slot launch
+constexpr int DNT = 256;       // threads per workgroup of the dense launch
 constexpr int ROW_LDS = 32768; // bytes of one dense row built in LDS (d_ff 16384 bf16 / 8192 f32)
+
+__global__ __launch_bounds__(SNT) void hyb_slots_kernel(
+    const int32_t *__restrict__ row_nnz, int T, int K, int max_ovf,
+    int32_t *__restrict__ row_slot, int32_t *__restrict__ ovf_rows, int32_t *__restrict__ n_ovf,
+    int32_t *__restrict__ status)
+{
+    __shared__ int wsum[SNT / 64];
+    __shared__ int n_before;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r0 = blockIdx.x * SNT;
+    if (tid == 0)
+        n_before = 0;
+    __syncthreads();
+    // overflow rows of the blocks before this one: 8 loads per thread in
+    // flight (rows clamped, flags masked), per-thread counts summed in LDS
+    int mine = 0;
+    for (int t0 = 0; t0 < r0; t0 += 8 * SNT) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = row_nnz[min(t0 + u * SNT + tid, r0 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            mine += (t0 + u * SNT + tid < r0 && v[u] > K) ? 1 : 0;
+    }
+    if (mine)
+        atomicAdd(&n_before, mine);
+    // this block: one flag per thread, slots by a block scan (ballots per
+    // wave, wave totals in LDS)
+    const int t = r0 + tid;
+    const bool f = t < T && row_nnz[t] > K;
+    const unsigned long long m = __ballot(f);
+    if (lane == 0)
+        wsum[wv] = __popcll(m);
+    __syncthreads();
+    int before = n_before;
+    for (int w = 0; w < wv; ++w)
+        before += wsum[w];
+    const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
+    if (t < T) {
+        row_slot[t] = f ? slot : -1;
+        if (f && slot < max_ovf)
+            ovf_rows[slot] = t;
+    }
+    if (tid == SNT - 1 && r0 + SNT >= T) { // last block: the true total
+        int total = n_before;
+        for (int w = 0; w < SNT / 64; ++w)
+            total += wsum[w];
+        *n_ovf = total;
+        if (total > max_ovf)
+            raise_status(status, TWELL_DEV_OVF_CAPACITY);
+    }
+}
 
 template <int DT>
 __global__ __launch_bounds__(DNT) void hyb_dense_kernel(
     const int32_t *__restrict__ count, const int16_t *__restrict__ col,
-    const void *__restrict__ val, const int32_t *__restrict__ row_nnz, int T, int nt, int W,
-    int K, int dff, int max_ovf, int32_t *__restrict__ row_slot, int32_t *__restrict__ ovf_rows,
-    int32_t *__restrict__ n_ovf, void *__restrict__ dense, int32_t *__restrict__ status)
+    const void *__restrict__ val, int nt, int W, int dff, int max_ovf,
+    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf,
+    void *__restrict__ dense, int32_t *__restrict__ status)
 {
     using S = typename elem<DT>::storage;
-    __shared__ int rows[BLK];
-    __shared__ int n_here, n_before;
     __shared__ __attribute__((aligned(16))) uint8_t rowbuf[ROW_LDS];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int r0 = blockIdx.x * BLK;
-    if (tid == 0)
-        n_before = 0;
-    __syncthreads();
-    // overflow rows before this block: 8 loads per thread in flight (rows
-    // clamped, flags masked), per-thread counts summed in LDS
-    int mine = 0;
-    for (int t0 = 0; t0 < r0; t0 += 8 * DNT) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = row_nnz[min(t0 + u * DNT + tid, r0 - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            mine += (t0 + u * DNT + tid < r0 && v[u] > K) ? 1 : 0;
-    }
-    if (mine)
-        atomicAdd(&n_before, mine);
-    __syncthreads();
-    const int before = n_before;
-    // this block's rows: wave 0 numbers them (one ballot over lanes < BLK)
-    if (wv == 0) {
-        const int t = r0 + lane;
-        const bool f = lane < BLK && t < T && row_nnz[t] > K;
-        const unsigned long long m = __ballot(f);
-        const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
-        if (lane < BLK && t < T) {
-            row_slot[t] = f ? slot : -1;
-            if (f && slot < max_ovf)
-                ovf_rows[slot] = t;
-        }
-        if (f)
-            rows[__popcll(m & ((1ull << lane) - 1ull))] = t;
-        if (lane == 0) {
-            n_here = __popcll(m);
-            if (r0 + BLK >= T) { // last block: the true total
-                *n_ovf = before + __popcll(m);
-                if (before + __popcll(m) > max_ovf)
-                    raise_status(status, TWELL_DEV_OVF_CAPACITY);
-            }
-        }
-    }
-    __syncthreads();
-    // dense rows of this block's overflow rows (within capacity), each built
-    // in LDS (zeros, then the row's entries) and stored with 16-byte lanes;
-    // rows wider than the LDS buffer go straight to memory
+    const int slot = blockIdx.x, tid = threadIdx.x;
+    if (slot >= min(*n_ovf, max_ovf))
+        return;
+    const int t = ovf_rows[slot];
+    S *drow = (S *)dense + (size_t)slot * dff;
+    // rows wider than the LDS buffer are built straight in memory
     const bool in_lds = (size_t)dff * sizeof(S) <= ROW_LDS;
-    for (int k = 0; k < n_here; ++k) {
-        const int slot = before + k;
-        if (slot >= max_ovf)
-            break;
-        const int t = rows[k];
-        S *drow = (S *)dense + (size_t)slot * dff;
-        S *brow = in_lds ? (S *)rowbuf : drow;
-        if (in_lds)
-            for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
-                ((uint4 *)rowbuf)[i] = make_uint4(0, 0, 0, 0);
-        else
-            for (int i = tid; i < dff; i += DNT)
-                drow[i] = S(0);
-        __syncthreads();
-        // every slot of the row's TwELL tiles, 8 per thread at a time (loads
-        // unconditional, stores of the stored slots only)
-        const size_t src = (size_t)t * nt * W;
-        const int nslot = nt * W;
-        for (int q0 = 0; q0 < nslot; q0 += 8 * DNT) {
-            int c[8], n[8];
-            S v[8];
+    S *brow = in_lds ? (S *)rowbuf : drow;
+    if (in_lds)
+        for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
+            ((uint4 *)rowbuf)[i] = make_uint4(0, 0, 0, 0);
+    else
+        for (int i = tid; i < dff; i += DNT)
+            drow[i] = S(0);
+    __syncthreads();
+    // every slot of the row's TwELL tiles, 8 per thread at a time (loads
+    // unconditional, stores of the stored slots only)
+    const size_t src = (size_t)t * nt * W;
+    const int nslot = nt * W;
+    for (int q0 = 0; q0 < nslot; q0 += 8 * DNT) {
+        int c[8], n[8];
+        S v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int q = min(q0 + u * DNT + tid, nslot - 1);
-                n[u] = count[(size_t)t * nt + q / W];
-                c[u] = col[src + q];
-                v[u] = ((const S *)val)[src + q];
-            }
+        for (int u = 0; u < 8; ++u) {
+            const int q = min(q0 + u * DNT + tid, nslot - 1);
+            n[u] = count[(size_t)t * nt + q / W];
+            c[u] = col[src + q];
+            v[u] = ((const S *)val)[src + q];
+        }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int q = q0 + u * DNT + tid;
-                if (q < nslot && q % W < min(n[u], W)) {
-                    if (c[u] >= 0 && c[u] < dff)
-                        brow[c[u]] = v[u];
-                    else
-                        raise_status(status, TWELL_DEV_BAD_INDEX);
-                }
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u * DNT + tid;
+            if (q < nslot && q % W < min(n[u], W)) {
+                if (c[u] >= 0 && c[u] < dff)
+                    brow[c[u]] = v[u];
+                else
+                    raise_status(status, TWELL_DEV_BAD_INDEX);
             }
         }
+    }
+    if (in_lds) {
         __syncthreads();
-        if (in_lds) {
-            for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
-                ((uint4 *)drow)[i] = ((const uint4 *)rowbuf)[i];
-            __syncthreads();
-        }
+        for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
+            ((uint4 *)drow)[i] = ((const uint4 *)rowbuf)[i];
     }
 }
 
@@ -190,11 +192,16 @@ hipError_t launch(const twell_t *h, const hybrid_t *o, int32_t *status, Timer &t
                            o->ell_val);
         tm.mark("hyb_rows_kernel");
     }
-    hipLaunchKernelGGL(hyb_dense_kernel<DT>, dim3(h->T > 0 ? (h->T + BLK - 1) / BLK : 1),
-                       dim3(DNT), 0, s, h->count, h->col, h->val, o->row_nnz, h->T, nt, h->width,
-                       o->K, h->d_ff, o->max_ovf, o->row_slot, o->ovf_rows, o->n_ovf, o->dense,
-                       status);
-    tm.mark("hyb_dense_kernel");
+    hipLaunchKernelGGL(hyb_slots_kernel, dim3(h->T > 0 ? (h->T + SNT - 1) / SNT : 1), dim3(SNT),
+                       0, s, o->row_nnz, h->T, o->K, o->max_ovf, o->row_slot, o->ovf_rows,
+                       o->n_ovf, status);
+    tm.mark("hyb_slots_kernel");
+    if (o->max_ovf > 0 && h->T > 0) {
+        hipLaunchKernelGGL(hyb_dense_kernel<DT>, dim3(o->max_ovf), dim3(DNT), 0, s, h->count,
+                           h->col, h->val, nt, h->width, h->d_ff, o->max_ovf, o->ovf_rows,
+                           o->n_ovf, o->dense, status);
+        tm.mark("hyb_dense_kernel");
+    }
     return hipGetLastError();
 }
 
