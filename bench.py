@@ -103,10 +103,10 @@ def kernel_sources_sha256(kernel):
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    counter summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what
-    the same counter reads for a plain copy of known size), or None with the
-    reason."""
+    """Bytes below L2 (MALL or HBM) per launch of `kernel` on `workload` from
+    the committed counter summary (rocprofv3 read requests counted by size,
+    plus WRITE_SIZE; both exact on a plain copy of known size), or None with
+    the reason."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None, "no counter summary"
@@ -117,12 +117,9 @@ def measured_traffic(kernel, workload):
         return None, "no counters for this kernel and workload"
     if k["sources_sha256"] != kernel_sources_sha256(kernel):
         return None, "kernel sources changed since the counters were taken"
-    cal = rec["copy_calibration"]
-    sf = cal["bytes"] / (cal["fetch_kib"] * 1024.0)
-    sw = cal["bytes"] / (cal["write_kib"] * 1024.0)
-    b = k["fetch_kib"] * 1024.0 * sf + k["write_kib"] * 1024.0 * sw
-    return round(b), (f"rocprofv3 FETCH_SIZE {k['fetch_kib']:.0f} KiB x {sf:.3f} + WRITE_SIZE "
-                      f"{k['write_kib']:.0f} KiB x {sw:.3f} per launch (copy-calibrated)")
+    b = k["read_bytes"] + k["write_kib"] * 1024.0
+    return round(b), (f"rocprofv3 per launch: read requests by size (32/64/128 B) = "
+                      f"{k['read_bytes'] / 1e6:.1f} MB, WRITE_SIZE {k['write_kib']:.0f} KiB")
 
 
 def parse():
