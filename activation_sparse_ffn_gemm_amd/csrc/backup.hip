@@ -49,8 +49,12 @@ using CU = ng::Cfg<128, 128, 2, 2>;
 // measured on the 1.5B skewed layer's products against 128 x 128 tiles of
 // four waves: y_O 49 -> 35 us, dx_O 71 -> 56 us, dW alike)
 using CW = ng::Cfg<256, 256, 2, 4, 2, 128>;
+// y_O (the forward's split-K product): 128 x 128 tiles of four waves, two
+// workgroups per CU
+using CY = ng::Cfg<128, 128, 2, 2, 2, 128>;
+using DX = ng::Cfg<128, 128, 2, 2, 3, 64>; // the backward's dx_O and dW tiles
 constexpr int TILE = 128;  // u/da tiles
-constexpr int WT = 256;    // split-K and dW tiles
+constexpr int WT = 256;    // dx split-K and dW tiles
 
 template <int DT> using Store = typename elem<DT>::storage;
 
@@ -61,10 +65,10 @@ int pad_rows(int max_ovf) { return (max_ovf + WT - 1) / WT * WT; }
 // CU far too little to overlap; aim at 512 workgroups over the capacity's
 // tiles (two per CU when about half the capacity is used; tiles wholly past
 // n_ovf return at once), at most 16 splits, at least 16 K steps each.
-int split_k(int R, int dm, int nk)
+int split_k(int R, int dm, int nk, int tile = WT, int target = 512)
 {
-    const int tiles = (R / WT) * ((dm + WT - 1) / WT);
-    int S = std::max(1, 512 / std::max(tiles, 1));
+    const int tiles = (R / tile) * ((dm + tile - 1) / tile);
+    int S = std::max(1, target / std::max(tiles, 1));
     S = std::min(S, 16);
     S = std::min(S, std::max(1, nk / 16));
     return S;
@@ -213,9 +217,9 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
                                             ? own[ni][e]
                                             : (which == 1 ? oth[ni][e] : hv[ni][e]);
                         if constexpr (DT == TWELL_BF16) {
-                            const uint16_t hi = f32_to_bf16(v);
+                            const uint32_t hl = f32_to_bf16_hilo(v);
                             *(uint16_t *)(Lq + r * P + c * 2) =
-                                part == 0 ? hi : f32_to_bf16(v - bf16_to_f32(hi));
+                                (uint16_t)(part == 0 ? hl : hl >> 16);
                         } else {
                             *(float *)(Lq + r * P + c * 4) = v;
                         }
@@ -242,15 +246,16 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
 // d_ff each. Segment q reads A array q (arrays `R dff` elements apart, K
 // along their rows) and weight matrix w0 (q >> BSHIFT == 0) or w1, stored
 // [d_ff][d_model], i.e. K-major: read through the transposing LDS loads.
-template <int DT, int NSEG, int BSHIFT>
+template <class C, int DT, int NSEG, int BSHIFT>
 DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ w0,
                      const uint8_t *__restrict__ w1, int n, int dm, int dff, int R, int S,
                      float *__restrict__ part, int bx, int by, int sp, uint8_t *L)
 {
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
-    constexpr int KS = CW::ROWB / esz; // K per step
-    const int m0 = by * WT, d0 = bx * WT;
+    constexpr int KS = C::ROWB / esz; // K per step
+    static_assert(C::BM == C::BN, "square tiles");
+    const int m0 = by * C::BM, d0 = bx * C::BN;
     if (m0 >= n)
         return;
     const size_t rowbytes = (size_t)dff * esz, plane = (size_t)R * dff * esz,
@@ -262,24 +267,24 @@ DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ 
     const ptrdiff_t w01 = w1 - w0;
     auto off = [&](int kt) {
         const int q = kt / spseg, kk = kt % spseg;
-        return ng::StepOff{q * plane + (size_t)kk * CW::ROWB,
+        return ng::StepOff{q * plane + (size_t)kk * C::ROWB,
                            (size_t)((q >> BSHIFT) ? w01 : 0) + (size_t)kk * KS * wrow};
     };
-    ng::Acc<CW> acc;
-    ng::mainloop_mixed<CW, DT, ng::KC, ng::KM>(L, rowa, rowb, off, kt0, kt1, acc, 1 << 30,
+    ng::Acc<C> acc;
+    ng::mainloop_mixed<C, DT, ng::KC, ng::KM>(L, rowa, rowb, off, kt0, kt1, acc, 1 << 30,
                                                dm - d0);
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<C>(), wn = ng::wave_n<C>();
     float *p = part + (size_t)sp * R * dm;
 #pragma unroll
-    for (int mi = 0; mi < CW::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < CW::NI; ++ni)
+        for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 // rows past n are padding rows of the R-row partial (never
                 // read): only the column needs a test, no branch per row
-                const int m = m0 + ng::acc_row<CW>(wm, mi, e, lane);
-                const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
+                const int m = m0 + ng::acc_row<C>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<C>(wn, ni, lane);
                 if (d < dm)
                     p[(size_t)m * dm + d] = acc.v[mi][ni][e];
             }
@@ -290,7 +295,7 @@ DEVI void rowsw_tile(const uint8_t *__restrict__ a, const uint8_t *__restrict__ 
 // for bf16. Both operands run along the rows m, the contraction index: both
 // are read K-major. Rows at or past n hold zeros in both (the u/da epilogue
 // stores its whole tiles, the gather zero rows), so whole K steps are safe.
-template <int DT>
+template <class C, int DT>
 DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xo, int n, int dm,
                   int dff, int R, float *__restrict__ dwd, float *__restrict__ dwu,
                   float *__restrict__ dwg, int bx, int by, int z, uint8_t *L)
@@ -298,10 +303,10 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xo
     using E = elem<DT>;
     constexpr int esz = sizeof(typename E::storage);
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    constexpr int KS = CW::ROWB / esz; // rows per K step
+    constexpr int KS = C::ROWB / esz; // rows per K step
     if (n <= 0)
         return;
-    const int d0 = bx * WT, i0 = by * WT;
+    const int d0 = bx * C::BN, i0 = by * C::BM;
     const size_t plane = (size_t)R * dff * esz, irow = (size_t)dff * esz,
                  xrow = (size_t)dm * esz;
     const uint8_t *ta = it + (size_t)z * NH * plane;             // a / du / dg, hi first
@@ -314,19 +319,19 @@ DEVI void dw_tile(const uint8_t *__restrict__ it, const uint8_t *__restrict__ xo
         const int q = kt / spseg, kk = kt % spseg;
         return ng::StepOff{q * plane + (size_t)kk * KS * irow, (size_t)kk * KS * xrow};
     };
-    ng::Acc<CW> acc;
-    ng::mainloop_mixed<CW, DT, ng::KM, ng::KM>(L, rowa, rowb, off, 0, nk, acc, dff - i0, dm - d0);
+    ng::Acc<C> acc;
+    ng::mainloop_mixed<C, DT, ng::KM, ng::KM>(L, rowa, rowb, off, 0, nk, acc, dff - i0, dm - d0);
     // the tile is the backup rows' share of dW, written whole: the ELL rows'
     // share is added to it by the neuron pass, which runs next
-    const int lane = threadIdx.x & 63, wm = ng::wave_m<CW>(), wn = ng::wave_n<CW>();
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<C>(), wn = ng::wave_n<C>();
 #pragma unroll
-    for (int mi = 0; mi < CW::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < CW::NI; ++ni)
+        for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int i = i0 + ng::acc_row<CW>(wm, mi, e, lane);
-                const int d = d0 + ng::acc_col<CW>(wn, ni, lane);
+                const int i = i0 + ng::acc_row<C>(wm, mi, e, lane);
+                const int d = d0 + ng::acc_col<C>(wn, ni, lane);
                 if (i < dff && d < dm)
                     out[(size_t)i * dm + d] = acc.v[mi][ni][e];
             }
@@ -365,19 +370,19 @@ __global__ __launch_bounds__(UD_NT, 1) void bk_ud_kernel(
 }
 
 template <int DT, int NH>
-__global__ __launch_bounds__(CW::NT, 1) void bk_y_kernel(
+__global__ __launch_bounds__(CY::NT, 2) void bk_y_kernel(
     const uint8_t *__restrict__ a, const uint8_t *__restrict__ wd,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
     float *__restrict__ part)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
-    rowsw_tile<DT, NH, 4>(a, wd, wd, n_rows(n_ovf_p, max_ovf), dm, dff, R, S, part, blockIdx.x,
-                          blockIdx.y, blockIdx.z, L);
+    __shared__ __attribute__((aligned(16))) uint8_t L[CY::LDS];
+    rowsw_tile<CY, DT, NH, 4>(a, wd, wd, n_rows(n_ovf_p, max_ovf), dm, dff, R, S, part,
+                              blockIdx.x, blockIdx.y, blockIdx.z, L);
 }
 
 // backward: the dx_O tiles (K split), then the dW tiles
 template <int DT>
-__global__ __launch_bounds__(CW::NT, 1) void bk_dxdw_kernel(
+__global__ __launch_bounds__(DX::NT, DX::NT <= 256 ? 3 : 1) void bk_dxdw_kernel(
     const uint8_t *__restrict__ inter, const uint8_t *__restrict__ wu,
     const uint8_t *__restrict__ wg, const uint8_t *__restrict__ xo,
     const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm, int dff, int R, int S,
@@ -385,24 +390,25 @@ __global__ __launch_bounds__(CW::NT, 1) void bk_dxdw_kernel(
     float *__restrict__ dwg, int n_dx)
 {
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    __shared__ __attribute__((aligned(16))) uint8_t L[CW::LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t L[DX::LDS];
     const int n = n_rows(n_ovf_p, max_ovf);
     if (n <= 0)
         return;
     int b = blockIdx.x;
-    const int nd = (dm + WT - 1) / WT;
+    const int nd = (dm + DX::BN - 1) / DX::BN;
     if (b < n_dx) {
         // segments (du hi, du lo, dg hi, dg lo) against (W_u, W_u, W_g, W_g),
         // or (du, dg) against (W_u, W_g); du is plane NH of inter (after a)
-        const int mt = R / WT;
+        const int mt = R / DX::BM;
         const size_t plane = (size_t)R * dff * sizeof(Store<DT>);
-        rowsw_tile<DT, 2 * NH, NH == 2 ? 1 : 0>(inter + NH * plane, wu, wg, n, dm, dff, R, S,
-                                                 part, b % nd, (b / nd) % mt, b / (nd * mt), L);
+        rowsw_tile<DX, DT, 2 * NH, NH == 2 ? 1 : 0>(inter + NH * plane, wu, wg, n, dm, dff, R, S,
+                                                     part, b % nd, (b / nd) % mt, b / (nd * mt),
+                                                     L);
         return;
     }
     b -= n_dx;
-    const int ni = (dff + WT - 1) / WT;
-    dw_tile<DT>(inter, xo, n, dm, dff, R, dwd, dwu, dwg, b % nd, (b / nd) % ni, b / (nd * ni), L);
+    const int ni = (dff + DX::BM - 1) / DX::BM;
+    dw_tile<DX, DT>(inter, xo, n, dm, dff, R, dwd, dwu, dwg, b % nd, (b / nd) % ni, b / (nd * ni), L);
 }
 
 } // namespace
@@ -423,7 +429,9 @@ BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
     const size_t esz = dt == TWELL_BF16 ? 2 : 4, nh = dt == TWELL_BF16 ? 2 : 1;
     L.R = pad_rows(max_ovf);
     const int nseg = (int)(bwd ? 2 * nh : nh);
-    L.S = split_k(L.R, dm, nseg * (int)(dff * esz / CW::ROWB));
+    L.S = bwd ? split_k(L.R, dm, nseg * (int)(dff * esz / DX::ROWB), DX::BM,
+                        DX::BM == 256 ? 512 : 2048)
+              : split_k(L.R, dm, nseg * (int)(dff * esz / CY::ROWB), CY::BM, 2048);
     size_t o = 0;
     L.inter = o; o += up256((bwd ? 3 : 1) * nh * L.R * dff * esz);
     L.xo = o;    o += bwd ? up256(2 * (size_t)L.R * dm * esz) : 0;
@@ -444,8 +452,8 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
                        h->dense, (void *)(ws + L.inter));
     tm.mark("bk_a_kernel");
     constexpr int NH = DT == TWELL_BF16 ? 2 : 1;
-    hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + WT - 1) / WT, L.R / WT, L.S),
-                       dim3(CW::NT), 0, s, (const uint8_t *)(ws + L.inter),
+    hipLaunchKernelGGL((bk_y_kernel<DT, NH>), dim3((dm + CY::BN - 1) / CY::BN, L.R / CY::BM, L.S),
+                       dim3(CY::NT), 0, s, (const uint8_t *)(ws + L.inter),
                        (const uint8_t *)wd, h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
                        (float *)(ws + L.part));
     tm.mark("bk_y_kernel");
@@ -471,9 +479,9 @@ void bk_dxdw_dt(const hybrid_t *h, const void *wu, const void *wg, int dm, float
 {
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, true);
-    const int nd = (dm + WT - 1) / WT;
-    const int n_dx = nd * (L.R / WT) * L.S, n_dw = nd * ((dff + WT - 1) / WT) * 3;
-    hipLaunchKernelGGL((bk_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(CW::NT), 0, s,
+    const int nd = (dm + DX::BN - 1) / DX::BN;
+    const int n_dx = nd * (L.R / DX::BM) * L.S, n_dw = nd * ((dff + DX::BM - 1) / DX::BM) * 3;
+    hipLaunchKernelGGL((bk_dxdw_kernel<DT>), dim3(n_dx + n_dw), dim3(DX::NT), 0, s,
                        (const uint8_t *)(ws + L.inter), (const uint8_t *)wu, (const uint8_t *)wg,
                        (const uint8_t *)(ws + L.xo), h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
                        (float *)(ws + L.part), dwd, dwu, dwg, n_dx);

@@ -28,6 +28,22 @@ DEVI uint16_t f32_to_bf16(float f)
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
+// The same rounding (nearest, ties to even) by gfx950's conversion
+// instruction, two values at once: low half a, high half b. NaN inputs are
+// not supported by the layer and may come out with another quiet payload.
+DEVI uint32_t f32x2_to_bf16x2(float a, float b)
+{
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// hi = bf16(v), lo = bf16(v - hi): the bf16 pair carrying v to about 16
+// significant bits, as (hi, lo) in the low and high halves
+DEVI uint32_t f32_to_bf16_hilo(float v)
+{
+    const __bf16 hi = (__bf16)v;
+    const bf16x2_t p = {hi, (__bf16)(v - (float)hi)};
+    return __builtin_bit_cast(uint32_t, p);
+}
 
 // Element type traits: how many elements a 16-byte chunk holds and how to widen.
 template <int DT> struct elem;
