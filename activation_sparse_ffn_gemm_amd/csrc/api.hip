@@ -45,13 +45,28 @@ int check_dff(int32_t dff)
                                                                               : TWELL_E_SHAPE;
 }
 
+// dtype, token count, d_model and d_ff within the documented limits
+bool sizes_ok(int dt, int32_t T, int32_t dm, int32_t dff)
+{
+    return dtype_ok(dt) && T >= 0 && T <= TWELL_MAX_ROWS && !check_dm((twell_dtype)dt, dm) &&
+           !check_dff(dff);
+}
+
+// a hybrid's K and backup capacity for T rows of d_ff columns; ELL slots are
+// numbered t * K + s in 32-bit integers (the backward's transpose)
+bool hybrid_sizes_ok(int32_t T, int32_t dff, int32_t K, int32_t max_ovf)
+{
+    return K >= 1 && K <= dff && K <= 32767 && max_ovf >= 0 && max_ovf <= TWELL_MAX_ROWS &&
+           (int64_t)T * K <= INT32_MAX;
+}
+
 int check_twell(const twell_t *h, twell_dtype dt)
 {
     if (!h)
         return TWELL_E_NULL;
     if (!dtype_ok(h->dtype) || h->dtype != dt)
         return TWELL_E_DTYPE;
-    if (h->T < 0 || h->width < 1 || h->width > TWELL_TILE_C)
+    if (h->T < 0 || h->T > TWELL_MAX_ROWS || h->width < 1 || h->width > TWELL_TILE_C)
         return TWELL_E_SHAPE;
     if (int rc = check_dff(h->d_ff))
         return rc;
@@ -66,11 +81,7 @@ int check_hybrid(const hybrid_t *h, twell_dtype dt)
         return TWELL_E_NULL;
     if (!dtype_ok(h->dtype) || h->dtype != dt)
         return TWELL_E_DTYPE;
-    if (h->T < 0 || h->K < 1 || h->K > h->d_ff || h->K > 32767 || h->max_ovf < 0)
-        return TWELL_E_SHAPE;
-    // ELL slots are numbered t * K + s in 32-bit integers (the backward's
-    // transpose of the pattern)
-    if ((int64_t)h->T * h->K > INT32_MAX)
+    if (h->T < 0 || h->T > TWELL_MAX_ROWS || !hybrid_sizes_ok(h->T, h->d_ff, h->K, h->max_ovf))
         return TWELL_E_SHAPE;
     if (int rc = check_dff(h->d_ff))
         return rc;
@@ -128,7 +139,7 @@ const char *twell_status_str(int code)
 
 size_t twell_gate_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff)
 {
-    if (!dtype_ok(dt) || T < 0 || check_dm(dt, d_model) || check_dff(d_ff))
+    if (!sizes_ok(dt, T, d_model, d_ff))
         return 0;
     return T <= TWELL_DECODE_T ? dec_gate_workspace(dt, T, d_model, d_ff) : 0;
 }
@@ -145,7 +156,7 @@ int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, 
         return rc;
     if (int rc = check_dm(dt, d_model))
         return rc;
-    if (T < 0 || out->T != T)
+    if (T < 0 || T > TWELL_MAX_ROWS || out->T != T)
         return TWELL_E_SHAPE;
     if (!a16(x) || !a16(wg_t))
         return TWELL_E_ALIGN;
@@ -163,7 +174,7 @@ int twell_gate_pack(twell_dtype dt, const void *x, const void *wg_t, int32_t T, 
 size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                  int32_t width)
 {
-    if (!dtype_ok(dt) || T < 0 || d_model < 1 || d_ff < TWELL_TILE_C || width < 1)
+    if (!sizes_ok(dt, T, d_model, d_ff) || width < 1 || width > TWELL_TILE_C)
         return 0;
     return fwd_workspace(dt, T, d_model, d_ff, width);
 }
@@ -199,8 +210,8 @@ int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *w
 size_t twell_decode_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                     int32_t width)
 {
-    if (!dtype_ok(dt) || T < 0 || T > TWELL_DECODE_T || check_dm(dt, d_model) ||
-        check_dff(d_ff) || width < 1 || width > TWELL_TILE_C)
+    if (!sizes_ok(dt, T, d_model, d_ff) || T > TWELL_DECODE_T || width < 1 ||
+        width > TWELL_TILE_C)
         return 0;
     return dec_layer_workspace(dt, T, d_model, d_ff, width);
 }
@@ -243,7 +254,7 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
 size_t hybrid_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                   int32_t K, int32_t max_ovf)
 {
-    if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0)
+    if (!sizes_ok(dt, T, d_model, d_ff) || !hybrid_sizes_ok(T, d_ff, K, max_ovf))
         return 0;
     return hyb_fwd_workspace(dt, T, d_model, max_ovf, d_ff, K);
 }
@@ -277,8 +288,7 @@ int hybrid_ffn_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void 
 size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                   int32_t K, int32_t max_ovf)
 {
-    if (!dtype_ok(dt) || T < 0 || d_model <= 0 || d_ff <= 0 || K <= 0 || max_ovf < 0 ||
-        (int64_t)T * K > INT32_MAX)
+    if (!sizes_ok(dt, T, d_model, d_ff) || !hybrid_sizes_ok(T, d_ff, K, max_ovf))
         return 0;
     return bwd_workspace_layout(dt, T, d_model, d_ff, K, max_ovf);
 }

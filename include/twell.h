@@ -36,7 +36,8 @@
  *   - Element types: TWELL_BF16 (bfloat16 storage, float32 accumulation) or
  *     TWELL_F32. y, dx and every weight gradient are float32.
  *   - Limits: d_model % 64 == 0 and 64 <= d_model <= 4096 (2048 for F32);
- *     d_ff % 128 == 0 and d_ff <= 32768; T >= 0. With T == 0 the token
+ *     d_ff % 128 == 0 and d_ff <= 32768; 0 <= T <= TWELL_MAX_ROWS; a
+ *     hybrid's max_ovf <= TWELL_MAX_ROWS. With T == 0 the token
  *     arrays (x, dy, y, dx) may be NULL; the forward calls do nothing and the
  *     backward writes zero weight gradients.
  *     x, dy, weights, y, dx and gradients must be 16-byte aligned.
@@ -51,7 +52,14 @@
 extern "C" {
 #endif
 
+/* Element type. In C++ the enumeration has a fixed 32-bit underlying type, so
+ * any int32 a caller passes is a value of the type: the calls check it and
+ * return TWELL_E_DTYPE for anything but the two below. */
+#ifdef __cplusplus
+typedef enum : int32_t { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+#else
 typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+#endif
 
 enum {
     TWELL_OK = 0,
@@ -72,6 +80,7 @@ enum {
 };
 
 #define TWELL_TILE_C 128 /* columns per TwELL tile: the gate kernel's N tile */
+#define TWELL_MAX_ROWS (1 << 28) /* most tokens, and most backup rows, a call takes */
 #define TWELL_DECODE_T 64 /* calls with at most this many tokens take the
                              few-token (decode) kernels; twell_decode_fwd's limit */
 
@@ -177,6 +186,8 @@ int twell_ffn_fwd(twell_dtype dt, const void *x, const twell_t *h, const void *w
                   size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
                   void *stream);
 
+/* Workspace bytes twell_ffn_fwd needs (0 when it needs none, and on invalid
+ * arguments). */
 size_t twell_fwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                  int32_t width);
 
@@ -283,6 +294,7 @@ int hybrid_ffn_bwd(twell_dtype dt, const void *x, const void *dy, const hybrid_t
                    size_t workspace_bytes, int32_t *dev_status, twell_timing_t *timing,
                    void *stream);
 
+/* Workspace bytes hybrid_ffn_bwd needs (0 on invalid arguments). */
 size_t hybrid_bwd_workspace_bytes(twell_dtype dt, int32_t T, int32_t d_model, int32_t d_ff,
                                   int32_t K, int32_t max_ovf);
 
