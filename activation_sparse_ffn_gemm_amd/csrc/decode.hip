@@ -7,10 +7,14 @@
 // The work is split into three phases, each spread over the whole chip:
 //
 //  1. gate partials. A workgroup item is one TwELL tile (128 neurons) and one
-//     of ks slices of d_model; its eight waves split the slice again, run bf16
-//     MFMAs with both operands straight from global memory (x is tiny, the W_g
-//     rows stream once), and sum their partial tiles in LDS in a fixed order.
-//     The item's [T][128] partial goes to the workspace.
+//     of ks slices of d_model; the item's [T][128] partial goes to the
+//     workspace. Up to GEMV_T tokens the product is a matrix-vector one: the
+//     slice of x sits in LDS, eight lanes cover one 128-byte line of a W_g row
+//     (a wave load reads eight whole lines), each lane keeps its own running
+//     dot products over the slice's lines and the eight lanes of a row are
+//     summed at the end. With more tokens the eight waves split the slice
+//     again, run bf16 MFMAs with both operands straight from global memory,
+//     and sum their partial tiles in LDS in a fixed order.
 //  2. pack + up. A wave item is one (token, tile): it sums the ks partials in
 //     slice order, packs the tile with two ballots into the TwELL arrays, and
 //     for each stored nonzero (i, h) gathers wu_t[i] and stores
@@ -42,6 +46,8 @@ constexpr int LP = TWELL_TILE_C + 8; // LDS pitch of a partial row (floats): row
 constexpr int LISTD = 2048;    // entries staged per pass of the down phase
 constexpr int GD = 8;          // wd slices in flight per wave in the down phase
 constexpr int GATE_ITEMS = 256; // aim: about one gate item per compute unit
+constexpr int GEMV_T = 4;      // most tokens of the matrix-vector gate
+constexpr int GLB = 8;         // W_g lines per row in flight per lane (matrix-vector gate)
 
 // Host-computed geometry of one decode call.
 struct DecPlan {
@@ -50,6 +56,8 @@ struct DecPlan {
     int ks, spw; // d_model slices per tile (gate items), K steps per wave
     int tcm;     // rows of a wave's LDS partial: min(T, TC)
     int nsl;     // 1 KB slices of a d_model row (down items per token)
+    bool gemv;   // matrix-vector gate: item k covers 128-byte lines [k lpi, (k + 1) lpi)
+    int nl, lpi; // 128-byte lines of a d_model row, lines per gate item
     size_t a_off, bytes; // workspace: partials [ks][T][dff] at 0, a [T][nt][W] at a_off
 };
 
@@ -70,6 +78,13 @@ DecPlan dec_plan(int dt, int T, int dm, int dff, int W, bool with_gate)
     ks = std::min(ks, std::max(1, 4 * P.nsteps / std::max(T, 1)));
     P.spw = (P.nsteps + ks * DW - 1) / (ks * DW);
     P.ks = (P.nsteps + P.spw * DW - 1) / (P.spw * DW);
+    P.gemv = T <= GEMV_T;
+    P.nl = dm * esz / 128; // d_model % 64 == 0: whole lines
+    if (P.gemv) {
+        const int ks0 = std::max(1, std::min(GATE_ITEMS / P.nt, P.nl));
+        P.lpi = (P.nl + ks0 - 1) / ks0;
+        P.ks = (P.nl + P.lpi - 1) / P.lpi;
+    }
     P.tcm = std::min(T, TC);
     P.nsl = (dm * esz + 1023) / 1024;
     const size_t part = with_gate ? (size_t)P.ks * T * dff * 4 : 0;
@@ -212,6 +227,74 @@ DEVI void gate_part_item(const DecPlan &P, const uint8_t *__restrict__ x,
         }
         __syncthreads(); // lds is rewritten by the next chunk
     }
+}
+
+// Matrix-vector form of phase 1 (T <= GEMV_T, TT = T rounded up to a power of
+// two): item = (tile, slice of lpi lines). Lane 8q + c of wave w covers
+// 16-byte chunk c of one line of rows 16w + q and 16w + 8 + q; xs holds the
+// slice of x, [T][lpi * 8] chunks.
+template <int DT, int TT>
+DEVI void gate_gemv_item(const DecPlan &P, const uint8_t *__restrict__ x,
+                         const uint8_t *__restrict__ wg, int item, float *__restrict__ part,
+                         uint4 *xs)
+{
+    using E = elem<DT>;
+    constexpr int EPL = E::per16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 3, c = lane & 7;
+    const int j = item / P.ks, k = item % P.ks, n0 = j * TWELL_TILE_C;
+    const int l0 = k * P.lpi, nli = min(P.nl, l0 + P.lpi) - l0;
+    const size_t rowbytes = (size_t)P.nl * 128;
+    for (int i = threadIdx.x; i < P.T * nli * 8; i += DNT) {
+        const int t = i / (nli * 8), r = i % (nli * 8);
+        xs[t * P.lpi * 8 + r] = ldg16(x + (size_t)t * rowbytes + (size_t)l0 * 128 + r * 16);
+    }
+    __syncthreads();
+    const uint8_t *w0 = wg + (size_t)(n0 + 16 * wave + q) * rowbytes + (size_t)l0 * 128 + c * 16;
+    const uint8_t *w1 = w0 + 8 * rowbytes;
+    float acc[2][TT];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            acc[g][t] = 0.f;
+    for (int lb = 0; lb < nli; lb += GLB) {
+        uint4 v[2][GLB];
+#pragma unroll
+        for (int u = 0; u < GLB; ++u) {
+            const int l = min(lb + u, nli - 1); // lines past the slice re-read its last, unused
+            v[0][u] = ldg16(w0 + (size_t)l * 128);
+            v[1][u] = ldg16(w1 + (size_t)l * 128);
+        }
+#pragma unroll
+        for (int u = 0; u < GLB; ++u)
+            if (lb + u < nli) { // uniform
+                float f0[EPL], f1[EPL];
+                E::widen(v[0][u], f0);
+                E::widen(v[1][u], f1);
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    float xf[EPL];
+                    E::widen(xs[min(t, P.T - 1) * P.lpi * 8 + (lb + u) * 8 + c], xf);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        acc[0][t] += f0[e] * xf[e];
+                        acc[1][t] += f1[e] * xf[e];
+                    }
+                }
+            }
+    }
+    // the eight lanes of a row: a fixed butterfly, then lane c == 0 stores
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float s = acc[g][t];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            s += __shfl_xor(s, 4, 64);
+            if (c == 0 && t < P.T)
+                part[((size_t)k * P.T + t) * P.dff + n0 + 16 * wave + 8 * g + q] = s;
+        }
 }
 
 // ---------------------------------------------------------------- phase 2
@@ -465,6 +548,14 @@ __global__ __launch_bounds__(DNT) void dec_gate_part_kernel(
     gate_part_item<DT, NC>(P, x, wg, blockIdx.x, part, smem);
 }
 
+template <int DT, int TT>
+__global__ __launch_bounds__(DNT) void dec_gate_gemv_kernel(
+    DecPlan P, const uint8_t *__restrict__ x, const uint8_t *__restrict__ wg, float *part)
+{
+    extern __shared__ __attribute__((aligned(16))) uint4 xs[];
+    gate_gemv_item<DT, TT>(P, x, wg, blockIdx.x, part, xs);
+}
+
 template <int DT, int NW, int G, bool UP>
 __global__ __launch_bounds__(DNT) void dec_pack_kernel(
     DecPlan P, const uint8_t *__restrict__ x, const uint8_t *__restrict__ wu,
@@ -515,6 +606,19 @@ template <int DT>
 void launch_gate_part(const DecPlan &P, const void *x, const void *wg, float *part, Timer &tm,
                       hipStream_t s)
 {
+    if (P.gemv) {
+        const size_t lds = (size_t)P.T * P.lpi * 128;
+        const uint8_t *xb = (const uint8_t *)x, *wb = (const uint8_t *)wg;
+        const dim3 g(P.nt * P.ks), b(DNT);
+        if (P.T == 1)
+            hipLaunchKernelGGL((dec_gate_gemv_kernel<DT, 1>), g, b, lds, s, P, xb, wb, part);
+        else if (P.T == 2)
+            hipLaunchKernelGGL((dec_gate_gemv_kernel<DT, 2>), g, b, lds, s, P, xb, wb, part);
+        else
+            hipLaunchKernelGGL((dec_gate_gemv_kernel<DT, 4>), g, b, lds, s, P, xb, wb, part);
+        tm.mark("dec_gate_gemv_kernel");
+        return;
+    }
     if (P.T > TC)
         hipLaunchKernelGGL((dec_gate_part_kernel<DT, 2>), dim3(P.nt * P.ks), dim3(DNT),
                            gate_lds(P), s, P, (const uint8_t *)x, (const uint8_t *)wg, part);

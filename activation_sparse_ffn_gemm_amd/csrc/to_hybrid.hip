@@ -47,17 +47,18 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
         const int excl = base + incl - n;
         const size_t src = ((size_t)t * nt + j) * W;
         const size_t dst = (size_t)t * K + excl;
-        // 8 slots at a time: loads unconditional (slot clamped to the tile),
-        // stores masked, so the loads of a lane are all in flight together
+        // 8 slots at a time, all loads of a lane in flight together; only
+        // stored slots are read: each lane reads its own tile, so every load
+        // is a request of its own, and most tiles hold one or two entries
         for (int s0 = 0; s0 < n; s0 += 8) {
             int16_t c[8];
             S v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const size_t q = src + min(s0 + u, W - 1);
-                c[u] = col[q];
-                v[u] = ((const S *)val)[q];
-            }
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < n) {
+                    c[u] = col[src + s0 + u];
+                    v[u] = ((const S *)val)[src + s0 + u];
+                }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (s0 + u < n) {

@@ -69,7 +69,8 @@ KERNEL_SOURCES = {
     "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "bk_ud_kernel": "backup.hip",
     "bk_dxdw_kernel": "backup.hip", "dec_gate_part_kernel": "decode.hip",
     "dec_pack_kernel": "decode.hip", "dec_up_kernel": "decode.hip",
-    "dec_down_kernel": "decode.hip",
+    "dec_down_kernel": "decode.hip", "dec_gate_gemv_kernel": "decode.hip",
+    "dec_pack_up_kernel": "decode.hip",
 }
 
 

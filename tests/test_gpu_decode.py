@@ -1,4 +1,4 @@
-"""GPU parity of twell_decode_fwd (the whole layer for few tokens in one call:
+"""GPU parity of twell_decode_fwd (the whole layer for few tokens in one call,
 three launches) against the oracle, through the C-ABI: its TwELL output
 against the oracle's pre-activations, its y against the oracle's forward."""
 import numpy as np
@@ -37,11 +37,13 @@ def oracle_forward(orc, d, dtype, W):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (8, 2304, 768), (33, 512, 1024),
-                                      (64, 1024, 384), (64, 4096, 256)])
+@pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (2, 256, 384), (3, 1024, 1024),
+                                      (4, 2304, 6144), (5, 512, 256), (8, 2304, 768),
+                                      (33, 512, 1024), (64, 1024, 384), (64, 4096, 256)])
 def test_decode_integer_exact(orc, dtype, T, dm, dff):
-    """Integer inputs: the TwELL and y match the oracle bit for bit (T = 33:
-    a second, one-token chunk in the gate)."""
+    """Integer inputs: the TwELL and y match the oracle bit for bit. T <= 4:
+    the matrix-vector gate (1, 2 and 4 tokens per lane); T = 33: a second,
+    one-token chunk in the MFMA gate."""
     if dtype == "f32" and dm > 2048:
         pytest.skip("fp32 limit is d_model <= 2048")
     announce("decode int", dtype, T, dm, dff)
@@ -88,11 +90,12 @@ def test_decode_agrees_with_two_calls():
     np.testing.assert_allclose(f64(y1), f64(y2), rtol=1e-3, atol=1e-3 * float(y2.abs().max()))
 
 
-def test_decode_width_overflow(orc):
+@pytest.mark.parametrize("T", [1, 4, 12])
+def test_decode_width_overflow(orc, T):
     """Dense rows with W = 8: true counts kept, first 8 entries stored and
-    used, device flag raised."""
-    announce("decode width overflow")
-    d = synth.make_integer_inputs(12, 128, 256, "bf16", 0.02, skew_rows=12)
+    used, device flag raised (matrix-vector and MFMA gates)."""
+    announce("decode width overflow", T)
+    d = synth.make_integer_inputs(T, 128, 256, "bf16", 0.02, skew_rows=T)
     g = orc.gate(f64(d["x"]), f64(d["wg_t"]))
     ref = orc.twell_pack(g, W=8)
     assert ref["overflow"]
