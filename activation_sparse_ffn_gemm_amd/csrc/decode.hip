@@ -45,6 +45,7 @@ constexpr int LP = TWELL_TILE_C + 8; // LDS pitch of a partial row (floats): row
                                      // apart (the two lane halves) land 32 banks apart
 constexpr int LISTD = 2048;    // entries staged per pass of the down phase
 constexpr int GD = 8;          // wd slices in flight per wave in the down phase
+constexpr int SPT = 4;         // TwELL slots per thread per round of the down phase's list
 constexpr int GATE_ITEMS = 256; // aim: about one gate item per compute unit
 constexpr int GEMV_T = 4;      // most tokens of the matrix-vector gate
 constexpr int GLB = 8;         // W_g lines per row in flight per lane (matrix-vector gate)
@@ -458,12 +459,28 @@ DEVI void down_item(const DecPlan &P, const int32_t *__restrict__ count,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int *lcol = (int *)smem;
     float *la = smem + LISTD;
-    int *tstart = (int *)(smem + 2 * LISTD); // [256] tile starts, [256] total
+    int *tstart = (int *)(smem + 2 * LISTD); // [nt] tile starts, [nt] total (nt <= 256)
     float *red = smem + 2 * LISTD + 260;     // [DW][SLE]
     const int t = q / P.nsl, e0 = (q % P.nsl) * SLE;
     const bool in = e0 + lane * EPL < P.dm;
     const size_t rowbytes = (size_t)P.dm * esz;
     const uint8_t *wdl = wd + (size_t)(e0 + lane * EPL) * esz;
+    // The token's slots (tile j, slot s) are q = j W + s. When there are few
+    // enough, every thread requests the column and a of its SPT slots before
+    // the count scan, so both wait on one trip to memory; entries are kept
+    // only where s < the tile's count.
+    const int nslots = P.nt * P.W;
+    const bool ahead = nslots <= SPT * DNT;
+    const size_t tsl = (size_t)t * nslots;
+    int cpre[SPT];
+    float apre[SPT];
+    if (ahead)
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int qs = min((int)threadIdx.x + u * DNT, nslots - 1); // past the end: unused
+            cpre[u] = col[tsl + qs];
+            apre[u] = aw[tsl + qs];
+        }
     if (wave == 0) {
         int run = 0;
         for (int jb = 0; jb < P.nt; jb += 64) {
@@ -475,29 +492,45 @@ DEVI void down_item(const DecPlan &P, const int32_t *__restrict__ count,
             run += __shfl(incl, 63, 64);
         }
         if (lane == 0)
-            tstart[256] = run;
+            tstart[P.nt] = run;
     }
     __syncthreads();
-    const int total = tstart[256];
+    const int total = tstart[P.nt];
     float acc[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
         acc[i] = 0.f;
     for (int p0 = 0; p0 < total; p0 += LISTD) {
-        for (int jj = threadIdx.x; jj < P.nt; jj += DNT) {
-            const int n = min(max(count[(size_t)t * P.nt + jj], 0), P.W), st = tstart[jj];
-            const size_t src = ((size_t)t * P.nt + jj) * P.W;
-            for (int s = max(0, p0 - st); s < n && st + s < p0 + LISTD; ++s) {
-                int c = col[src + s];
-                float a = aw[src + s];
-                if (c < 0 || c >= P.dff) { // corrupt entry: skipped and reported
-                    raise_status(status, TWELL_DEV_BAD_INDEX);
-                    c = 0;
-                    a = 0.f;
+        // list entries [p0, p0 + LISTD): SPT slots per thread per round, the
+        // round's loads in flight together
+        for (int q0 = threadIdx.x; q0 < nslots; q0 += SPT * DNT) {
+            int pos[SPT], c[SPT];
+            float a[SPT];
+#pragma unroll
+            for (int u = 0; u < SPT; ++u) {
+                const int qs = q0 + u * DNT;
+                pos[u] = -1;
+                if (qs < nslots) {
+                    const int j = qs / P.W, sl = qs % P.W, st = tstart[j];
+                    const int e = st + sl - p0;
+                    if (sl < tstart[j + 1] - st && e >= 0 && e < LISTD) {
+                        pos[u] = e;
+                        c[u] = ahead ? cpre[u] : col[tsl + qs];
+                        a[u] = ahead ? apre[u] : aw[tsl + qs];
+                    }
                 }
-                lcol[st + s - p0] = c;
-                la[st + s - p0] = a;
             }
+#pragma unroll
+            for (int u = 0; u < SPT; ++u)
+                if (pos[u] >= 0) {
+                    if (c[u] < 0 || c[u] >= P.dff) { // corrupt entry: skipped and reported
+                        raise_status(status, TWELL_DEV_BAD_INDEX);
+                        c[u] = 0;
+                        a[u] = 0.f;
+                    }
+                    lcol[pos[u]] = c[u];
+                    la[pos[u]] = a[u];
+                }
         }
         __syncthreads();
         const int ne = min(LISTD, total - p0);
