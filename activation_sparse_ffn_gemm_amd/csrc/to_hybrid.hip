@@ -29,27 +29,13 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T)
         return;
-    int total = 0;
-    for (int j0 = 0; j0 < nt; j0 += 64) {
-        const int j = j0 + lane;
-        const int n = j < nt ? min(count[(size_t)t * nt + j], W) : 0;
-        total += __shfl(wave_incl_scan(n, lane), 63, 64);
-    }
-    if (lane == 0)
-        row_nnz[t] = total;
-    if (total > K)
-        return; // overflow row: goes to the dense backup
-    int base = 0;
-    for (int j0 = 0; j0 < nt; j0 += 64) {
-        const int j = j0 + lane;
-        const int n = j < nt ? min(count[(size_t)t * nt + j], W) : 0;
-        const int incl = wave_incl_scan(n, lane);
-        const int excl = base + incl - n;
+    // tile j's n stored entries to ELL slots [excl, excl + n) of row t, 8 at a
+    // time with all loads of a lane in flight together; only stored slots are
+    // read: each lane reads its own tile, so every load is a request of its
+    // own, and most tiles hold one or two entries
+    auto copy = [&](int j, int n, int excl) {
         const size_t src = ((size_t)t * nt + j) * W;
         const size_t dst = (size_t)t * K + excl;
-        // 8 slots at a time, all loads of a lane in flight together; only
-        // stored slots are read: each lane reads its own tile, so every load
-        // is a request of its own, and most tiles hold one or two entries
         for (int s0 = 0; s0 < n; s0 += 8) {
             int16_t c[8];
             S v[8];
@@ -66,6 +52,33 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
                     ((S *)ell_val)[dst + s0 + u] = v[u];
                 }
         }
+    };
+    if (nt <= 64) { // one tile per lane: the counts are read once
+        const int n = lane < nt ? min(count[(size_t)t * nt + lane], W) : 0;
+        const int incl = wave_incl_scan(n, lane);
+        const int total = __shfl(incl, 63, 64);
+        if (lane == 0)
+            row_nnz[t] = total;
+        if (total <= K) // otherwise an overflow row: it goes to the dense backup
+            copy(lane, n, incl - n);
+        return;
+    }
+    int total = 0;
+    for (int j0 = 0; j0 < nt; j0 += 64) {
+        const int j = j0 + lane;
+        const int n = j < nt ? min(count[(size_t)t * nt + j], W) : 0;
+        total += __shfl(wave_incl_scan(n, lane), 63, 64);
+    }
+    if (lane == 0)
+        row_nnz[t] = total;
+    if (total > K)
+        return; // overflow row: goes to the dense backup
+    int base = 0;
+    for (int j0 = 0; j0 < nt; j0 += 64) {
+        const int j = j0 + lane;
+        const int n = j < nt ? min(count[(size_t)t * nt + j], W) : 0;
+        const int incl = wave_incl_scan(n, lane);
+        copy(j, n, base + incl - n);
         base += __shfl(incl, 63, 64);
     }
 }
