@@ -140,6 +140,7 @@ def parse():
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache leg")
     p.add_argument("--no-decode", action="store_true", help="skip the 2B decode leg")
     p.add_argument("--no-sweep", action="store_true", help="skip the density sweep leg")
+    p.add_argument("--no-tiny", action="store_true", help="skip the tiny float32 leg")
     p.add_argument("--only", action="store_true",
                    help="the headline step alone (every other leg skipped)")
     p.add_argument("--copy-calib", action="store_true",
@@ -147,7 +148,7 @@ def parse():
     a = p.parse_args()
     if a.only:
         a.no_cpu = a.no_dense = a.no_train = a.no_small = a.no_cold = True
-        a.no_decode = a.no_sweep = True
+        a.no_decode = a.no_sweep = a.no_tiny = True
     return a
 
 
@@ -346,16 +347,19 @@ class Layer:
         self.dy = d["dy"].to(dev) if with_dy else None
         self.host = d
         T, dm, dff, W = w.T, w.d_model, w.d_ff, w.width
-        bf = tw.TWELL_BF16
+        f32 = w.dtype == "f32"
+        bf = tw.TWELL_F32 if f32 else tw.TWELL_BF16  # the element type of the layer
+        tdt = torch.float32 if f32 else torch.bfloat16
+        self.esz = 4 if f32 else 2
         self.st = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.twl = tw.empty_twell(T, dff, W, torch.bfloat16, dev)
+        self.twl = tw.empty_twell(T, dff, W, tdt, dev)
         self.y = torch.empty((T, dm), dtype=torch.float32, device=dev)
         u8 = dict(dtype=torch.uint8, device=dev)
         self.gws = torch.empty(max(1, tw.gate_workspace_bytes(bf, T, dm, dff)), **u8)
         self.fws = torch.empty(max(1, tw.fwd_workspace_bytes(bf, T, dm, dff, W)), **u8)
         self.train = with_dy
         if with_dy:
-            self.hy = tw.empty_hybrid(T, dff, w.K, w.max_ovf, torch.bfloat16, dev)
+            self.hy = tw.empty_hybrid(T, dff, w.K, w.max_ovf, tdt, dev)
             self.hfws = torch.empty(max(1, tw.hybrid_fwd_workspace_bytes(bf, T, dm, dff, w.K,
                                                                          w.max_ovf)), **u8)
             f32 = dict(dtype=torch.float32, device=dev)
@@ -403,7 +407,7 @@ class Layer:
     def counts(self, torch):
         W = self.w.width
         nnz = int(torch.clamp(self.twl.count, max=W).sum())
-        out = {"T": self.w.T, "d_model": self.w.d_model, "d_ff": self.w.d_ff, "esz": 2,
+        out = {"T": self.w.T, "d_model": self.w.d_model, "d_ff": self.w.d_ff, "esz": self.esz,
                "nnz": nnz, "W": W}
         if self.train:
             ell = self.hy.row_slot < 0
@@ -705,6 +709,45 @@ def decode_leg(torch, tw, synth, dev):
             "by_T": rows}
 
 
+def tiny_leg(torch, tw, synth, dev, steps):
+    """The tiny float32 configuration (T 64, d_model 256, d_ff 1024, 2%: the
+    float32 MFMA gate and the few-token kernels): the inference forward
+    (gate_pack + ffn_fwd, and twell_decode_fwd: the same layer in one call)
+    and the training step (gate, TwELL->hybrid, forward
+    over the hybrid, backward) against the dense float32 layer in torch. The
+    forwards are graph-timed; the training steps are event-timed on both sides
+    (torch's autograd is not captured), launches included."""
+    w = synth.TINY_F32.with_(K=64, max_ovf=16)
+    L = Layer(torch, tw, synth, w, dev, with_dy=True)
+    fwd_us = graph_us(torch, L.fwd_step)
+    L.check_status("tiny forward")
+    dws = torch.empty(max(1, tw.decode_workspace_bytes(tw.TWELL_F32, w.T, w.d_model, w.d_ff,
+                                                       w.width)), dtype=torch.uint8, device=dev)
+    dec_us = graph_us(torch, lambda: tw.decode_fwd(L.x, L.wg, L.wu, L.wd, width=w.width,
+                                                   out=L.twl, y=L.y, workspace=dws,
+                                                   status=L.st))
+    L.check_status("tiny forward in one call")
+    tr_ms = event_ms(torch, L.train_step, steps)
+    L.check_status("tiny training step")
+    kms = kernel_ms(torch, tw, [L.gate, L.ffn], 20)
+    fwd, _, train, _ = dense_fns(torch, L)
+    with torch.no_grad():
+        de_fwd_us = graph_us(torch, fwd)
+    de_tr_ms = event_ms(torch, train, steps)
+    c = L.counts(torch)
+    return {"workload": "tiny-fp32", "T": w.T, "d_model": w.d_model, "d_ff": w.d_ff,
+            "density": w.density, "dtype": "f32", "nnz": c["nnz"], "n_ovf": c["n_ovf"],
+            "forward_us": round(fwd_us, 2), "dense_forward_us": round(de_fwd_us, 2),
+            "forward_speedup": round(de_fwd_us / fwd_us, 3),
+            "forward_one_call_us": round(dec_us, 2),
+            "forward_one_call_speedup": round(de_fwd_us / dec_us, 3),
+            "forward_kernel_us": {k: round(v * 1e3, 2) for k, v in kms.items()},
+            "train_us": round(tr_ms * 1e3, 2), "dense_train_us": round(de_tr_ms * 1e3, 2),
+            "train_speedup": round(de_tr_ms / tr_ms, 3),
+            "timing": "forwards: HIP graph of 10 calls, replayed 20 times; training steps: "
+                      "events around back-to-back steps"}
+
+
 def sweep_leg(torch, tw, synth, dev):
     """The 1.5B-scale forward (T 8192, d_model 2048, d_ff 5632) at gate
     densities 0.5, 1, 2, 5 and 20%: gate GEMM + TwELL pack, then the fused
@@ -898,6 +941,8 @@ def main():
         extra["cold"] = cold_leg(torch, tw, synth, L)
     if not a.no_decode:
         extra["decode"] = decode_leg(torch, tw, synth, dev)
+    if not a.no_tiny:
+        extra["tiny_fp32"] = tiny_leg(torch, tw, synth, dev, a.steps)
     if not a.no_sweep:
         extra["density_sweep"] = sweep_leg(torch, tw, synth, dev)
     cpu = None if a.no_cpu else cpu_leg(synth, w)
