@@ -12,9 +12,9 @@
 //     slice of x sits in LDS, eight lanes cover one 128-byte line of a W_g row
 //     (a wave load reads eight whole lines), each lane keeps its own running
 //     dot products over the slice's lines and the eight lanes of a row are
-//     summed at the end. With more tokens the eight waves split the slice
-//     again, run bf16 MFMAs with both operands straight from global memory,
-//     and sum their partial tiles in LDS in a fixed order.
+//     summed at the end. With more tokens the item is a [T][128] tile of g
+//     over its slice on the shared LDS-DMA MFMA main loop (ntgemm.hpp), which
+//     loads every operand line whole, and each wave stores its accumulators.
 //  2. pack + up. A wave item is one (token, tile): it sums the ks partials in
 //     slice order, packs the tile with two ballots into the TwELL arrays, and
 //     for each stored nonzero (i, h) gathers wu_t[i] and stores
@@ -40,9 +40,6 @@ namespace {
 
 constexpr int DW = 8;          // waves per workgroup
 constexpr int DNT = 64 * DW;
-constexpr int TC = 32;         // tokens per MFMA chunk of the gate
-constexpr int LP = TWELL_TILE_C + 8; // LDS pitch of a partial row (floats): rows 4
-                                     // apart (the two lane halves) land 32 banks apart
 constexpr int LISTD = 2048;    // entries staged per pass of the down phase
 constexpr int GD = 8;          // wd slices in flight per wave in the down phase
 constexpr int SPT = 4;         // TwELL slots per thread per round of the down phase's list
@@ -53,10 +50,9 @@ constexpr int GLB = 8;         // W_g lines per row in flight per lane (matrix-v
 // Host-computed geometry of one decode call.
 struct DecPlan {
     int T, dm, dff, nt, W;
-    int nsteps;  // 32-byte K steps in a row of d_model elements
-    int ks, spw; // d_model slices per tile (gate items), K steps per wave
-    int tcm;     // rows of a wave's LDS partial: min(T, TC)
+    int ks;      // d_model slices per tile (gate items)
     int nsl;     // 1 KB slices of a d_model row (down items per token)
+    int nk;      // 64-byte K steps of a d_model row (tiled MFMA gate)
     bool gemv;   // matrix-vector gate: item k covers 128-byte lines [k lpi, (k + 1) lpi)
     int nl, lpi; // 128-byte lines of a d_model row, lines per gate item
     size_t a_off, bytes; // workspace: partials [ks][T][dff] at 0, a [T][nt][W] at a_off
@@ -71,22 +67,20 @@ DecPlan dec_plan(int dt, int T, int dm, int dff, int W, bool with_gate)
     P.dff = dff;
     P.nt = dff / TWELL_TILE_C;
     P.W = W;
-    P.nsteps = dm * esz / 32;
-    // about one item per compute unit, at least one K step per wave, and the
-    // partials (ks T dff floats) at most half of W_g's bytes
-    int ks = std::max(1, GATE_ITEMS / P.nt);
-    ks = std::min(ks, std::max(1, P.nsteps / DW));
-    ks = std::min(ks, std::max(1, 4 * P.nsteps / std::max(T, 1)));
-    P.spw = (P.nsteps + ks * DW - 1) / (ks * DW);
-    P.ks = (P.nsteps + P.spw * DW - 1) / (P.spw * DW);
     P.gemv = T <= GEMV_T;
     P.nl = dm * esz / 128; // d_model % 64 == 0: whole lines
-    if (P.gemv) {
+    P.nk = dm * esz / 64;
+    if (P.gemv) { // about one item per compute unit
         const int ks0 = std::max(1, std::min(GATE_ITEMS / P.nt, P.nl));
         P.lpi = (P.nl + ks0 - 1) / ks0;
         P.ks = (P.nl + P.lpi - 1) / P.lpi;
+    } else {
+        // tiled MFMA gate: about two items per compute unit, at least 12 K
+        // steps per item, the partials at most half of W_g's bytes
+        int ks = std::max(1, 2 * GATE_ITEMS / P.nt);
+        ks = std::min(ks, std::max(1, P.nk / 12));
+        P.ks = std::min(ks, std::max(1, dm * esz / (8 * std::max(T, 1))));
     }
-    P.tcm = std::min(T, TC);
     P.nsl = (dm * esz + 1023) / 1024;
     const size_t part = with_gate ? (size_t)P.ks * T * dff * 4 : 0;
     P.a_off = (part + 255) / 256 * 256;
@@ -131,102 +125,6 @@ DEVI void pack_tile(float g0, float g1, size_t tj, int n0, int W, int lane, int3
         count[tj] = n;
         if (n > W)
             raise_status(status, TWELL_DEV_TILE_OVERFLOW);
-    }
-}
-
-// MFMA partial of one tile's 128 columns for NC chunks of 32 tokens over K
-// steps [s0, s1) (4 blocks of 32 columns; accumulator element e of lane l in
-// a block holds row 8(e/4) + 4(l/32) + e%4, column l%32). Each W_g fragment
-// is loaded once for all chunks. Rows of x past the last token repeat a valid
-// row: they only feed output rows that are never stored.
-template <int DT, int NC>
-DEVI void gate_steps(const uint8_t *const (&xrow)[NC], const uint8_t *const (&wrow)[4], int s0,
-                     int s1, floatx16_t (&acc)[NC][4])
-{
-    constexpr int NSB = NC == 1 ? 4 : 2; // K steps of loads in flight
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[c][b][e] = 0.f;
-    for (int s = s0; s < s1; s += NSB) {
-        // steps past the range re-read its last step and are not used
-        uint4 a[NSB][NC], b[NSB][4];
-#pragma unroll
-        for (int i = 0; i < NSB; ++i) {
-            const size_t o = (size_t)min(s + i, s1 - 1) * 32;
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-                a[i][c] = ldg16(xrow[c] + o);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                b[i][q] = ldg16(wrow[q] + o);
-        }
-#pragma unroll
-        for (int i = 0; i < NSB; ++i)
-            if (s + i < s1) // uniform
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        ng::mma_group<DT>(acc[c][q], a[i][c], b[i][q]);
-    }
-}
-
-// Rows r < tn of this wave's partial tile into lds[(wave * tcm + r) * LP + column].
-DEVI void park_partial(const floatx16_t (&acc)[4], float *lds, int wave, int tcm, int tn, int half,
-                       int l32)
-{
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 8 * q + 4 * half + e;
-                if (r < tn)
-                    lds[(wave * tcm + r) * LP + b * 32 + l32] = acc[b][4 * q + e];
-            }
-}
-
-// ---------------------------------------------------------------- phase 1
-template <int DT, int NC>
-DEVI void gate_part_item(const DecPlan &P, const uint8_t *__restrict__ x,
-                         const uint8_t *__restrict__ wg, int item, float *__restrict__ part,
-                         float *lds)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, l32 = lane & 31;
-    const int j = item / P.ks, k = item % P.ks, n0 = j * TWELL_TILE_C;
-    const size_t rowbytes = (size_t)P.nsteps * 32;
-    const int s0 = (k * DW + wave) * P.spw, s1 = min(P.nsteps, s0 + P.spw);
-    const uint8_t *wrow[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        wrow[b] = wg + (size_t)(n0 + b * 32 + l32) * rowbytes + half * 16;
-    const uint8_t *xrow[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int tn = min(TC, P.T - c * TC); // >= 1: NC chunks cover T
-        xrow[c] = x + (size_t)(c * TC + min(l32, tn - 1)) * rowbytes + half * 16;
-    }
-    floatx16_t acc[NC][4];
-    gate_steps<DT, NC>(xrow, wrow, s0, s1, acc);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int tc = c * TC, tn = min(TC, P.T - tc);
-        park_partial(acc[c], lds, wave, P.tcm, tn, half, l32);
-        __syncthreads();
-        for (int i = threadIdx.x; i < tn * TWELL_TILE_C; i += DNT) {
-            const int r = i / TWELL_TILE_C, q = i % TWELL_TILE_C;
-            float g = lds[r * LP + q];
-#pragma unroll
-            for (int w = 1; w < DW; ++w)
-                g += lds[(w * P.tcm + r) * LP + q];
-            part[((size_t)k * P.T + tc + r) * P.dff + n0 + q] = g;
-        }
-        __syncthreads(); // lds is rewritten by the next chunk
     }
 }
 
@@ -570,23 +468,49 @@ DEVI void down_item(const DecPlan &P, const int32_t *__restrict__ count,
 }
 
 size_t down_lds() { return (2 * LISTD + 260 + DW * 512) * 4; }
-size_t gate_lds(const DecPlan &P) { return (size_t)DW * P.tcm * LP * 4; }
 
 // ---------------------------------------------------------------- kernels
-template <int DT, int NC>
-__global__ __launch_bounds__(DNT) void dec_gate_part_kernel(
-    DecPlan P, const uint8_t *__restrict__ x, const uint8_t *__restrict__ wg, float *part)
-{
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    gate_part_item<DT, NC>(P, x, wg, blockIdx.x, part, smem);
-}
-
 template <int DT, int TT>
 __global__ __launch_bounds__(DNT) void dec_gate_gemv_kernel(
     DecPlan P, const uint8_t *__restrict__ x, const uint8_t *__restrict__ wg, float *part)
 {
     extern __shared__ __attribute__((aligned(16))) uint4 xs[];
     gate_gemv_item<DT, TT>(P, x, wg, blockIdx.x, part, xs);
+}
+
+// Phase 1 for more than GEMV_T tokens: item (tile j, slice k) is a [T][128]
+// tile of g over K steps [k nk / ks, (k + 1) nk / ks) on the shared LDS-DMA
+// MFMA main loop (C::BM = 32 or 64 token rows; rows past T repeat the last
+// token and are not stored); each wave stores its accumulators as the item's
+// partial. Every operand line is loaded whole, straight into LDS.
+using GC32 = ng::Cfg<32, 128, 1, 4, 4, 64>; // up to 32 tokens: four waves of 32 x 32
+using GC64 = ng::Cfg<64, 128, 2, 4, 4, 64>; // up to 64 tokens: eight waves of 32 x 32
+template <int DT, class C>
+__global__ __launch_bounds__(C::NT) void dec_gate_mm_kernel(DecPlan P, const uint8_t *__restrict__ x,
+                                                            const uint8_t *__restrict__ wg,
+                                                            float *__restrict__ part)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t L[C::LDS];
+    const int j = blockIdx.x / P.ks, k = blockIdx.x % P.ks, n0 = j * TWELL_TILE_C;
+    const size_t rowbytes = (size_t)P.nk * 64;
+    const int kt0 = (int)((long)P.nk * k / P.ks), kt1 = (int)((long)P.nk * (k + 1) / P.ks);
+    auto rowa = [&](int r) { return x + (size_t)min(r, P.T - 1) * rowbytes; };
+    auto rowb = [&](int r) { return wg + (size_t)(n0 + r) * rowbytes; };
+    auto off = [](int kt) { return ng::StepOff{(size_t)kt * C::ROWB, (size_t)kt * C::ROWB}; };
+    ng::Acc<C> acc;
+    ng::mainloop<C, DT>(L, rowa, rowb, off, kt0, kt1, acc);
+    const int lane = threadIdx.x & 63, wm = ng::wave_m<C>(), wn = ng::wave_n<C>();
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = ng::acc_row<C>(wm, mi, e, lane);
+                if (r < P.T)
+                    part[((size_t)k * P.T + r) * P.dff + n0 + ng::acc_col<C>(wn, ni, lane)] =
+                        acc.v[mi][ni][e];
+            }
 }
 
 template <int DT, int NW, int G, bool UP>
@@ -652,13 +576,13 @@ void launch_gate_part(const DecPlan &P, const void *x, const void *wg, float *pa
         tm.mark("dec_gate_gemv_kernel");
         return;
     }
-    if (P.T > TC)
-        hipLaunchKernelGGL((dec_gate_part_kernel<DT, 2>), dim3(P.nt * P.ks), dim3(DNT),
-                           gate_lds(P), s, P, (const uint8_t *)x, (const uint8_t *)wg, part);
+    if (P.T > 32)
+        hipLaunchKernelGGL((dec_gate_mm_kernel<DT, GC64>), dim3(P.nt * P.ks), dim3(GC64::NT), 0,
+                           s, P, (const uint8_t *)x, (const uint8_t *)wg, part);
     else
-        hipLaunchKernelGGL((dec_gate_part_kernel<DT, 1>), dim3(P.nt * P.ks), dim3(DNT),
-                           gate_lds(P), s, P, (const uint8_t *)x, (const uint8_t *)wg, part);
-    tm.mark("dec_gate_part_kernel");
+        hipLaunchKernelGGL((dec_gate_mm_kernel<DT, GC32>), dim3(P.nt * P.ks), dim3(GC32::NT), 0,
+                           s, P, (const uint8_t *)x, (const uint8_t *)wg, part);
+    tm.mark("dec_gate_mm_kernel");
 }
 
 template <int DT>
