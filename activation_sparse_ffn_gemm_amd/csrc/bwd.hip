@@ -51,8 +51,12 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // The dx pass gathers two weight rows per entry. With many tokens and
 // weights well beyond one XCD's L2 it runs XCD-local (slices.hpp): XCD k sums
-// the k-th slice of d_model from an interleaved slice-major copy of wu_t and
-// wg_t, which the masks launch makes on the side.
+// the k-th slice of d_model of the wu_t and wg_t rows from an interleaved
+// slice-major copy that the masks launch makes on the side: an entry's two
+// slices are then one run of lines. (Reading the slices in place, where they
+// are runs of whole lines, saves the copy's 12 us at the 1.5B shape but makes
+// the dx pass 16 us slower: each XCD's slices are then 512-byte runs at a
+// 4 KB stride in two matrices.)
 inline bool dx_split(int dt, int T, int dm, int dff)
 {
     return T >= 1024 && (size_t)dff * dm * (dt == TWELL_BF16 ? 2 : 4) >= ((size_t)16 << 20);
@@ -454,8 +458,8 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 // ------------------------------------------------------------ masks launch
 // Work that only has to be done before later passes rides on the masks
 // launch: workgroups b < n_mask build masks; the next n_copy copy wu_t and
-// wg_t into the dx pass's interleaved slice-major array; the rest make the
-// backup products' transposed copies.
+// wg_t into the dx pass's interleaved slice-major array; the rest gather the
+// backup rows' x and dy rows for the dW products.
 constexpr int MASK_LDS = CH * 8 + BR * 4;
 template <int DT>
 __global__ __launch_bounds__(NT) void mask_kernel(
@@ -489,7 +493,7 @@ __global__ __launch_bounds__(NT) void mask_kernel(
 // partials for the slice.
 template <int DT, int SPL, int G>
 __global__ __launch_bounds__(NT) void bwd_dxs_kernel(
-    const uint32_t *__restrict__ wsl, int dff, Slices sl, const int32_t *__restrict__ row_nnz,
+    SliceSrc src, int dff, Slices sl, const int32_t *__restrict__ row_nnz,
     const int32_t *__restrict__ row_slot, const int16_t *__restrict__ ell_col,
     const float *__restrict__ coef, int T, int K, int dm, float *__restrict__ dx, BkPart bp,
     int max_ovf)
@@ -510,17 +514,16 @@ __global__ __launch_bounds__(NT) void bwd_dxs_kernel(
     }
     const int n = min(row_nnz[t], K);
     const size_t TK = (size_t)T * K, rb = (size_t)t * K;
-    const uint32_t *slice = wsl + (size_t)k * dff * 2 * sl.swp;
-    // one descriptor over this XCD's slice array (rows of 2 swp words); a
-    // lane's word offsets are clamped to the padded slice, words past nk are
-    // never stored
-    const int rowb = 2 * sl.swp * 4;
-    const __amdgpu_buffer_rsrc_t rs_all = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)slice, (short)0, dff * rowb, BUF_DWORD3);
+    // one descriptor over this XCD's slice of every wu_t row, one over wg_t's;
+    // a lane's word offsets are clamped to the slice, words past nk are never
+    // stored
+    const int rowb = src.rowb;
+    const __amdgpu_buffer_rsrc_t rs_u = slice_rsrc(src.a + (size_t)k * src.kstride, dff, src);
+    const __amdgpu_buffer_rsrc_t rs_g = slice_rsrc(src.b + (size_t)k * src.kstride, dff, src);
     int offq[SPL];
 #pragma unroll
     for (int q = 0; q < SPL; ++q)
-        offq[q] = min(q * 64 + lane, sl.swp - 1) * 4;
+        offq[q] = min(q * 64 + lane, src.lim - 1) * 4;
     float acc[SPL][EPW];
 #pragma unroll
     for (int q = 0; q < SPL; ++q)
@@ -546,9 +549,8 @@ __global__ __launch_bounds__(NT) void bwd_dxs_kernel(
             const int rc = bcast(ci, min(e, m - 1)) * rowb;
 #pragma unroll
             for (int q = 0; q < SPL; ++q) {
-                u[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_all, rc + offq[q], 0, 0);
-                g[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_all, rc + sl.swp * 4 + offq[q], 0,
-                                                            0);
+                u[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_u, rc + offq[q], 0, 0);
+                g[q] = __builtin_amdgcn_raw_buffer_load_b32(rs_g, rc + offq[q], 0, 0);
             }
         };
 #pragma unroll
@@ -648,18 +650,19 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     if (T > 0) {
         const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, true, ws + L.backup);
         if (L.split) {
+            const SliceSrc src = slice_src_copy(wsl, 2, dff, sl);
             const int spl = (sl.sww + 63) / 64;
             const dim3 grid(rgroups * NXCD);
             if (spl <= 1)
-                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 1, 8>), grid, dim3(NT), 0, s, wsl, dff, sl,
+                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 1, 8>), grid, dim3(NT), 0, s, src, dff, sl,
                                    h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dm, dx, bp,
                                    h->max_ovf);
             else if (spl == 2)
-                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 2, 4>), grid, dim3(NT), 0, s, wsl, dff, sl,
+                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 2, 4>), grid, dim3(NT), 0, s, src, dff, sl,
                                    h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dm, dx, bp,
                                    h->max_ovf);
             else
-                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 4, 2>), grid, dim3(NT), 0, s, wsl, dff, sl,
+                hipLaunchKernelGGL((bwd_dxs_kernel<DT, 4, 2>), grid, dim3(NT), 0, s, src, dff, sl,
                                    h->row_nnz, h->row_slot, h->ell_col, coef, T, K, dm, dx, bp,
                                    h->max_ovf);
             tm.mark("bwd_dxs_kernel");

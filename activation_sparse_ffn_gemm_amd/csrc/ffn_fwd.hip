@@ -14,12 +14,13 @@
 //         token holds x[t] in registers, gathers the wu_t rows of its
 //         entries in those tiles and writes a = h u for each, with the entry's
 //         column, into the token's compact entry list (entries of all tiles in
-//         column order, so each XCD's share is one contiguous run). Extra
-//         workgroups copy wd into a slice-major layout for the down pass.
+//         column order, so each XCD's share is one contiguous run). When a
+//         slice of a wd row is not a run of whole 128-byte lines in place,
+//         extra workgroups copy wd into a slice-major layout (slices.hpp).
 //   down: XCD k owns the k-th eighth of the d_model columns. A wave per token
 //         walks the token's compact list and gathers, per entry, only the
-//         slice of the wd row in that copy (slices are contiguous per XCD, so
-//         the gathers spread over all L2 channels), accumulating y[t]'s slice.
+//         slice of the wd row (in place, or in that copy), accumulating
+//         y[t]'s slice.
 // Otherwise: one fused pass, a wave per token doing both projections, a is
 // never written to memory.
 #include "backup.hpp"
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------- split
-// Workspace of the two-pass design: slice-major wd, then the compact entry
+// Workspace of the two-pass design: slice-major wd (if copied), then the compact entry
 // lists (a as float32, columns as int16) and their lengths.
 struct FwdLayout {
     size_t wds, ac, cc, rn, total;
@@ -188,7 +189,7 @@ inline FwdLayout fwd_layout(int dt, int T, int dm, int dff, int W)
     const Slices sl = slices(dt, dm);
     L.cap = dff / TWELL_TILE_C * W;
     size_t o = 0;
-    L.wds = o; o += up256((size_t)NXCD * dff * sl.swp * 4);
+    L.wds = o; o += up256(slice_copy_bytes(1, dff, sl));
     L.ac = o;  o += up256((size_t)T * L.cap * 4);
     L.cc = o;  o += up256((size_t)T * L.cap * 2);
     L.rn = o;  o += up256((size_t)T * 4);
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(NT) void hfwd_up_kernel(
 // partials.
 template <int DT, int SPL, int G>
 __global__ __launch_bounds__(NT) void fwd_down_kernel(
-    const uint32_t *__restrict__ wds, int dff, Slices sl, const float *__restrict__ ac,
+    SliceSrc src, int dff, Slices sl, const float *__restrict__ ac,
     const int16_t *__restrict__ cc, const int32_t *__restrict__ rn, int cap, int T, int dm,
     float *__restrict__ y, const int32_t *__restrict__ row_slot, BkPart bp, int max_ovf)
 {
@@ -392,16 +393,14 @@ __global__ __launch_bounds__(NT) void fwd_down_kernel(
     const int n = min(rn[t], cap);
     const float *arow = ac + (size_t)t * cap;
     const int16_t *crow = cc + (size_t)t * cap;
-    const uint32_t *slice = wds + (size_t)k * dff * sl.swp;
-    // one descriptor over this XCD's slice array; a lane's word offsets are
-    // clamped to the padded slice (words past nk are never stored)
-    const int rowb = sl.swp * 4;
-    const __amdgpu_buffer_rsrc_t rs_all = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)slice, (short)0, dff * rowb, BUF_DWORD3);
+    // one descriptor over this XCD's slice of every wd row; a lane's word
+    // offsets are clamped to the slice (words past nk are never stored)
+    const int rowb = src.rowb;
+    const __amdgpu_buffer_rsrc_t rs_all = slice_rsrc(src.a + (size_t)k * src.kstride, dff, src);
     int offq[SPL];
 #pragma unroll
     for (int q = 0; q < SPL; ++q)
-        offq[q] = min(q * 64 + lane, sl.swp - 1) * 4;
+        offq[q] = min(q * 64 + lane, src.lim - 1) * 4;
     float acc[SPL][EPW];
 #pragma unroll
     for (int c = 0; c < SPL; ++c)
@@ -480,7 +479,8 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
     float *ac = (float *)(ws + L.ac);
     int16_t *cc = (int16_t *)(ws + L.cc);
     int32_t *rn = (int32_t *)(ws + L.rn);
-    const int n_copy = ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD;
+    const int n_copy = sl.direct ? 0 : copy_groups(dff);
+    const SliceSrc src = sl.direct ? slice_src_direct(wd, nullptr, sl) : slice_src_copy(wds, 1, dff, sl);
     constexpr int GU = NW <= 8 ? 2 : 1; // entries in flight per wave (occupancy first)
     hipLaunchKernelGGL((fwd_up_kernel<DT, NW, GU>), dim3(n_copy + groups * NXCD), dim3(NT), 0, s,
                        (const uint8_t *)x, h->count, h->col, h->val, T, nt, h->width,
@@ -489,13 +489,13 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
     tm.mark("fwd_up_kernel");
     const int spl = (sl.sww + 63) / 64;
     if (spl <= 1)
-        hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
                            dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
     else if (spl == 2)
-        hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
                            dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
     else
-        hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, src,
                            dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
     tm.mark("fwd_down_kernel");
 }
@@ -518,11 +518,11 @@ void launch_dt(const void *x, const twell_t *h, const void *wu, const void *wd, 
 // ---- the forward over a hybrid's ELL rows, two-pass form (hyb_fwd.hip)
 bool hyb_use_split(int dt, int T, int dm, int dff) { return use_split(dt, T, dm, dff); }
 
-// slice-major wd copy, then a per ELL slot (float32 [T][K])
+// slice-major wd copy (unless read in place), then a per ELL slot (float32 [T][K])
 size_t hyb_split_workspace(int dt, int T, int dm, int dff, int K)
 {
     const Slices sl = slices(dt, dm);
-    return up256((size_t)NXCD * dff * sl.swp * 4) + up256((size_t)T * K * 4);
+    return up256(slice_copy_bytes(1, dff, sl)) + up256((size_t)T * K * 4);
 }
 
 namespace {
@@ -535,8 +535,9 @@ void launch_hyb_split_nw(const void *x, const hybrid_t *h, const void *wu, const
     const int groups = (T + NT / 64 - 1) / (NT / 64);
     const Slices sl = slices(DT, dm);
     uint32_t *wds = (uint32_t *)ws;
-    float *ac = (float *)(ws + up256((size_t)NXCD * dff * sl.swp * 4));
-    const int n_copy = ((dff + RL_ROWS - 1) / RL_ROWS + NXCD - 1) / NXCD * NXCD;
+    float *ac = (float *)(ws + up256(slice_copy_bytes(1, dff, sl)));
+    const int n_copy = sl.direct ? 0 : copy_groups(dff);
+    const SliceSrc src = sl.direct ? slice_src_direct(wd, nullptr, sl) : slice_src_copy(wds, 1, dff, sl);
     constexpr int GU = NW <= 8 ? 2 : 1;
     hipLaunchKernelGGL((hfwd_up_kernel<DT, NW, GU>), dim3(n_copy + groups * NXCD), dim3(NT), 0, s,
                        (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col, h->ell_val, T,
@@ -545,15 +546,15 @@ void launch_hyb_split_nw(const void *x, const hybrid_t *h, const void *wu, const
     tm.mark("hfwd_up_kernel");
     const int spl = (sl.sww + 63) / 64;
     if (spl <= 1)
-        hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
                            dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
                            h->max_ovf);
     else if (spl == 2)
-        hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
                            dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
                            h->max_ovf);
     else
-        hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, wds,
+        hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, src,
                            dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
                            h->max_ovf);
     tm.mark("hfwd_down_kernel");

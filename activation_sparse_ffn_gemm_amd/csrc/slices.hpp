@@ -9,12 +9,18 @@
 //   slices), each row's slice padded to swp words (a multiple of 32).
 // With NSRC = 2 two matrices are interleaved per row: row i of slice k holds
 // the first matrix's slice, then the second's (2 swp words).
+// When a row is eight whole runs of 128-byte lines (ndw a multiple of 256
+// words: d_model % 512 == 0 in bf16, % 256 in f32), a slice already is one
+// run of whole lines in place ("direct"), and the forward's down pass reads
+// wd as stored: no copy is made.
 #pragma once
 
 #include "common.hpp"
+#include "rows.hpp"
 
 struct Slices {
     int ndw, sww, swp;
+    bool direct;
     DEVI int valid(int k) const { return max(0, min(sww, ndw - k * sww)); }
 };
 
@@ -24,7 +30,43 @@ inline Slices slices(int dt, int dm)
     s.ndw = dt == TWELL_BF16 ? dm / 2 : dm;
     s.sww = (s.ndw + NXCD - 1) / NXCD;
     s.swp = (s.sww + 31) / 32 * 32;
+    s.direct = s.ndw % (NXCD * 32) == 0;
     return s;
+}
+
+// Where a pass finds slice k of row c of one or two matrices: row c of slice
+// k of matrix a starts at word a + k kstride + c rowb / 4 (b likewise), and a
+// lane's word offsets within it are clamped to [0, lim).
+struct SliceSrc {
+    const uint32_t *a, *b;
+    size_t kstride;
+    int rowb, lim;
+};
+
+// the weights as stored (Slices::direct)
+inline SliceSrc slice_src_direct(const void *a, const void *b, const Slices &sl)
+{
+    return SliceSrc{(const uint32_t *)a, (const uint32_t *)b, (size_t)sl.sww, sl.ndw * 4, sl.sww};
+}
+
+// a slice-major copy of NSRC matrices (copy_slices_rows)
+inline SliceSrc slice_src_copy(const uint32_t *w, int nsrc, int dff, const Slices &sl)
+{
+    return SliceSrc{w, w + sl.swp, (size_t)dff * nsrc * sl.swp, nsrc * sl.swp * 4, sl.swp};
+}
+
+// Bytes of a slice-major copy of NSRC matrices (0 when the slices are read in place)
+inline size_t slice_copy_bytes(int nsrc, int dff, const Slices &sl)
+{
+    return sl.direct ? 0 : (size_t)NXCD * dff * nsrc * sl.swp * 4;
+}
+
+// Buffer descriptor over rows 0 .. dff - 1 of one matrix's slice k, from
+// its base (range: the last row's lim words; loads past it read 0)
+DEVI __amdgpu_buffer_rsrc_t slice_rsrc(const uint32_t *base, int dff, const SliceSrc &s)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0,
+                                             (dff - 1) * s.rowb + s.lim * 4, BUF_DWORD3);
 }
 
 constexpr int RL_ROWS = 8; // weight rows per workgroup of the copy

@@ -150,11 +150,12 @@ def _fwd_on_oracle_twell(orc, d, dtype, W):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,dm,dff", [(1, 64, 128), (77, 320, 384), (130, 1024, 512),
                                       (40, 2304, 768), (33, 2048, 384), (64, 4096, 256),
-                                      (65, 896, 640), (1029, 2048, 4096)])
+                                      (65, 896, 640), (1029, 2048, 4096), (1029, 2304, 4096)])
 def test_ffn_fwd_integer_exact(orc, dtype, T, dm, dff):
     """Integer inputs: y matches the oracle bit for bit. 1029 tokens with 16 MB
-    (bf16) or 32 MB (f32) weights take the two-pass XCD-local path, with a
-    ragged last group of tokens."""
+    or more of weights take the two-pass XCD-local path, with a ragged last
+    group of tokens: d_model 2048 reads each XCD's slice of wd in place,
+    d_model 2304 (slices of 576 bytes) from a slice-major copy."""
     if dtype == "f32" and dm > 2048:
         pytest.skip("fp32 limit is d_model <= 2048")
     announce("ffn_fwd int", dtype, T, dm, dff)
