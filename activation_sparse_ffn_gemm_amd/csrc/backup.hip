@@ -62,9 +62,11 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 int pad_rows(int max_ovf) { return (max_ovf + WT - 1) / WT * WT; }
 
 // K split of the y_O / dx_O products: few row tiles give one workgroup per
-// CU far too little to overlap; aim at 512 workgroups over the capacity's
-// tiles (two per CU when about half the capacity is used; tiles wholly past
-// n_ovf return at once), at most 16 splits, at least 16 K steps each.
+// CU far too little to overlap; aim at `target` workgroups over the
+// capacity's tiles (tiles wholly past n_ovf return at once), at most 16
+// splits, at least 16 K steps each. The callers aim at 1024: at the 1.5B
+// skewed layer (1024 rows of capacity, 410 used) that is 8 splits, which ran
+// faster than 16 (and 4) and halves the float32 partials.
 int split_k(int R, int dm, int nk, int tile = WT, int target = 512)
 {
     const int tiles = (R / tile) * ((dm + tile - 1) / tile);
@@ -429,9 +431,8 @@ BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
     const size_t esz = dt == TWELL_BF16 ? 2 : 4, nh = dt == TWELL_BF16 ? 2 : 1;
     L.R = pad_rows(max_ovf);
     const int nseg = (int)(bwd ? 2 * nh : nh);
-    L.S = bwd ? split_k(L.R, dm, nseg * (int)(dff * esz / DX::ROWB), DX::BM,
-                        DX::BM == 256 ? 512 : 2048)
-              : split_k(L.R, dm, nseg * (int)(dff * esz / CY::ROWB), CY::BM, 2048);
+    L.S = bwd ? split_k(L.R, dm, nseg * (int)(dff * esz / DX::ROWB), DX::BM, 1024)
+              : split_k(L.R, dm, nseg * (int)(dff * esz / CY::ROWB), CY::BM, 1024);
     size_t o = 0;
     L.inter = o; o += up256((bwd ? 3 : 1) * nh * L.R * dff * esz);
     L.xo = o;    o += bwd ? up256(2 * (size_t)L.R * dm * esz) : 0;
