@@ -73,19 +73,33 @@ DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, 
                     make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
             }
         }
+    // g > 0 masks: ballot i (over mi, e, ni in that order) covers rows r (lanes
+    // 0-31) and r + 4 (lanes 32-63) of one 32-column block. Its two words are
+    // gathered into lanes 2 i and 2 i + 1 (mod 64) of a register, 32 ballots
+    // per register, and each lane then stores one row's word: four LDS stores
+    // per wave instead of one per ballot.
+    constexpr int NBAL = C::MI * 16 * C::NI;
+    static_assert(NBAL % 32 == 0, "whole registers of ballots");
+    uint32_t mv[NBAL / 32];
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = wm * C::WM + mi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            const bool ok = m0 + r < T;
+        for (int e = 0; e < 16; ++e)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) {
-                const uint64_t b = __ballot(ok && acc.v[mi][ni][e] > 0.f);
-                if (l32 == 0)
-                    masks[r * NBK + wn * (C::WN / 32) + ni] = (uint32_t)(b >> (32 * half));
+                const int i = (mi * 16 + e) * C::NI + ni;
+                const int r = wm * C::WM + mi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                const uint64_t b = __ballot(m0 + r < T && acc.v[mi][ni][e] > 0.f);
+                if (lane >> 1 == i % 32) // lanes 2 i % 64 and 2 i % 64 + 1
+                    mv[i / 32] = (uint32_t)(b >> (32 * (lane & 1)));
             }
-        }
+#pragma unroll
+    for (int q = 0; q < NBAL / 32; ++q) {
+        const int i = q * 32 + lane / 2, ni = i % C::NI, e = (i / C::NI) % 16,
+                  mi = i / (C::NI * 16);
+        const int r = wm * C::WM + mi * 32 + 8 * (e >> 2) + 4 * (lane & 1) + (e & 3);
+        masks[r * NBK + wn * (C::WN / 32) + ni] = mv[q];
+    }
     __syncthreads();
     for (int q = threadIdx.x; q < BM * (BN / TWELL_TILE_C); q += C::NT) {
         const int r = q / (BN / TWELL_TILE_C), tl = q % (BN / TWELL_TILE_C);
