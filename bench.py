@@ -67,7 +67,7 @@ KERNEL_SOURCES = {
     "hyb_dense_kernel": "to_hybrid.hip", "hfwd_ell_kernel": "hyb_fwd.hip",
     "hfwd_up_kernel": "ffn_fwd.hip", "hfwd_down_kernel": "ffn_fwd.hip",
     "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "bk_ud_kernel": "backup.hip",
-    "bk_dxdw_kernel": "backup.hip", "dec_gate_part_kernel": "decode.hip",
+    "bk_dxdw_kernel": "backup.hip", "dec_gate_mm_kernel": "decode.hip",
     "dec_pack_kernel": "decode.hip", "dec_up_kernel": "decode.hip",
     "dec_down_kernel": "decode.hip", "dec_gate_gemv_kernel": "decode.hip",
     "dec_pack_up_kernel": "decode.hip",
@@ -228,6 +228,12 @@ def kernel_work(ctx):
     n_t = dff // 128
     nblk = (T + 63) // 64
     dx_split = T >= 1024 and dff * dm * esz >= (16 << 20)
+    # the forward's down pass reads wd's XCD slices in place when they are runs
+    # of whole 128-byte lines (a row of 256 k words); otherwise the up pass
+    # copies wd into a slice-major array first
+    ndw = dm * esz // 4
+    wd_copy = 0 if ndw % 256 == 0 else 2 * dff * dm * esz
+    copy_note = "" if wd_copy == 0 else "; wd slice-major copy (read + write)"
     row_b = dm * esz
     T_ell = T - n_ovf
     twell_b = T * n_t * 4 + nnz * (2 + esz)
@@ -236,9 +242,9 @@ def kernel_work(ctx):
                              "2 d_model d_ff flop per token (TwELL written in the epilogue)"),
         "ffn_fwd_kernel": ("hbm", nnz * 2 * row_b + T * row_b + T * dm * 4 + twell_b,
                            "per nonzero one wu_t row + one wd row; x, y, TwELL once"),
-        "fwd_up_kernel": ("hbm", nnz * row_b + T * row_b + twell_b + 2 * dff * row_b + nnz * 6,
-                          "per nonzero one wu_t row; x, TwELL once; wd slice-major copy "
-                          "(read + write); a and column per nonzero written"),
+        "fwd_up_kernel": ("hbm", nnz * row_b + T * row_b + twell_b + wd_copy + nnz * 6,
+                          "per nonzero one wu_t row; x, TwELL once; a and column per nonzero "
+                          "written" + copy_note),
         "fwd_down_kernel": ("hbm", nnz * row_b + nnz * 6 + T * dm * 4,
                             "per nonzero one wd row (as 8 slices); a and column per nonzero; y"),
         "hyb_rows_kernel": ("hbm", T * n_t * 4 + nnz_ell * 8 + 4 * T,
@@ -260,9 +266,9 @@ def kernel_work(ctx):
                            "col, du, dg; dx rows"),
         "hfwd_ell_kernel": ("hbm", nnz_ell * (2 * row_b + 4) + T_ell * (row_b + dm * 4),
                             "per ELL nonzero one wu_t row + one wd row + (col, h); x, y rows"),
-        "hfwd_up_kernel": ("hbm", nnz_ell * (row_b + 8) + T_ell * row_b + 2 * dff * row_b,
-                           "per ELL nonzero one wu_t row + (col, h) + a written; x rows; wd "
-                           "slice-major copy (read + write)"),
+        "hfwd_up_kernel": ("hbm", nnz_ell * (row_b + 8) + T_ell * row_b + wd_copy,
+                           "per ELL nonzero one wu_t row + (col, h) + a written; x rows"
+                           + copy_note),
         "hfwd_down_kernel": ("hbm", nnz_ell * (row_b + 6) + T_ell * dm * 4,
                              "per ELL nonzero one wd row (as 8 slices) + (col, a); y rows"),
         "bk_a_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "A = h_O (.) x_O W_u (1 GEMM)"),
