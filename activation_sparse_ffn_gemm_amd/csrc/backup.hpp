@@ -16,12 +16,18 @@ size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
 BkPart bk_part(int dt, int dm, int dff, int max_ovf, bool bwd, const void *ws);
 void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
                    const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s);
-void launch_bk_ud(twell_dtype dt, const void *x, const void *dy, const hybrid_t *h,
-                  const void *wu, const void *wd, int dm, float l1, void *ws, Timer &tm,
-                  hipStream_t s);
-void launch_bk_dxdw(twell_dtype dt, const hybrid_t *h, const void *wu, const void *wg, int dm,
-                    float *dx, float *dwd, float *dwu, float *dwg, void *ws, Timer &tm,
-                    hipStream_t s);
+
+// The backward's products run as extra workgroups of the ELL passes' launches
+// (bwd.hip; device side in backup_tiles.hpp): their operands in the
+// workspace, and their workgroup counts (all zero without backup capacity).
+struct BkBwd {
+    uint8_t *inter; // a, du, dg: [3][NH][R][d_ff] (NH = 2 halves hi, lo for bf16)
+    uint8_t *xo;    // x_O, dy_O: [2][R][d_model]
+    float *part;    // split-K partials of dx_O: [S][R][d_model]
+    int R, S;
+    int n_ud, n_dx, n_dw; // u/da tiles, dx_O tiles, dW tiles
+};
+BkBwd bk_bwd(int dt, int dm, int dff, int max_ovf, void *ws);
 
 // Row `slot` of the backup: words [base, min(base + 64 NW, end, ndw)) of a
 // d_model row (EPW floats each, lane l owning words base + 64 c + l) of sum

@@ -11,10 +11,12 @@
 // ELL rows (gathers, fp32 accumulation, no atomics, deterministic):
 //   1. masks:  per block of 64 rows and per neuron, a 64-bit mask of the
 //      rows holding that neuron; its popcount is the block's count;
-//   2. scans:  per neuron, the prefix of those counts over blocks, then the
-//      prefix over neurons (column pointers). Entry (t, i) then sits at
-//      colptr[i] + prefix[i][block(t)] + popcount(mask bits below t): the
-//      column-major order of the entries, rows ascending inside a column;
+//   2. scans:  per neuron, the prefix of those counts over blocks, and per
+//      group of 64 neurons the prefix of the neurons' totals inside the
+//      group and the group's total. Entry (t, i) then sits at (totals of the
+//      groups before i's) + (i's prefix in its group) + prefix[i][block(t)]
+//      + popcount(mask bits below t): the column-major order of the entries,
+//      rows ascending inside a column;
 //   3. fill: each ELL slot writes its row index at its column-major position;
 //   4. neuron pass (dense-to-sparse, then sparse^T-to-dense): a wave per
 //      neuron keeps its wu_t and wd rows in registers and walks its entries in
@@ -26,18 +28,19 @@
 //   5. dx (sparse-to-dense): a wave per (row, part of d_model) sums
 //      du wu_t[i] + dg wg_t[i] over the row's entries.
 // Rows are gathered with 4-byte lanes (rows.hpp).
-// Backup rows (dense MFMA, fp32 accumulation; the products live in
-// backup.hip):
+// Backup rows (dense MFMA, fp32 accumulation; the tiles live in
+// backup_tiles.hpp):
 //   6. U/DA: u and da of every backup row and neuron, then a, du, dg (dg zero
-//      where h is zero), launched before the ELL passes;
+//      where h is zero), as extra workgroups of the scans launch;
 //   7. DX:   dx of backup rows = [du | dg] [W_u ; W_g]^T as split-K partials,
 //      summed into their rows by the dx pass;
 //   8. DW:   dW = [a | du | dg]^T [dy | x | x] over the backup rows, written
 //      before the neuron pass, which adds the ELL rows' share (a two-term
 //      sum, so its value does not depend on the order of the two passes).
-// The x and dy rows of the backup rows are gathered once by extra workgroups
-// of the masks launch; no operand is transposed.
-#include "backup.hpp"
+// DX and DW ride on the fill launch, and the x and dy rows of the backup rows
+// are gathered once by extra workgroups of the masks launch: five launches in
+// all, with or without backup rows; no operand is transposed.
+#include "backup_tiles.hpp"
 #include "rows.hpp"
 #include "slices.hpp"
 
@@ -63,7 +66,7 @@ inline bool dx_split(int dt, int T, int dm, int dff)
 }
 
 struct Layout {
-    size_t coef, masks, cnt, colptr, csc, backup, wsl, total;
+    size_t coef, masks, cnt, lp, gt, csc, backup, wsl, total;
     int nblk;
     bool split;
 };
@@ -77,7 +80,8 @@ Layout layout(int dt, int T, int dm, int dff, int K, int max_ovf)
     L.coef = o;   o += up256((size_t)2 * T * K * 4); // du, dg per ELL slot
     L.masks = o;  o += up256((size_t)L.nblk * dff * 8);
     L.cnt = o;    o += up256((size_t)L.nblk * dff * 4);
-    L.colptr = o; o += up256((size_t)(dff + 1) * 4);
+    L.lp = o;     o += up256((size_t)dff * 4);
+    L.gt = o;     o += up256((size_t)(dff + 63) / 64 * 4);
     L.csc = o;    o += up256((size_t)T * K * 4);
     L.backup = o; o += up256(bk_workspace(dt, dm, dff, max_ovf, true));
     L.wsl = o;    o += L.split ? up256((size_t)NXCD * dff * 2 * slices(dt, dm).swp * 4) : 0;
@@ -88,37 +92,42 @@ Layout layout(int dt, int T, int dm, int dff, int K, int max_ovf)
 // ------------------------------------------------------------ 1. masks
 // One workgroup per (block of 64 rows, chunk of CH neurons): the masks of the
 // chunk are built in LDS, then written once, coalesced, with their popcounts:
-// masks and cnt are both [nblk][dff].
+// masks and cnt are both [nblk][dff]. Wave w takes the block's rows w, w + 4,
+// ..., lane s reading ELL slot s of each (stored slots only): the sixteen
+// rows' loads go out together.
 DEVI void ell_mask_block(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, int T, int K, int dff,
     uint64_t *__restrict__ masks, int32_t *__restrict__ cnt, int b, int chunk,
-    unsigned long long *m, int *rn)
+    unsigned long long *m)
 {
+    constexpr int NWV = NT / 64, RPW = BR / NWV;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c0 = chunk * CH, c1 = min(dff, c0 + CH);
     const int r0 = b * BR, nr = min(T - r0, BR);
     for (int i = threadIdx.x; i < c1 - c0; i += NT)
         m[i] = 0ull;
-    // stored entries of each of the block's rows (0 for backup rows)
-    if (threadIdx.x < BR)
-        rn[threadIdx.x] = threadIdx.x < nr && row_slot[r0 + threadIdx.x] < 0
-                              ? min(row_nnz[r0 + threadIdx.x], K) : 0;
+    // lane j < RPW: stored entries of the wave's row wv + NWV j (none for
+    // backup rows and rows past T)
+    int rn = 0;
+    if (lane < RPW) {
+        const int r = wv + NWV * lane;
+        if (r < nr && row_slot[r0 + r] < 0)
+            rn = min(row_nnz[r0 + r], K);
+    }
     __syncthreads();
-    // every ELL slot of the block's rows, 8 per thread at a time: loads
-    // unconditional (slot clamped into the block), bits set for stored slots
-    const int nslot = nr * K;
-    const int16_t *base = ell_col + (size_t)r0 * K;
-    for (int q0 = 0; q0 < nslot; q0 += 8 * NT) {
-        int c[8];
+    for (int s0 = 0; __ballot(rn > s0) != 0ull; s0 += 64) {
+        int c[RPW];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            c[u] = base[min(q0 + u * NT + (int)threadIdx.x, nslot - 1)];
+        for (int j = 0; j < RPW; ++j)
+            c[j] = s0 + lane < bcast(rn, j)
+                       ? ell_col[(size_t)(r0 + wv + NWV * j) * K + s0 + lane] : -1;
+        // corrupt columns fall outside every chunk: skipped here, reported
+        // by the fill
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int q = q0 + u * NT + threadIdx.x, r = q / K;
-            if (q < nslot && q - r * K < rn[r] && c[u] >= c0 && c[u] < c1)
-                atomicOr(&m[c[u] - c0], 1ull << r);
-        }
+        for (int j = 0; j < RPW; ++j)
+            if (c[j] >= c0 && c[j] < c1)
+                atomicOr(&m[c[j] - c0], 1ull << (wv + NWV * j));
     }
     __syncthreads();
     for (int i = threadIdx.x; i < c1 - c0; i += NT) {
@@ -128,21 +137,25 @@ DEVI void ell_mask_block(
 }
 
 // ------------------------------------------------------------ 2. scans
-// One workgroup per 64 neurons (a lane each); its four waves take a quarter
-// of the blocks each. Pass 1 sums each wave's counts, the waves' sums are
-// combined in LDS, pass 2 rewrites the counts as exclusive prefixes over the
-// blocks (in place) and the last wave stores the neuron's total, which the
-// column-pointer scan turns into offsets. Loads are unconditional (indices
-// clamped, values masked) so each pass keeps U loads in flight per lane.
-__global__ __launch_bounds__(NT) void blk_prefix_kernel(int32_t *__restrict__ cnt, int nblk, int dff,
-                                                         int32_t *__restrict__ colptr)
+// One workgroup per group of 64 neurons (a lane each); its NTH / 64 waves take
+// a share of the blocks each. Pass 1 sums each wave's counts, the waves' sums
+// are combined in LDS, pass 2 rewrites the counts as exclusive prefixes over
+// the blocks (in place). The last wave holds the neurons' totals: it stores
+// their inclusive prefix inside the group (lp) and the group's total (gt).
+// A neuron's entries then start at the sum of gt over the groups before its
+// own plus lp of the neuron before it in its group (no scan over all
+// neurons, and no launch for one: the fill and the neuron pass add the few
+// group totals themselves). Loads are unconditional (indices clamped,
+// values masked) so each pass keeps U loads in flight per lane.
+template <int NTH>
+DEVI void blk_prefix_block(int g, int32_t *__restrict__ cnt, int nblk, int dff,
+                           int32_t *__restrict__ lp, int32_t *__restrict__ gt, int (*tot)[64])
 {
-    constexpr int U = 8;
-    __shared__ int tot[NT / 64][64];
+    constexpr int U = 8, NWV = NTH / 64;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int i = blockIdx.x * 64 + lane, ic = min(i, dff - 1);
-    const int per = (nblk + NT / 64 - 1) / (NT / 64);
-    const int b0 = wv * per, b1 = min(nblk, b0 + per);
+    const int i = g * 64 + lane, ic = min(i, dff - 1);
+    const int per = (nblk + NWV - 1) / NWV;
+    const int b0 = min(nblk, wv * per), b1 = min(nblk, b0 + per);
     int run = 0;
     for (int b = b0; b < b1; b += U) {
         int v[U];
@@ -158,8 +171,13 @@ __global__ __launch_bounds__(NT) void blk_prefix_kernel(int32_t *__restrict__ cn
     int base = 0;
     for (int w = 0; w < wv; ++w)
         base += tot[w][lane];
-    if (wv == NT / 64 - 1 && i < dff)
-        colptr[i] = base + run;
+    if (wv == NWV - 1) {
+        const int incl = wave_incl_scan(i < dff ? base + run : 0, lane);
+        if (i < dff)
+            lp[i] = incl;
+        if (lane == 63)
+            gt[g] = incl;
+    }
     run = base;
     for (int b = b0; b < b1; b += U) {
         int v[U];
@@ -175,74 +193,69 @@ __global__ __launch_bounds__(NT) void blk_prefix_kernel(int32_t *__restrict__ cn
     }
 }
 
-constexpr int SCAN_NT = 1024;
-
-// In-place exclusive scan of colptr[0..dff); colptr[dff] = total. Thread t
-// owns a run of consecutive elements (at most 32 for d_ff <= 32768): it sums
-// its run (8 loads in flight, indices clamped, values masked), one
-// block-wide scan of the run totals gives each run its start, and the thread
-// rewrites its own run. A clamped load outside the run is never used.
-__global__ __launch_bounds__(SCAN_NT) void colptr_kernel(int32_t *__restrict__ colptr, int dff)
-{
-    __shared__ int wsum[SCAN_NT / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int per = (dff + SCAN_NT - 1) / SCAN_NT;
-    const int b0 = min(dff, tid * per), b1 = min(dff, b0 + per);
-    int tot = 0;
-    for (int k0 = b0; k0 < b1; k0 += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = colptr[min(k0 + u, dff - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            tot += k0 + u < b1 ? v[u] : 0;
-    }
-    const int incl = wave_incl_scan(tot, lane);
-    if (lane == 63)
-        wsum[wv] = incl;
-    __syncthreads();
-    int run = incl - tot;
-    for (int w = 0; w < wv; ++w)
-        run += wsum[w];
-    for (int k0 = b0; k0 < b1; k0 += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = colptr[min(k0 + u, dff - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (k0 + u < b1) {
-                colptr[k0 + u] = run;
-                run += v[u];
-            }
-    }
-    if (tid == SCAN_NT - 1) // the last thread's run ends at the total
-        colptr[dff] = run;
-}
-
 // ------------------------------------------------------------ 3. fill
-__global__ __launch_bounds__(NT) void csc_fill_kernel(
-    const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
-    const int16_t *__restrict__ ell_col, int T, int K, int dff, int nblk,
+// Each stored ELL slot writes its index t K + s at its column-major position.
+// Wave w of workgroup b takes rows FILL_ROWS b + FR w .. + FR - 1 (one 64-row
+// block), lane s slot s of each, all the rows' loads in flight together; wave
+// 0 first scans the group totals into LDS (gpre).
+constexpr int FR = 4;                   // rows per wave of the fill
+constexpr int FILL_ROWS = FR * NT / 64; // rows per workgroup of the fill
+static_assert(BR % FR == 0, "a wave's rows share one mask block");
+DEVI void csc_fill_block(
+    int b, const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
+    const int16_t *__restrict__ ell_col, int T, int K, int dff,
     const uint64_t *__restrict__ masks, const int32_t *__restrict__ blkpre,
-    const int32_t *__restrict__ colptr, int32_t *__restrict__ csc, int32_t *__restrict__ status)
+    const int32_t *__restrict__ lp, const int32_t *__restrict__ gt, int32_t *__restrict__ csc,
+    int32_t *__restrict__ status, int *gpre)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (t >= T || row_slot[t] >= 0)
-        return;
-    const int n = min(row_nnz[t], K), blk = t / BR;
-    const unsigned long long below = (1ull << (t % BR)) - 1ull;
-    for (int s = lane; s < n; s += 64) {
-        const int c = ell_col[(size_t)t * K + s];
-        if (c < 0 || c >= dff) { // corrupt entry: skipped (the masks skip it too), reported
-            raise_status(status, TWELL_DEV_BAD_INDEX);
-            continue;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (wv == 0) { // exclusive prefix of the group totals
+        const int ng = (dff + 63) / 64;
+        int run = 0;
+        for (int g0 = 0; g0 < ng; g0 += 64) {
+            const int g = g0 + lane;
+            const int v = g < ng ? gt[g] : 0;
+            const int incl = wave_incl_scan(v, lane);
+            if (g < ng)
+                gpre[g] = run + incl - v;
+            run += bcast(incl, 63);
         }
-        const int p = colptr[c] + blkpre[(size_t)blk * dff + c] +
-                      __popcll(masks[(size_t)blk * dff + c] & below);
-        csc[p] = t * K + s;
+    }
+    const int t0 = b * FILL_ROWS + wv * FR, blk = t0 / BR;
+    int nn = 0; // lane j < FR: stored entries of row t0 + j (none for backup rows)
+    if (lane < FR && t0 + lane < T && row_slot[t0 + lane] < 0)
+        nn = min(row_nnz[t0 + lane], K);
+    __syncthreads();
+    const size_t mb = (size_t)blk * dff;
+    for (int s0 = 0; __ballot(nn > s0) != 0ull; s0 += 64) {
+        const int s = s0 + lane;
+        int c[FR];
+#pragma unroll
+        for (int j = 0; j < FR; ++j)
+            c[j] = s < bcast(nn, j) ? ell_col[(size_t)(t0 + j) * K + s] : -1;
+        int pre[FR];
+        unsigned long long mk[FR];
+        bool in[FR];
+#pragma unroll
+        for (int j = 0; j < FR; ++j) {
+            in[j] = s < bcast(nn, j);
+            if (in[j] && (c[j] < 0 || c[j] >= dff)) { // corrupt entry: skipped (the masks
+                raise_status(status, TWELL_DEV_BAD_INDEX); // skip it too), reported
+                in[j] = false;
+            }
+            pre[j] = 0;
+            mk[j] = 0ull;
+            if (in[j]) {
+                pre[j] = blkpre[mb + c[j]] + ((c[j] & 63) ? lp[c[j] - 1] : 0);
+                mk[j] = masks[mb + c[j]];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < FR; ++j)
+            if (in[j]) {
+                const unsigned long long below = (1ull << ((t0 + j) % BR)) - 1ull;
+                csc[gpre[c[j] >> 6] + pre[j] + __popcll(mk[j] & below)] = (t0 + j) * K + s;
+            }
     }
 }
 
@@ -251,8 +264,9 @@ __global__ __launch_bounds__(NT) void csc_fill_kernel(
 // words of part `part` (PARTS = NW / NWP parts, one per blockIdx.y).
 template <int DT, int NW, int NWP, int G, int S>
 __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
-    const int32_t *__restrict__ colptr, const int32_t *__restrict__ csc,
-    const void *__restrict__ ell_val, int T, int K, int dff, const uint8_t *__restrict__ x,
+    const int32_t *__restrict__ lp, const int32_t *__restrict__ gt,
+    const int32_t *__restrict__ csc, const void *__restrict__ ell_val, int T, int K, int dff,
+    const uint8_t *__restrict__ x,
     const uint8_t *__restrict__ dy, const uint8_t *__restrict__ wu, const uint8_t *__restrict__ wd,
     int dm, float l1, float *__restrict__ coef, float *__restrict__ dwg, float *__restrict__ dwu,
     float *__restrict__ dwd, const int32_t *__restrict__ n_ovf_p, int max_ovf)
@@ -281,7 +295,13 @@ __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
     // The neuron's entries are dealt to the S waves round-robin (entry p0 + w,
     // p0 + w + S, ...), so the chain of dependent gathers each wave walks is
     // 1/S of the list; the S partial dW rows are summed in LDS below.
-    const int p0 = colptr[i], p1 = colptr[i + 1];
+    // the neuron's entries [p0, p1) of the column-major list: the totals of
+    // the groups of 64 neurons before its own, plus its group's prefix
+    int gs = 0;
+    for (int j = lane; j < (i >> 6); j += 64)
+        gs += gt[j];
+    const int base = bcast(wave_incl_scan(gs, lane), 63);
+    const int p0 = base + ((i & 63) ? lp[i - 1] : 0), p1 = base + lp[i];
     for (int pb = p0 + wv; pb < p1; pb += 64 * S) {
         // lane L prefetches this wave's entry pb + S L: its ELL slot, row and h
         const int p = pb + S * lane;
@@ -460,7 +480,6 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 // launch: workgroups b < n_mask build masks; the next n_copy copy wu_t and
 // wg_t into the dx pass's interleaved slice-major array; the rest gather the
 // backup rows' x and dy rows for the dW products.
-constexpr int MASK_LDS = CH * 8 + BR * 4;
 template <int DT>
 __global__ __launch_bounds__(NT) void mask_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
@@ -471,11 +490,11 @@ __global__ __launch_bounds__(NT) void mask_kernel(
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf_p, int max_ovf,
     int dm)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MASK_LDS];
+    __shared__ unsigned long long lds[CH];
     int b = blockIdx.x;
     if (b < n_mask) {
         ell_mask_block(row_nnz, row_slot, ell_col, T, K, dff, masks, cnt, b / n_chunk,
-                       b % n_chunk, (unsigned long long *)lds, (int *)(lds + CH * 8));
+                       b % n_chunk, lds);
         return;
     }
     b -= n_mask;
@@ -484,6 +503,52 @@ __global__ __launch_bounds__(NT) void mask_kernel(
         return;
     }
     bk_gather_block<DT, NT>(b - n_copy, bg, x, dy, ovf_rows, n_ovf_p, max_ovf, dm);
+}
+
+// ------------------------------------------------------------ scans launch
+// Workgroups g < n_grp run the block scans of neuron group g; the rest are the
+// backup rows' u/da tiles, which need nothing from the masks launch.
+template <int DT>
+__global__ __launch_bounds__(bk::UD_NT, 1) void prefix_ud_kernel(
+    int32_t *__restrict__ cnt, int nblk, int dff, int32_t *__restrict__ lp,
+    int32_t *__restrict__ gt, int n_grp, BkBwd bw, const uint8_t *__restrict__ x,
+    const uint8_t *__restrict__ dy, const int32_t *__restrict__ ovf_rows,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, const uint8_t *__restrict__ wu,
+    const uint8_t *__restrict__ wd, int dm, const void *__restrict__ dense, float l1)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t L[bk::ud_lds<DT>()];
+    if ((int)blockIdx.x < n_grp) {
+        blk_prefix_block<bk::UD_NT>(blockIdx.x, cnt, nblk, dff, lp, gt, (int (*)[64])L);
+        return;
+    }
+    bk::ud_block<DT>(blockIdx.x - n_grp, bw, x, dy, ovf_rows, n_ovf_p, max_ovf, wu, wd, dm, dff,
+                     dense, l1, L);
+}
+
+// ------------------------------------------------------------ fill launch
+// Workgroups b < n_fill fill the CSC list; the rest are the backup rows' dx_O
+// and dW tiles (their dW tiles write dW, to which the neuron pass adds the
+// ELL rows' share; the dx pass sums their dx partials).
+template <int DT>
+__global__ __launch_bounds__(NT, 3) void fill_dxdw_kernel(
+    const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
+    const int16_t *__restrict__ ell_col, int T, int K, int dff,
+    const uint64_t *__restrict__ masks, const int32_t *__restrict__ blkpre,
+    const int32_t *__restrict__ lp, const int32_t *__restrict__ gt, int32_t *__restrict__ csc,
+    int32_t *__restrict__ status, int n_fill, BkBwd bw, const uint8_t *__restrict__ wu,
+    const uint8_t *__restrict__ wg, const int32_t *__restrict__ n_ovf_p, int max_ovf, int dm,
+    float *__restrict__ dwd, float *__restrict__ dwu, float *__restrict__ dwg)
+{
+    static_assert(bk::DX::NT == NT, "one workgroup size for both");
+    static_assert(bk::DX::LDS >= 512 * 4, "group offsets of d_ff <= 32768");
+    __shared__ __attribute__((aligned(16))) uint8_t L[bk::DX::LDS];
+    if ((int)blockIdx.x < n_fill) {
+        csc_fill_block(blockIdx.x, row_nnz, row_slot, ell_col, T, K, dff, masks, blkpre, lp, gt,
+                       csc, status, (int *)L);
+        return;
+    }
+    bk::dxdw_block<DT>(blockIdx.x - n_fill, bw, wu, wg, n_ovf_p, max_ovf, dm, dff, dwd, dwu, dwg,
+                       L);
 }
 
 // ------------------------------------------------------------ 5'. dx, XCD-local
@@ -601,7 +666,8 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
     const Layout L = layout(DT, T, dm, dff, K, h->max_ovf);
     float *coef = (float *)(ws + L.coef);
     uint64_t *masks = (uint64_t *)(ws + L.masks);
-    int32_t *cnt = (int32_t *)(ws + L.cnt), *colptr = (int32_t *)(ws + L.colptr);
+    int32_t *cnt = (int32_t *)(ws + L.cnt), *lp = (int32_t *)(ws + L.lp);
+    int32_t *gt = (int32_t *)(ws + L.gt);
     int32_t *csc = (int32_t *)(ws + L.csc);
     const uint8_t *xb = (const uint8_t *)x, *dyb = (const uint8_t *)dy;
     const int rgroups = (T + NT / 64 - 1) / (NT / 64);
@@ -628,24 +694,25 @@ void launch_all(const void *x, const void *dy, const hybrid_t *h, const void *wg
                            bg, xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf, dm);
         tm.mark("mask_kernel");
     }
-    launch_bk_ud((twell_dtype)DT, x, dy, h, wu, wd, dm, l1, ws + L.backup, tm, s);
-    hipLaunchKernelGGL(blk_prefix_kernel, dim3((dff + 63) / 64), dim3(NT), 0, s, cnt, L.nblk, dff,
-                       colptr);
-    tm.mark("blk_prefix_kernel");
-    hipLaunchKernelGGL(colptr_kernel, dim3(1), dim3(SCAN_NT), 0, s, colptr, dff);
-    tm.mark("colptr_kernel");
-    if (T > 0) {
-        hipLaunchKernelGGL(csc_fill_kernel, dim3(rgroups), dim3(NT), 0, s, h->row_nnz,
-                           h->row_slot, h->ell_col, T, K, dff, L.nblk, masks, cnt, colptr, csc,
-                           status);
-        tm.mark("csc_fill_kernel");
+    // the backup rows' products (none without backup capacity or rows)
+    const BkBwd bw = T > 0 ? bk_bwd(DT, dm, dff, h->max_ovf, ws + L.backup) : BkBwd{};
+    const int n_grp = (dff + 63) / 64;
+    hipLaunchKernelGGL((prefix_ud_kernel<DT>), dim3(n_grp + bw.n_ud), dim3(bk::UD_NT), 0, s, cnt,
+                       L.nblk, dff, lp, gt, n_grp, bw, xb, dyb, h->ovf_rows, h->n_ovf, h->max_ovf,
+                       (const uint8_t *)wu, (const uint8_t *)wd, dm, h->dense, l1);
+    tm.mark("prefix_ud_kernel");
+    const int n_fill = (T + FILL_ROWS - 1) / FILL_ROWS;
+    if (n_fill + bw.n_dx + bw.n_dw > 0) {
+        hipLaunchKernelGGL((fill_dxdw_kernel<DT>), dim3(n_fill + bw.n_dx + bw.n_dw), dim3(NT), 0,
+                           s, h->row_nnz, h->row_slot, h->ell_col, T, K, dff, masks, cnt, lp, gt,
+                           csc, status, n_fill, bw, (const uint8_t *)wu, (const uint8_t *)wg,
+                           h->n_ovf, h->max_ovf, dm, dwd, dwu, dwg);
+        tm.mark("fill_dxdw_kernel");
     }
-    // the backup rows' dW products write dW (the neuron pass adds the ELL
-    // rows' share to it); their dx partials are summed by the dx pass
-    launch_bk_dxdw((twell_dtype)DT, h, wu, wg, dm, dx, dwd, dwu, dwg, ws + L.backup, tm, s);
     hipLaunchKernelGGL((bwd_neuron_kernel<DT, NW, NWN, GN, NSPLIT>), dim3(dff, NW / NWN),
-                       dim3(64 * NSPLIT), 0, s, colptr, csc, h->ell_val, T, K, dff, xb, dyb, (const uint8_t *)wu,
-                       (const uint8_t *)wd, dm, l1, coef, dwg, dwu, dwd, h->n_ovf, h->max_ovf);
+                       dim3(64 * NSPLIT), 0, s, lp, gt, csc, h->ell_val, T, K, dff, xb, dyb,
+                       (const uint8_t *)wu, (const uint8_t *)wd, dm, l1, coef, dwg, dwu, dwd,
+                       h->n_ovf, h->max_ovf);
     tm.mark("bwd_neuron_kernel");
     if (T > 0) {
         const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, true, ws + L.backup);
