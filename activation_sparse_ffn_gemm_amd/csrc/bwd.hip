@@ -102,7 +102,7 @@ DEVI void ell_mask_block(
     unsigned long long *m)
 {
     constexpr int NWV = NT / 64, RPW = BR / NWV;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int c0 = chunk * CH, c1 = min(dff, c0 + CH);
     const int r0 = b * BR, nr = min(T - r0, BR);
     for (int i = threadIdx.x; i < c1 - c0; i += NT)
@@ -152,7 +152,7 @@ DEVI void blk_prefix_block(int g, int32_t *__restrict__ cnt, int nblk, int dff,
                            int32_t *__restrict__ lp, int32_t *__restrict__ gt, int (*tot)[64])
 {
     constexpr int U = 8, NWV = NTH / 64;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int i = g * 64 + lane, ic = min(i, dff - 1);
     const int per = (nblk + NWV - 1) / NWV;
     const int b0 = min(nblk, wv * per), b1 = min(nblk, b0 + per);
@@ -208,7 +208,7 @@ DEVI void csc_fill_block(
     const int32_t *__restrict__ lp, const int32_t *__restrict__ gt, int32_t *__restrict__ csc,
     int32_t *__restrict__ status, int *gpre)
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     if (wv == 0) { // exclusive prefix of the group totals
         const int ng = (dff + 63) / 64;
         int run = 0;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(64 * S) void bwd_neuron_kernel(
     constexpr int EPW = R::EPW;
     constexpr int PL = NWP * 64 * EPW; // elements of one part of a row
     __shared__ __attribute__((aligned(16))) float red[S > 1 ? S : 1][S > 1 ? PL : 4];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int i = blockIdx.x, part = blockIdx.y;
     const R geo(dm, lane, 0);
     const RP pgeo(dm, lane, part);
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(NT) void bwd_dx_kernel(
 {
     using R = Row<DT, NW>;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+    const int t = blockIdx.x * (NT / 64) + wave_id();
     if (t >= T)
         return;
     const R geo(dm, lane, blockIdx.y);
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(NT) void bwd_dxs_kernel(
     int max_ovf)
 {
     constexpr int EPW = DT == TWELL_BF16 ? 2 : 1;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int k = blockIdx.x % NXCD;
     const int t = (blockIdx.x / NXCD) * (NT / 64) + wv;
     const int nk = sl.valid(k);

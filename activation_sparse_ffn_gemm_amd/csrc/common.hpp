@@ -107,6 +107,10 @@ DEVI int wave_incl_scan(int v, int lane)
 
 DEVI uint32_t lanemask_lt32(int lane32) { return (1u << lane32) - 1u; }
 
+// This wave's index in its workgroup, as a scalar: values derived from it
+// (a token or row per wave, its row pointers) then live in scalar registers.
+DEVI int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Broadcast lane `src` (wave-uniform) of v to every lane, through a scalar register.
 DEVI int bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 DEVI float bcast(float v, int src)

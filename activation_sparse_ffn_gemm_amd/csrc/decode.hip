@@ -519,7 +519,7 @@ __global__ __launch_bounds__(DNT) void dec_pack_kernel(
     const float *__restrict__ part, int32_t *count, int16_t *col, void *val, float *aw,
     int32_t *status)
 {
-    const int p = blockIdx.x * DW + (threadIdx.x >> 6);
+    const int p = blockIdx.x * DW + wave_id();
     if (p < P.T * P.nt)
         pack_up_item<DT, NW, G, UP>(P, x, wu, part, p, count, col, val, aw, status);
 }
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(DNT) void dec_up_kernel(
     const int32_t *__restrict__ count, const int16_t *__restrict__ col,
     const void *__restrict__ val, float *aw, int32_t *status)
 {
-    const int p = blockIdx.x * DW + (threadIdx.x >> 6);
+    const int p = blockIdx.x * DW + wave_id();
     if (p < P.T * P.nt)
         up_item<DT, NW, G>(P, x, wu, count, col, val, p, aw, status);
 }

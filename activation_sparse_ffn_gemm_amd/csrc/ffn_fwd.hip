@@ -45,10 +45,11 @@ inline bool use_split(int dt, int T, int dm, int dff)
 // Stage the stored entries of row t, tiles [j0, j1), into LDS: element e of
 // the list is (column, value). Calls fn(p0, ne) after each pass of up to LIST
 // entries, p0 being the index of the pass's first entry among the range's
-// entries (in column order). A lane reads the slots of one tile, 8
-// independent loads at a time, through buffer descriptors over row t's slots:
-// 32-bit offsets instead of 64-bit addresses keep the staging's registers
-// few (measured: the 1.5B up pass about 10% faster). Slots past a tile's
+// entries (in column order). A lane reads the slots of one tile, 4
+// independent loads at a time (most tiles hold one or two entries; eight at a
+// time cost the fused 0.5B pass a wave per SIMD), through buffer descriptors
+// over row t's slots: 32-bit offsets instead of 64-bit addresses keep the
+// staging's registers few (measured: the 1.5B up pass about 10% faster). Slots past a tile's
 // count (the next tile's, or past the row: 0 from the range check) are read
 // but never used. With VALS false val is not read.
 template <int DT, bool VALS, class Fn>
@@ -70,13 +71,13 @@ DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *
         const int excl = incl - n;
         const int tot = __shfl(incl, 63, 64);
         for (int p0 = 0; p0 < tot; p0 += LIST) {
-            for (int s0 = max(0, p0 - excl); s0 < n && excl + s0 < p0 + LIST; s0 += 8) {
-                // branch-free: every lane issues its 8 loads before any is used
+            for (int s0 = max(0, p0 - excl); s0 < n && excl + s0 < p0 + LIST; s0 += 4) {
+                // branch-free: every lane issues its loads before any is used
                 const int q = j * W + s0;
-                int c[8];
-                float v[8];
+                int c[4];
+                float v[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     c[u] = (int16_t)__builtin_amdgcn_raw_buffer_load_b16(rc, (q + u) * 2, 0, 0);
                     if constexpr (!VALS)
                         v[u] = 0.f;
@@ -86,7 +87,7 @@ DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *
                         v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (q + u) * 4, 0, 0));
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     const int e = excl + s0 + u - p0;
                     if (s0 + u < n && e < LIST) {
                         if (c[u] < 0 || c[u] >= dff) { // corrupt entry: skipped and reported
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(NT) void ffn_fwd_kernel(
     using RP = Row<DT, NWP>; // this wave's part of the row, for the down projection
     __shared__ int lcol[NT / 64][LIST];
     __shared__ float lval[NT / 64][LIST];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int t = blockIdx.x * (NT / 64) + wv;
     if (t >= T)
         return;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NT) void fwd_up_kernel(
     using R = Row<DT, NW>;
     __shared__ int lcol[NT / 64][LIST];
     __shared__ float lval[NT / 64][LIST];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     int b = blockIdx.x;
     if (b < n_copy) {
         copy_slices(b, wd, wds, dff, sl);
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(NT) void hfwd_up_kernel(
     __shared__ int lcol[NT / 64][64];
     __shared__ int lslot[NT / 64][64];
     __shared__ float lval[NT / 64][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     int b = blockIdx.x;
     if (b < n_copy) {
         copy_slices(b, wd, wds, dff, sl);
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(NT) void fwd_down_kernel(
     float *__restrict__ y, const int32_t *__restrict__ row_slot, BkPart bp, int max_ovf)
 {
     constexpr int EPW = DT == TWELL_BF16 ? 2 : 1;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int k = blockIdx.x % NXCD;
     const int t = (blockIdx.x / NXCD) * (NT / 64) + wv;
     const int nk = sl.valid(k);

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(NT) void hfwd_ell_kernel(
     using R = Row<DT, NW>;   // whole row, for the up dot product
     using RP = Row<DT, NWP>; // this wave's part of the row, for the down projection
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+    const int t = blockIdx.x * (NT / 64) + wave_id();
     if (t >= T)
         return;
     const R geo(dm, lane, 0);

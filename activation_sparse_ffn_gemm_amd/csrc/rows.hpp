@@ -37,9 +37,15 @@ template <int DT, int NW> struct Row {
         const int bytes = ndw > base ? (ndw - base) * 4 : 0;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(m + row * 4), (short)0, bytes, BUF_DWORD3);
+        // the lane's byte offset is redefined here (an empty asm, no code), so
+        // that it is not hoisted out of a caller's loop: each load then folds
+        // c * 256 into its immediate offset instead of holding NW offsets in
+        // vector registers across the loop
+        int off = lane * 4;
+        asm volatile("" : "+v"(off));
 #pragma unroll
         for (int c = 0; c < NW; ++c)
-            w[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (c * 64 + lane) * 4, 0, 0);
+            w[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + c * 256, 0, 0);
     }
 
     DEVI void widen(uint32_t w, float (&f)[EPW]) const

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
 {
     using S = typename elem<DT>::storage;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = blockIdx.x * 4 + wave_id();
     if (t >= T)
         return;
     // tile j's n stored entries to ELL slots [excl, excl + n) of row t, 8 at a
