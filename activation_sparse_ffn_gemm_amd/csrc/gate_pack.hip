@@ -48,6 +48,14 @@ template <class C> constexpr int kernel_lds()
     return pack_lds<C>() > C::LDS ? pack_lds<C>() : C::LDS;
 }
 
+// v_writelane through its compiler intrinsic (no HIP builtin for it here):
+// lane `lane` of `old` becomes the wave-uniform `v`.
+extern "C" __device__ int amdgcn_writelane_i32(int v, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+DEVI uint32_t lane_write(uint32_t old, uint32_t v, int lane)
+{
+    return (uint32_t)amdgcn_writelane_i32((int)v, lane, (int)old);
+}
+
 template <class C>
 DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, int nt, int W,
                     int wm, int wn, int lane, int32_t *__restrict__ count,
@@ -74,25 +82,36 @@ DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, 
             }
         }
     // g > 0 masks: ballot i (over mi, e, ni in that order) covers rows r (lanes
-    // 0-31) and r + 4 (lanes 32-63) of one 32-column block. Its two words are
-    // gathered into lanes 2 i and 2 i + 1 (mod 64) of a register, 32 ballots
-    // per register, and each lane then stores one row's word: four LDS stores
-    // per wave instead of one per ballot.
+    // 0-31) and r + 4 (lanes 32-63) of one 32-column block. The ballot stays
+    // in scalar registers and its two words are written straight into lanes
+    // 2 i and 2 i + 1 (mod 64) of a register (v_writelane), 32 ballots per
+    // register; each lane then stores one row's word: four LDS stores per
+    // wave: one compare and two lane writes per ballot.
     constexpr int NBAL = C::MI * 16 * C::NI;
     static_assert(NBAL % 32 == 0, "whole registers of ballots");
     uint32_t mv[NBAL / 32];
 #pragma unroll
+    for (int q = 0; q < NBAL / 32; ++q)
+        mv[q] = 0u;
+    // rows of the tile past T get no bits: a wave-uniform mask per (mi, e)
+    const int rlim = T - m0 - wm * C::WM; // rows r of this wave's block are valid if r < rlim
+#pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
+        for (int e = 0; e < 16; ++e) {
+            const int r = mi * 32 + 8 * (e >> 2) + (e & 3);
+            const uint32_t ok0 = r < rlim ? ~0u : 0u, ok1 = r + 4 < rlim ? ~0u : 0u;
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) {
                 const int i = (mi * 16 + e) * C::NI + ni;
-                const int r = wm * C::WM + mi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-                const uint64_t b = __ballot(m0 + r < T && acc.v[mi][ni][e] > 0.f);
-                if (lane >> 1 == i % 32) // lanes 2 i % 64 and 2 i % 64 + 1
-                    mv[i / 32] = (uint32_t)(b >> (32 * (lane & 1)));
+                const uint64_t b = __ballot(acc.v[mi][ni][e] > 0.f);
+                mv[i / 32] = lane_write(mv[i / 32], (uint32_t)b & ok0, 2 * (i % 32));
+                mv[i / 32] = lane_write(mv[i / 32], (uint32_t)(b >> 32) & ok1, 2 * (i % 32) + 1);
+                // keep each ballot next to its lane writes: hoisted together,
+                // the ballots would not fit the scalar registers
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
 #pragma unroll
     for (int q = 0; q < NBAL / 32; ++q) {
         const int i = q * 32 + lane / 2, ni = i % C::NI, e = (i / C::NI) % 16,
