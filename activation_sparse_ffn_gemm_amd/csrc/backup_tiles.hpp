@@ -74,6 +74,20 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
     auto rowa = [&](int r) { return src + (size_t)ovf_rows[min(m0 + r, n - 1)] * rowbytes; };
     auto rowb = [&](int r) { return w + (size_t)(i0 + r) * rowbytes; };
     const int kt0 = BWD ? 0 : grp * (nk / 2), kt1 = BWD ? nk : kt0 + nk / 2;
+    // the stored h of this wave's epilogue elements (block row grp), requested
+    // before the K loop: their latency then overlaps the first K step's loads
+    // instead of following the accumulator swap
+    const int mi = grp;
+    typename E::storage hraw[NI][16];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
+            const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
+            hraw[ni][e] = m < n ? ((const typename E::storage *)dense)[(size_t)m * dff + i]
+                                : typename E::storage(0);
+        }
     ng::Acc<CU> acc; // group 0: u (fwd: its first K half); group 1: da (fwd: u, second half)
     ng::mainloop<CU, DT>(L + grp * CU::LDS, rowa, rowb, off, kt0, kt1, acc, grp * CU::NWV);
     // swap: group g stores block row 1 - g of its accumulators in exchange
@@ -113,16 +127,16 @@ DEVI void ud_tile(const uint8_t *__restrict__ x, const uint8_t *__restrict__ dy,
         }
     __syncthreads(); // L is free again
     // block row grp of this wave: u and (bwd) da of each element
-    const int mi = grp;
     const size_t plane = (size_t)R * dff; // elements per intermediate array
     float hv[NI][16];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int m = m0 + ng::acc_row<CU>(wm, mi, e, lane);
-            const int i = i0 + ng::acc_col<CU>(wn, ni, lane);
-            hv[ni][e] = m < n ? E::load1(dense, (size_t)m * dff + i) : 0.f;
+            if constexpr (DT == TWELL_BF16)
+                hv[ni][e] = bf16_to_f32(hraw[ni][e]);
+            else
+                hv[ni][e] = hraw[ni][e];
         }
     // own / oth become a and (bwd) du, hv becomes dg
 #pragma unroll
