@@ -239,8 +239,9 @@ DEVI void csc_fill_block(
 #pragma unroll
         for (int j = 0; j < FR; ++j) {
             in[j] = s < bcast(nn, j);
-            if (in[j] && (c[j] < 0 || c[j] >= dff)) { // corrupt entry: skipped (the masks
-                raise_status(status, TWELL_DEV_BAD_INDEX); // skip it too), reported
+            // a corrupt entry is skipped (the masks skip it too) and reported
+            if (in[j] && (c[j] < 0 || c[j] >= dff)) {
+                raise_status(status, TWELL_DEV_BAD_INDEX);
                 in[j] = false;
             }
             pre[j] = 0;

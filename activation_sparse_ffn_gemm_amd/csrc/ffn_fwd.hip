@@ -49,9 +49,9 @@ inline bool use_split(int dt, int T, int dm, int dff)
 // independent loads at a time (most tiles hold one or two entries; eight at a
 // time cost the fused 0.5B pass a wave per SIMD), through buffer descriptors
 // over row t's slots: 32-bit offsets instead of 64-bit addresses keep the
-// staging's registers few (measured: the 1.5B up pass about 10% faster). Slots past a tile's
-// count (the next tile's, or past the row: 0 from the range check) are read
-// but never used. With VALS false val is not read.
+// staging's registers few (measured: the 1.5B up pass about 10% faster).
+// Slots past a tile's count (the next tile's, or past the row: 0 from the
+// range check) are read but never used. With VALS false val is not read.
 template <int DT, bool VALS, class Fn>
 DEVI void for_row_entries(const int32_t *count, const int16_t *col, const void *val, int t,
                           int nt, int W, int j0, int j1, int dff, int lane, int *lcol, float *lval,

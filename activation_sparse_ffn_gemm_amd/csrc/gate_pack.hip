@@ -85,8 +85,8 @@ DEVI void pack_bf16(const ng::Acc<C> &acc, uint8_t *lds, int m0, int n0, int T, 
     // 0-31) and r + 4 (lanes 32-63) of one 32-column block. The ballot stays
     // in scalar registers and its two words are written straight into lanes
     // 2 i and 2 i + 1 (mod 64) of a register (v_writelane), 32 ballots per
-    // register; each lane then stores one row's word: four LDS stores per
-    // wave: one compare and two lane writes per ballot.
+    // register, so a ballot costs one compare and two lane writes; each lane
+    // then stores one row's word (four LDS stores per wave).
     constexpr int NBAL = C::MI * 16 * C::NI;
     static_assert(NBAL % 32 == 0, "whole registers of ballots");
     uint32_t mv[NBAL / 32];
