@@ -531,7 +531,7 @@ __global__ __launch_bounds__(bk::UD_NT, 1) void prefix_ud_kernel(
 // and dW tiles (their dW tiles write dW, to which the neuron pass adds the
 // ELL rows' share; the dx pass sums their dx partials).
 template <int DT>
-__global__ __launch_bounds__(NT, 3) void fill_dxdw_kernel(
+__global__ __launch_bounds__(NT, 5) void fill_dxdw_kernel(
     const int32_t *__restrict__ row_nnz, const int32_t *__restrict__ row_slot,
     const int16_t *__restrict__ ell_col, int T, int K, int dff,
     const uint64_t *__restrict__ masks, const int32_t *__restrict__ blkpre,
