@@ -77,13 +77,16 @@ def oracle_bwd(orc, d, ref, l1=0.0):
                                                 (300, 512, 1024, 40, 21, 0.0),
                                                 (77, 320, 256, 128, 0, 0.0),
                                                 (150, 192, 384, 12, 9, 0.5),
+                                                (130, 128, 16384, 512, 5, 0.0),
                                                 (1024, 2048, 4096, 256, 51, 0.0),
                                                 (1024, 2304, 4096, 256, 51, 0.0)])
 def test_bwd_integer_exact(orc, dtype, T, dm, dff, K, skew, l1):
     """Integer inputs (and an L1 weight of 0.5): ELL gathers and the backup
     rows' hi/lo MFMA products are exact, so every gradient matches the oracle
-    bit for bit. The last two shapes (1024 tokens, 16 MB or more of weights in
-    bf16) take the XCD-local dx pass (slices of 512 and 576 bytes)."""
+    bit for bit. d_ff 16384 gives 256 groups of 64 neurons (the column offsets
+    sum many group totals) and 16 mask chunks. The last two shapes (1024
+    tokens, 16 MB or more of weights in bf16) take the XCD-local dx pass
+    (slices of 512 and 576 bytes)."""
     if dtype == "f32" and T == 1024:
         pytest.skip("one dtype is enough for the two-pass shape")
     announce("bwd int", dtype, T, dm, dff, K, skew, l1)
