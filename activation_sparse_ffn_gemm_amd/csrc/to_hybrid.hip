@@ -3,17 +3,20 @@
 // so rows with few nonzeros go to a compact ELL matrix and overflow rows are
 // redirected to a dense backup, through a dedicated conversion kernel).
 //
-// Three launches, all integer / copy work:
-//   1. rows:  one wave per row sums the tile counts (row_nnz) and, for a row
-//             with row_nnz <= K, concatenates its tiles into ELL row t; the
-//             tiles are in column order, so the ELL row is ascending.
-//   2. slots: one thread per row; a workgroup counts the overflow rows of
-//             the blocks before its own (a reduction over row_nnz) and scans
-//             its block's flags, so backup slots follow ascending row order;
-//             writes row_slot and ovf_rows, and the last block n_ovf.
-//   3. dense: one workgroup per backup slot builds that row (zeros, then its
-//             entries) in LDS and stores it with 16-byte lanes, all backup
-//             rows at once.
+// Two launches, all integer / copy work:
+//   1. rows:   one wave per row sums the tile counts (row_nnz) and, for a row
+//              with row_nnz <= K, concatenates its tiles into ELL row t; the
+//              tiles are in column order, so the ELL row is ascending.
+//   2. backup: R workgroups per block of 256 rows. Each counts the overflow
+//              rows of the blocks before its own (a reduction over row_nnz)
+//              and scans its block's flags, so backup slots follow ascending
+//              row order; the first of the R writes row_slot and ovf_rows (and,
+//              in the last block, n_ovf), and workgroup j builds the block's
+//              backup rows j, j + R, ... (zeros, then the row's entries) in
+//              LDS and stores them with 16-byte lanes. Slots and dense rows
+//              share the launch, so backup rows cost no launch of their own.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace {
@@ -83,19 +86,77 @@ __global__ __launch_bounds__(256) void hyb_rows_kernel(
     }
 }
 
-constexpr int SNT = 256;       // threads (and rows) per workgroup of the slot launch
-constexpr int DNT = 256;       // threads per workgroup of the dense launch
+constexpr int SNT = 256;       // threads (and rows) per workgroup of the backup launch
 constexpr int ROW_LDS = 32768; // bytes of one dense row built in LDS (d_ff 16384 bf16 / 8192 f32)
+constexpr int RMAX = 32;       // workgroups per block of rows (backup rows built in parallel)
 
-__global__ __launch_bounds__(SNT) void hyb_slots_kernel(
-    const int32_t *__restrict__ row_nnz, int T, int K, int max_ovf,
+// Backup row `slot` from TwELL row t, by the whole workgroup: zeros, then
+// every stored entry of the row's tiles (loads unconditional, 8 per thread at
+// a time; stores of stored slots only), in LDS and then to memory with
+// 16-byte lanes (rows wider than the LDS buffer are built in memory).
+template <int DT>
+DEVI void build_dense_row(const int32_t *__restrict__ count, const int16_t *__restrict__ col,
+                          const void *__restrict__ val, int nt, int W, int dff, int t, int slot,
+                          void *__restrict__ dense, int32_t *__restrict__ status,
+                          uint8_t *rowbuf)
+{
+    using S = typename elem<DT>::storage;
+    const int tid = threadIdx.x;
+    S *drow = (S *)dense + (size_t)slot * dff;
+    const bool in_lds = (size_t)dff * sizeof(S) <= ROW_LDS;
+    S *brow = in_lds ? (S *)rowbuf : drow;
+    if (in_lds)
+        for (int i = tid; i < dff * (int)sizeof(S) / 16; i += SNT)
+            ((uint4 *)rowbuf)[i] = make_uint4(0, 0, 0, 0);
+    else
+        for (int i = tid; i < dff; i += SNT)
+            drow[i] = S(0);
+    __syncthreads();
+    const size_t src = (size_t)t * nt * W;
+    const int nslot = nt * W;
+    for (int q0 = 0; q0 < nslot; q0 += 8 * SNT) {
+        int c[8], n[8];
+        S v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = min(q0 + u * SNT + tid, nslot - 1);
+            n[u] = count[(size_t)t * nt + q / W];
+            c[u] = col[src + q];
+            v[u] = ((const S *)val)[src + q];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u * SNT + tid;
+            if (q < nslot && q % W < min(n[u], W)) {
+                if (c[u] >= 0 && c[u] < dff)
+                    brow[c[u]] = v[u];
+                else
+                    raise_status(status, TWELL_DEV_BAD_INDEX);
+            }
+        }
+    }
+    __syncthreads();
+    if (in_lds)
+        for (int i = tid; i < dff * (int)sizeof(S) / 16; i += SNT)
+            ((uint4 *)drow)[i] = ((const uint4 *)rowbuf)[i];
+    __syncthreads(); // the buffer is rebuilt by the workgroup's next row
+}
+
+template <int DT>
+__global__ __launch_bounds__(SNT) void hyb_backup_kernel(
+    const int32_t *__restrict__ row_nnz, int T, int K, int max_ovf, int R,
     int32_t *__restrict__ row_slot, int32_t *__restrict__ ovf_rows, int32_t *__restrict__ n_ovf,
+    const int32_t *__restrict__ count, const int16_t *__restrict__ col,
+    const void *__restrict__ val, int nt, int W, int dff, void *__restrict__ dense,
     int32_t *__restrict__ status)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[ROW_LDS];
     __shared__ int wsum[SNT / 64];
     __shared__ int n_before;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int r0 = blockIdx.x * SNT;
+    __shared__ int brows[SNT]; // the block's backup rows, by slot - first slot of the block
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+    const int blk = blockIdx.x / R, j = blockIdx.x % R;
+    const int r0 = blk * SNT;
     if (tid == 0)
         n_before = 0;
     __syncthreads();
@@ -121,79 +182,36 @@ __global__ __launch_bounds__(SNT) void hyb_slots_kernel(
     if (lane == 0)
         wsum[wv] = __popcll(m);
     __syncthreads();
-    int before = n_before;
+    int in_blk = 0; // overflow rows of this block before this thread's wave
     for (int w = 0; w < wv; ++w)
-        before += wsum[w];
-    const int slot = before + __popcll(m & ((1ull << lane) - 1ull));
-    if (t < T) {
-        row_slot[t] = f ? slot : -1;
-        if (f && slot < max_ovf)
-            ovf_rows[slot] = t;
-    }
-    if (tid == SNT - 1 && r0 + SNT >= T) { // last block: the true total
-        int total = n_before;
-        for (int w = 0; w < SNT / 64; ++w)
-            total += wsum[w];
-        *n_ovf = total;
-        if (total > max_ovf)
-            raise_status(status, TWELL_DEV_OVF_CAPACITY);
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(DNT) void hyb_dense_kernel(
-    const int32_t *__restrict__ count, const int16_t *__restrict__ col,
-    const void *__restrict__ val, int nt, int W, int dff, int max_ovf,
-    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ n_ovf,
-    void *__restrict__ dense, int32_t *__restrict__ status)
-{
-    using S = typename elem<DT>::storage;
-    __shared__ __attribute__((aligned(16))) uint8_t rowbuf[ROW_LDS];
-    const int slot = blockIdx.x, tid = threadIdx.x;
-    if (slot >= min(*n_ovf, max_ovf))
-        return;
-    const int t = ovf_rows[slot];
-    S *drow = (S *)dense + (size_t)slot * dff;
-    // rows wider than the LDS buffer are built straight in memory
-    const bool in_lds = (size_t)dff * sizeof(S) <= ROW_LDS;
-    S *brow = in_lds ? (S *)rowbuf : drow;
-    if (in_lds)
-        for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
-            ((uint4 *)rowbuf)[i] = make_uint4(0, 0, 0, 0);
-    else
-        for (int i = tid; i < dff; i += DNT)
-            drow[i] = S(0);
-    __syncthreads();
-    // every slot of the row's TwELL tiles, 8 per thread at a time (loads
-    // unconditional, stores of the stored slots only)
-    const size_t src = (size_t)t * nt * W;
-    const int nslot = nt * W;
-    for (int q0 = 0; q0 < nslot; q0 += 8 * DNT) {
-        int c[8], n[8];
-        S v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int q = min(q0 + u * DNT + tid, nslot - 1);
-            n[u] = count[(size_t)t * nt + q / W];
-            c[u] = col[src + q];
-            v[u] = ((const S *)val)[src + q];
+        in_blk += wsum[w];
+    const int first = n_before;
+    const int rank = in_blk + __popcll(m & ((1ull << lane) - 1ull)); // within the block
+    const int slot = first + rank;
+    if (f)
+        brows[rank] = t;
+    if (j == 0) {
+        if (t < T) {
+            row_slot[t] = f ? slot : -1;
+            if (f && slot < max_ovf)
+                ovf_rows[slot] = t;
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int q = q0 + u * DNT + tid;
-            if (q < nslot && q % W < min(n[u], W)) {
-                if (c[u] >= 0 && c[u] < dff)
-                    brow[c[u]] = v[u];
-                else
-                    raise_status(status, TWELL_DEV_BAD_INDEX);
-            }
+        if (tid == SNT - 1 && r0 + SNT >= T) { // last block: the true total
+            int total = first;
+            for (int w = 0; w < SNT / 64; ++w)
+                total += wsum[w];
+            *n_ovf = total;
+            if (total > max_ovf)
+                raise_status(status, TWELL_DEV_OVF_CAPACITY);
         }
     }
-    if (in_lds) {
-        __syncthreads();
-        for (int i = tid; i < dff * (int)sizeof(S) / 16; i += DNT)
-            ((uint4 *)drow)[i] = ((const uint4 *)rowbuf)[i];
-    }
+    int nb = 0; // backup rows of this block
+    for (int w = 0; w < SNT / 64; ++w)
+        nb += wsum[w];
+    __syncthreads(); // brows complete
+    for (int k = j; k < nb && first + k < max_ovf; k += R)
+        build_dense_row<DT>(count, col, val, nt, W, dff, brows[k], first + k, dense, status,
+                            rowbuf);
 }
 
 template <int DT>
@@ -206,16 +224,14 @@ hipError_t launch(const twell_t *h, const hybrid_t *o, int32_t *status, Timer &t
                            o->ell_val);
         tm.mark("hyb_rows_kernel");
     }
-    hipLaunchKernelGGL(hyb_slots_kernel, dim3(h->T > 0 ? (h->T + SNT - 1) / SNT : 1), dim3(SNT),
-                       0, s, o->row_nnz, h->T, o->K, o->max_ovf, o->row_slot, o->ovf_rows,
-                       o->n_ovf, status);
-    tm.mark("hyb_slots_kernel");
-    if (o->max_ovf > 0 && h->T > 0) {
-        hipLaunchKernelGGL(hyb_dense_kernel<DT>, dim3(o->max_ovf), dim3(DNT), 0, s, h->count,
-                           h->col, h->val, nt, h->width, h->d_ff, o->max_ovf, o->ovf_rows,
-                           o->n_ovf, o->dense, status);
-        tm.mark("hyb_dense_kernel");
-    }
+    // R workgroups per block of rows, for about one backup row each at the
+    // capacity: the capacity's rows spread over the blocks, at most RMAX
+    const int nblk = h->T > 0 ? (h->T + SNT - 1) / SNT : 1;
+    const int R = std::max(1, std::min(RMAX, (o->max_ovf + nblk - 1) / nblk));
+    hipLaunchKernelGGL((hyb_backup_kernel<DT>), dim3(nblk * R), dim3(SNT), 0, s, o->row_nnz,
+                       h->T, o->K, o->max_ovf, R, o->row_slot, o->ovf_rows, o->n_ovf, h->count,
+                       h->col, h->val, nt, h->width, h->d_ff, o->dense, status);
+    tm.mark("hyb_backup_kernel");
     return hipGetLastError();
 }
 

@@ -63,8 +63,8 @@ CSRC = os.path.join(ROOT, "activation_sparse_ffn_gemm_amd", "csrc")
 KERNEL_SOURCES = {
     "gate_pack_kernel": "gate_pack.hip", "ffn_fwd_kernel": "ffn_fwd.hip",
     "fwd_up_kernel": "ffn_fwd.hip", "fwd_down_kernel": "ffn_fwd.hip",
-    "hyb_rows_kernel": "to_hybrid.hip", "hyb_slots_kernel": "to_hybrid.hip",
-    "hyb_dense_kernel": "to_hybrid.hip", "hfwd_ell_kernel": "hyb_fwd.hip",
+    "hyb_rows_kernel": "to_hybrid.hip", "hyb_backup_kernel": "to_hybrid.hip",
+    "hfwd_ell_kernel": "hyb_fwd.hip",
     "hfwd_up_kernel": "ffn_fwd.hip", "hfwd_down_kernel": "ffn_fwd.hip",
     "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "prefix_ud_kernel": "bwd.hip",
     "fill_dxdw_kernel": "bwd.hip", "dec_gate_mm_kernel": "decode.hip",
@@ -249,12 +249,12 @@ def kernel_work(ctx):
                             "per nonzero one wd row (as 8 slices); a and column per nonzero; y"),
         "hyb_rows_kernel": ("hbm", T * n_t * 4 + nnz_ell * 8 + 4 * T,
                             "TwELL counts + ELL rows' entries read; ELL entries, row_nnz written"),
-        "hyb_slots_kernel": ("hbm", 8 * T + 4 * n_ovf,
-                             "row_nnz read, row_slot and the backup rows' ids written"),
-        "hyb_dense_kernel": ("hbm", n_ovf * n_t * (4 + ctx.get("W", 128) * (2 + esz))
-                             + n_ovf * dff * esz,
-                             "backup rows' TwELL tiles (counts and every slot) read, dense "
-                             "backup rows written"),
+        "hyb_backup_kernel": ("hbm", 8 * T + 4 * n_ovf
+                              + n_ovf * n_t * (4 + ctx.get("W", 128) * (2 + esz))
+                              + n_ovf * dff * esz,
+                              "row_nnz read, row_slot and the backup rows' ids written; the "
+                              "backup rows' TwELL tiles (counts and every slot) read, dense "
+                              "backup rows written"),
         "bwd_neuron_kernel": ("hbm", nnz_ell * (2 * row_b + 4 + 2 + 8)
                               + dff * (2 * row_b + 3 * dm * 4),
                               "per ELL nonzero one x row + one dy row + CSC slot, h, du/dg; "
