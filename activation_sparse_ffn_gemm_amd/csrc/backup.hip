@@ -27,15 +27,17 @@
 // significant bits); float32 inputs keep one float32 array.
 //
 // y_O and dx_O have few rows and a long K (d_ff, or 2-4 segments of it): K is
-// split over S workgroups per tile, each writing a float32 partial; the ELL
-// row kernels that run next (they skip backup rows otherwise) add a backup
-// row's S partials in order and store the row (see BkPart).
+// split over S workgroups per tile, each writing a float32 partial. A backup
+// row's S partials are added in split order, starting from zero, by the ELL
+// row kernels that run next (they skip backup rows otherwise; see BkPart), or
+// for the large layers' y_O by a third forward launch (bk_out).
 // Row counts are device values: workgroups whose rows all lie past n_ovf
 // return at once, and the grids are sized for the capacity max_ovf. The
 // backward's products run as extra workgroups of the ELL passes' launches
 // (the u/da tiles with the block scans, the dx_O and dW tiles with the CSC
 // fill; bwd.hip), so that a layer without backup rows pays no launch for them;
-// the forward's two have launches of their own (this file).
+// the forward's have launches of their own (this file), on a second stream
+// beside the ELL passes for the large layers (hyb_fwd.hip).
 #include "backup_tiles.hpp"
 
 using namespace bk;
@@ -89,6 +91,42 @@ __global__ __launch_bounds__(CY::NT, 2) void bk_y_kernel(
                               blockIdx.x, blockIdx.y, blockIdx.z, L);
 }
 
+// y rows of the backup rows: y[ovf_rows[m]] = sum over s = 0 .. S-1, in that
+// order from zero, of part[s][m] (float32 [S][R][d_model]). One wave per row,
+// four floats per lane (d_model is a multiple of 64), eight splits in flight.
+constexpr int OUT_NT = 256;
+__global__ __launch_bounds__(OUT_NT) void bk_out_kernel(
+    const float *__restrict__ part, const int32_t *__restrict__ ovf_rows,
+    const int32_t *__restrict__ n_ovf_p, int max_ovf, int R, int S, int dm,
+    float *__restrict__ y)
+{
+    const int m = blockIdx.x * (OUT_NT / 64) + wave_id();
+    if (m >= n_rows(n_ovf_p, max_ovf))
+        return;
+    const int lane = threadIdx.x & 63;
+    const size_t stride = (size_t)R * dm;
+    const float *src = part + (size_t)m * dm;
+    float *dst = y + (size_t)ovf_rows[m] * dm;
+    for (int c = lane * 4; c < dm; c += 256) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < S; s0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = *(const float4 *)(src + (size_t)min(s0 + u, S - 1) * stride + c);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) {
+                    acc.x += v[u].x;
+                    acc.y += v[u].y;
+                    acc.z += v[u].z;
+                    acc.w += v[u].w;
+                }
+        }
+        *(float4 *)(dst + c) = acc;
+    }
+}
+
 } // namespace
 
 // ---------------------------------------------------------------- host side
@@ -119,7 +157,7 @@ BkLayout bk_layout(int dt, int dm, int dff, int max_ovf, bool bwd)
 
 template <int DT>
 void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd, int dm, float *y,
-               uint8_t *ws, Timer &tm, hipStream_t s)
+               uint8_t *ws, bool out_rows, Timer &tm, hipStream_t s)
 {
     const int dff = h->d_ff;
     const BkLayout L = bk_layout(DT, dm, dff, h->max_ovf, false);
@@ -134,6 +172,12 @@ void bk_fwd_dt(const void *x, const hybrid_t *h, const void *wu, const void *wd,
                        (const uint8_t *)wd, h->n_ovf, h->max_ovf, dm, dff, L.R, L.S,
                        (float *)(ws + L.part));
     tm.mark("bk_y_kernel");
+    if (!out_rows)
+        return;
+    hipLaunchKernelGGL(bk_out_kernel, dim3(L.R / (OUT_NT / 64)), dim3(OUT_NT), 0, s,
+                       (const float *)(ws + L.part), h->ovf_rows, h->n_ovf, h->max_ovf, L.R, L.S,
+                       dm, y);
+    tm.mark("bk_out_kernel");
 }
 
 BkPart bk_part(int dt, int dm, int dff, int max_ovf, bool bwd, const void *ws)
@@ -170,12 +214,13 @@ BkGather bk_gather(int dt, int dm, int dff, int max_ovf, void *ws)
 }
 
 void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
-                   const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s)
+                   const void *wd, int dm, float *y, void *ws, bool out_rows, Timer &tm,
+                   hipStream_t s)
 {
     if (h->max_ovf <= 0 || h->T <= 0)
         return;
     if (dt == TWELL_BF16)
-        bk_fwd_dt<TWELL_BF16>(x, h, wu, wd, dm, y, (uint8_t *)ws, tm, s);
+        bk_fwd_dt<TWELL_BF16>(x, h, wu, wd, dm, y, (uint8_t *)ws, out_rows, tm, s);
     else
-        bk_fwd_dt<TWELL_F32>(x, h, wu, wd, dm, y, (uint8_t *)ws, tm, s);
+        bk_fwd_dt<TWELL_F32>(x, h, wu, wd, dm, y, (uint8_t *)ws, out_rows, tm, s);
 }

@@ -14,8 +14,12 @@ struct BkPart {
 
 size_t bk_workspace(int dt, int dm, int dff, int max_ovf, bool bwd);
 BkPart bk_part(int dt, int dm, int dff, int max_ovf, bool bwd, const void *ws);
+// The forward's backup products (A, then the split-K partials of y_O); with
+// out_rows, a third launch sums each backup row's partials into its y row
+// (otherwise the ELL rows' kernel does, through bk_finish_row).
 void launch_bk_fwd(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
-                   const void *wd, int dm, float *y, void *ws, Timer &tm, hipStream_t s);
+                   const void *wd, int dm, float *y, void *ws, bool out_rows, Timer &tm,
+                   hipStream_t s);
 
 // The backward's products run as extra workgroups of the ELL passes' launches
 // (bwd.hip; device side in backup_tiles.hpp): their operands in the

@@ -366,31 +366,21 @@ __global__ __launch_bounds__(NT) void hfwd_up_kernel(
 }
 
 // Down pass: y[t][slice k] from the token's (a, column) list. For the forward
-// over a hybrid (row_slot non-null) the list is the ELL row itself and a
-// backup row's slice is the sum, in split order, of the dense product's
-// partials.
+// over a hybrid (row_slot non-null) the list is the ELL row itself; backup
+// rows are skipped (their y rows come from the dense products).
 template <int DT, int SPL, int G>
 __global__ __launch_bounds__(NT) void fwd_down_kernel(
     SliceSrc src, int dff, Slices sl, const float *__restrict__ ac,
     const int16_t *__restrict__ cc, const int32_t *__restrict__ rn, int cap, int T, int dm,
-    float *__restrict__ y, const int32_t *__restrict__ row_slot, BkPart bp, int max_ovf)
+    float *__restrict__ y, const int32_t *__restrict__ row_slot)
 {
     constexpr int EPW = DT == TWELL_BF16 ? 2 : 1;
     const int lane = threadIdx.x & 63, wv = wave_id();
     const int k = blockIdx.x % NXCD;
     const int t = (blockIdx.x / NXCD) * (NT / 64) + wv;
     const int nk = sl.valid(k);
-    if (t >= T || nk == 0)
+    if (t >= T || nk == 0 || (row_slot && row_slot[t] >= 0))
         return;
-    if (row_slot) {
-        const int slot = row_slot[t];
-        if (slot >= 0) {
-            if (bp.part && slot < max_ovf)
-                bk_finish_row<SPL, EPW>(bp, slot, sl.ndw, k * sl.sww, k * sl.sww + nk, lane,
-                                        y + (size_t)t * dm);
-            return;
-        }
-    }
     const int n = min(rn[t], cap);
     const float *arow = ac + (size_t)t * cap;
     const int16_t *crow = cc + (size_t)t * cap;
@@ -491,13 +481,13 @@ void launch_nw(const void *x, const twell_t *h, const void *wu, const void *wd, 
     const int spl = (sl.sww + 63) / 64;
     if (spl <= 1)
         hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
-                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr);
     else if (spl == 2)
         hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
-                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr);
     else
         hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, src,
-                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr, BkPart{nullptr, 0, 0}, 0);
+                           dff, sl, ac, cc, rn, L.cap, T, dm, y, nullptr);
     tm.mark("fwd_down_kernel");
 }
 
@@ -529,8 +519,7 @@ size_t hyb_split_workspace(int dt, int T, int dm, int dff, int K)
 namespace {
 template <int DT, int NW>
 void launch_hyb_split_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd, int dm,
-                         float *y, uint8_t *ws, BkPart bp, int32_t *status, Timer &tm,
-                         hipStream_t s)
+                         float *y, uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int T = h->T, dff = h->d_ff, nt = dff / TWELL_TILE_C;
     const int groups = (T + NT / 64 - 1) / (NT / 64);
@@ -548,37 +537,34 @@ void launch_hyb_split_nw(const void *x, const hybrid_t *h, const void *wu, const
     const int spl = (sl.sww + 63) / 64;
     if (spl <= 1)
         hipLaunchKernelGGL((fwd_down_kernel<DT, 1, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
-                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
-                           h->max_ovf);
+                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot);
     else if (spl == 2)
         hipLaunchKernelGGL((fwd_down_kernel<DT, 2, 8>), dim3(groups * NXCD), dim3(NT), 0, s, src,
-                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
-                           h->max_ovf);
+                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot);
     else
         hipLaunchKernelGGL((fwd_down_kernel<DT, 4, 4>), dim3(groups * NXCD), dim3(NT), 0, s, src,
-                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot, bp,
-                           h->max_ovf);
+                           dff, sl, ac, h->ell_col, h->row_nnz, h->K, T, dm, y, h->row_slot);
     tm.mark("hfwd_down_kernel");
 }
 } // namespace
 
 void launch_hyb_split(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
-                      const void *wd, int dm, float *y, void *ws, BkPart bp, int32_t *status,
-                      Timer &tm, hipStream_t s)
+                      const void *wd, int dm, float *y, void *ws, int32_t *status, Timer &tm,
+                      hipStream_t s)
 {
 #define TW_CASE(D, N) \
-    case N: launch_hyb_split_nw<D, N>(x, h, wu, wd, dm, y, (uint8_t *)ws, bp, status, tm, s); break;
+    case N: launch_hyb_split_nw<D, N>(x, h, wu, wd, dm, y, (uint8_t *)ws, status, tm, s); break;
     if (dt == TWELL_BF16) {
         switch (row_nw<TWELL_BF16>(dm)) {
             TW_CASE(TWELL_BF16, 1) TW_CASE(TWELL_BF16, 2) TW_CASE(TWELL_BF16, 4)
             TW_CASE(TWELL_BF16, 8) TW_CASE(TWELL_BF16, 16)
-        default: launch_hyb_split_nw<TWELL_BF16, 32>(x, h, wu, wd, dm, y, (uint8_t *)ws, bp, status, tm, s);
+        default: launch_hyb_split_nw<TWELL_BF16, 32>(x, h, wu, wd, dm, y, (uint8_t *)ws, status, tm, s);
         }
     } else {
         switch (row_nw<TWELL_F32>(dm)) {
             TW_CASE(TWELL_F32, 1) TW_CASE(TWELL_F32, 2) TW_CASE(TWELL_F32, 4)
             TW_CASE(TWELL_F32, 8) TW_CASE(TWELL_F32, 16)
-        default: launch_hyb_split_nw<TWELL_F32, 32>(x, h, wu, wd, dm, y, (uint8_t *)ws, bp, status, tm, s);
+        default: launch_hyb_split_nw<TWELL_F32, 32>(x, h, wu, wd, dm, y, (uint8_t *)ws, status, tm, s);
         }
     }
 #undef TW_CASE

@@ -12,6 +12,20 @@
 //   A = h (.) (x_O W_u)   [n_ovf x d_ff],   y_O = A W_d   [n_ovf x d_model],
 // with A kept as a float32 intermediate (for bf16 inputs as a hi/lo bf16 pair,
 // so the second product keeps about 16 significant bits of A).
+//
+// Small layers: the backup products first, then the ELL rows' kernel, which
+// also stores each backup row's y (the sum of the products' split-K partials).
+// Large layers (the XCD-split ELL passes): the two parts write disjoint rows
+// of y and read only what the conversion wrote, so the backup products and a
+// launch that sums their partials into the backup rows' y run on a second
+// stream of the device, beside the ELL passes (MFMA-bound tiles beside
+// gathers bound by memory requests); the call's stream waits for them before
+// its next work. The fork and join cost about 15 us of host time and more
+// than two empty launches on the device, which a small layer does not win
+// back. Under graph capture, and when per-kernel timing is asked for, all
+// kernels run in order on the call's stream.
+#include <mutex>
+
 #include "backup.hpp"
 #include "rows.hpp"
 
@@ -19,10 +33,57 @@
 bool hyb_use_split(int dt, int T, int dm, int dff);
 size_t hyb_split_workspace(int dt, int T, int dm, int dff, int K);
 void launch_hyb_split(twell_dtype dt, const void *x, const hybrid_t *h, const void *wu,
-                      const void *wd, int dm, float *y, void *ws, BkPart bp, int32_t *status,
-                      Timer &tm, hipStream_t s);
+                      const void *wd, int dm, float *y, void *ws, int32_t *status, Timer &tm,
+                      hipStream_t s);
 
 namespace {
+
+// ---------------------------------------------------------------- side stream
+// Per device: a non-blocking stream of default priority and two events, made
+// on first use and kept until the process ends. The mutex holds one call's
+// fork ... join sequence together when several host threads call at once
+// (their backup products then also queue one after another on this stream).
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex m;
+    bool ok = false;
+};
+constexpr int MAX_DEVICES = 64;
+SideStream g_side[MAX_DEVICES];
+std::once_flag g_side_once[MAX_DEVICES];
+
+// The side stream of stream s's device, or nullptr when s is being captured,
+// its device is unknown or the stream could not be made (the caller then
+// stays on s).
+SideStream *side_stream(hipStream_t s)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    int d = -1;
+    if (hipStreamGetDevice(s, &d) != hipSuccess || d < 0 || d >= MAX_DEVICES) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::call_once(g_side_once[d], [d] {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(d) != hipSuccess)
+            return;
+        SideStream &ss = g_side[d];
+        // both streams are on one device: a device-scope release orders them
+        // (the default system-scope one writes back and invalidates the caches)
+        const unsigned ef = hipEventDisableTiming | hipEventReleaseToDevice;
+        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&ss.fork, ef) == hipSuccess &&
+                hipEventCreateWithFlags(&ss.join, ef) == hipSuccess;
+        (void)hipSetDevice(cur);
+        (void)hipGetLastError();
+    });
+    return g_side[d].ok ? &g_side[d] : nullptr;
+}
 
 constexpr int NT = 256; // 4 waves = 4 rows per workgroup
 
@@ -48,7 +109,7 @@ __global__ __launch_bounds__(NT) void hfwd_ell_kernel(
     if (slot >= 0) { // a backup row: y is the sum of the dense product's partials
         if (bp.part && slot < max_ovf)
             bk_finish_row<NWP, RP::EPW>(bp, slot, part.ndw, part.base, part.ndw, lane,
-                                            y + (size_t)t * dm);
+                                        y + (size_t)t * dm);
         return;
     }
     uint32_t xw[NW];
@@ -102,21 +163,40 @@ void launch_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd,
                uint8_t *ws, int32_t *status, Timer &tm, hipStream_t s)
 {
     const int T = h->T, dff = h->d_ff;
-    launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, tm, s);
-    const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, false, ws);
-    if (hyb_use_split(DT, T, dm, dff)) { // many tokens, large weights: XCD-local passes
-        const size_t off = (bk_workspace(DT, dm, dff, h->max_ovf, false) + 255) & ~(size_t)255;
-        launch_hyb_split((twell_dtype)DT, x, h, wu, wd, dm, y, ws + off, bp, status, tm, s);
+    if (!hyb_use_split(DT, T, dm, dff)) {
+        launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, false, tm, s);
+        const BkPart bp = bk_part(DT, dm, dff, h->max_ovf, false, ws);
+        constexpr int NWP = NW < 16 ? NW : 16;
+        constexpr int G = NW <= 4 ? 4 : 1; // entries in flight per wave (occupancy first)
+        const int parts = row_parts<DT>(dm, NWP);
+        hipLaunchKernelGGL((hfwd_ell_kernel<DT, NW, NWP, G>),
+                           dim3((T + NT / 64 - 1) / (NT / 64), parts), dim3(NT), 0, s,
+                           (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col, h->ell_val, T,
+                           h->K, dff, (const uint8_t *)wu, (const uint8_t *)wd, dm, y, bp,
+                           h->max_ovf, status);
+        tm.mark("hfwd_ell_kernel");
         return;
     }
-    constexpr int NWP = NW < 16 ? NW : 16;
-    constexpr int G = NW <= 4 ? 4 : 1; // entries in flight per wave (occupancy first)
-    const int parts = row_parts<DT>(dm, NWP);
-    hipLaunchKernelGGL((hfwd_ell_kernel<DT, NW, NWP, G>), dim3((T + NT / 64 - 1) / (NT / 64), parts),
-                       dim3(NT), 0, s, (const uint8_t *)x, h->row_nnz, h->row_slot, h->ell_col,
-                       h->ell_val, T, h->K, dff, (const uint8_t *)wu, (const uint8_t *)wd, dm, y,
-                       bp, h->max_ovf, status);
-    tm.mark("hfwd_ell_kernel");
+    // many tokens, large weights: XCD-local ELL passes on s; fork: the backup
+    // products on the side stream after everything already on s; join: s
+    // waits for them after its own kernels
+    SideStream *ss = h->max_ovf > 0 && T > 0 && !tm.t ? side_stream(s) : nullptr;
+    std::unique_lock<std::mutex> lk;
+    if (ss) {
+        lk = std::unique_lock<std::mutex>(ss->m);
+        if (hipEventRecord(ss->fork, s) != hipSuccess ||
+            hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            lk.unlock();
+            ss = nullptr;
+        }
+    }
+    launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, true, tm, ss ? ss->s : s);
+    const bool join = ss && hipEventRecord(ss->join, ss->s) == hipSuccess;
+    const size_t off = (bk_workspace(DT, dm, dff, h->max_ovf, false) + 255) & ~(size_t)255;
+    launch_hyb_split((twell_dtype)DT, x, h, wu, wd, dm, y, ws + off, status, tm, s);
+    if (ss && (!join || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess))
+        (void)hipStreamSynchronize(ss->s); // cannot order s after the side stream: wait here
 }
 
 template <int DT>

@@ -66,7 +66,8 @@ KERNEL_SOURCES = {
     "hyb_rows_kernel": "to_hybrid.hip", "hyb_backup_kernel": "to_hybrid.hip",
     "hfwd_ell_kernel": "hyb_fwd.hip",
     "hfwd_up_kernel": "ffn_fwd.hip", "hfwd_down_kernel": "ffn_fwd.hip",
-    "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "prefix_ud_kernel": "bwd.hip",
+    "bk_a_kernel": "backup.hip", "bk_y_kernel": "backup.hip", "bk_out_kernel": "backup.hip",
+    "prefix_ud_kernel": "bwd.hip",
     "fill_dxdw_kernel": "bwd.hip", "dec_gate_mm_kernel": "decode.hip",
     "dec_pack_kernel": "decode.hip", "dec_up_kernel": "decode.hip",
     "dec_down_kernel": "decode.hip", "dec_gate_gemv_kernel": "decode.hip",
@@ -273,6 +274,9 @@ def kernel_work(ctx):
                              "per ELL nonzero one wd row (as 8 slices) + (col, a); y rows"),
         "bk_a_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "A = h_O (.) x_O W_u (1 GEMM)"),
         "bk_y_kernel": ("mfma", 2.0 * n_ovf * dm * dff, "y_O = A W_d (1 GEMM)"),
+        "bk_out_kernel": ("hbm", n_ovf * dm * 4 * (ctx.get("S_y", 1) + 1) + 8 * n_ovf,
+                          "per backup row its S_y float32 partials of y_O read, its y row "
+                          "written"),
         # the backward's backup products ride on the ELL scans' and fill's
         # launches: with backup rows the products dominate those launches
         "prefix_ud_kernel": (("mfma", 2 * 2.0 * n_ovf * dm * dff,
@@ -424,8 +428,17 @@ class Layer:
             ell = self.hy.row_slot < 0
             out.update(n_ovf=int(self.hy.n_ovf.item()),
                        nnz_ell=int(self.hy.row_nnz[ell].sum()),
-                       R=(self.w.max_ovf + 127) // 128 * 128)
+                       R=(self.w.max_ovf + 127) // 128 * 128, S_y=self.y_splits())
         return out
+
+    def y_splits(self):
+        """K splits of the forward's y_O product, by the library's rule: about
+        1024 workgroups over the 128 x 128 tiles of the capacity (rows padded
+        to 256), at most 16, at least 16 K steps of 128 bytes each."""
+        R = (self.w.max_ovf + 255) // 256 * 256
+        tiles = (R // 128) * ((self.w.d_model + 127) // 128)
+        nk = (2 if self.esz == 2 else 1) * (self.w.d_ff * self.esz // 128)
+        return max(1, min(16, max(1, 1024 // max(tiles, 1)), max(1, nk // 16)))
 
 
 def dense_fns(torch, L):
@@ -582,7 +595,7 @@ def train_leg(torch, tw, L, steps, workload, l1, dense=True):
                    "backward (dx, dW_g, dW_u, dW_d)",
            "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
            "kernels": kernel_entries(kms, work), "roofline": roofline_of(kms, work, workload)}
-    bk = [k for k in kms if k.startswith("bk_")
+    bk = [k for k in kms if (k.startswith("bk_") and k != "bk_out_kernel")
           or (ctx["n_ovf"] > 0 and k in ("prefix_ud_kernel", "fill_dxdw_kernel"))]
     if bk:
         fl = sum(work[k][1] for k in bk)

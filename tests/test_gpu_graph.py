@@ -15,6 +15,11 @@ DEV = "cuda:0"
 @pytest.mark.parametrize("w", [
     synth.Workload("graph-skewed", 512, 256, 768, "bf16", 0.02, skew_frac=0.05, skew_density=0.3,
                    K=40, max_ovf=64, width=128),
+    # 1029 tokens and 16 MB weights: the XCD-split forward, whose backup
+    # products run on a second stream when called eagerly and in order on the
+    # captured stream, so replays check the two orders agree bit for bit
+    synth.Workload("graph-split", 1029, 2048, 4096, "bf16", 0.01, skew_frac=0.05,
+                   skew_density=0.3, K=128, max_ovf=128, width=128),
     synth.DECODE_2B.with_(T=8),
 ], ids=lambda w: w.name)
 def test_step_graph_replays_equal_eager(w):
