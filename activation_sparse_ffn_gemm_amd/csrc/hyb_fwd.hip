@@ -24,10 +24,9 @@
 // than two empty launches on the device, which a small layer does not win
 // back. Under graph capture, and when per-kernel timing is asked for, all
 // kernels run in order on the call's stream.
-#include <mutex>
-
 #include "backup.hpp"
 #include "rows.hpp"
+#include "side.hpp"
 
 
 bool hyb_use_split(int dt, int T, int dm, int dff);
@@ -37,53 +36,6 @@ void launch_hyb_split(twell_dtype dt, const void *x, const hybrid_t *h, const vo
                       hipStream_t s);
 
 namespace {
-
-// ---------------------------------------------------------------- side stream
-// Per device: a non-blocking stream of default priority and two events, made
-// on first use and kept until the process ends. The mutex holds one call's
-// fork ... join sequence together when several host threads call at once
-// (their backup products then also queue one after another on this stream).
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    std::mutex m;
-    bool ok = false;
-};
-constexpr int MAX_DEVICES = 64;
-SideStream g_side[MAX_DEVICES];
-std::once_flag g_side_once[MAX_DEVICES];
-
-// The side stream of stream s's device, or nullptr when s is being captured,
-// its device is unknown or the stream could not be made (the caller then
-// stays on s).
-SideStream *side_stream(hipStream_t s)
-{
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    int d = -1;
-    if (hipStreamGetDevice(s, &d) != hipSuccess || d < 0 || d >= MAX_DEVICES) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    std::call_once(g_side_once[d], [d] {
-        int cur = -1;
-        if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(d) != hipSuccess)
-            return;
-        SideStream &ss = g_side[d];
-        // both streams are on one device: a device-scope release orders them
-        // (the default system-scope one writes back and invalidates the caches)
-        const unsigned ef = hipEventDisableTiming | hipEventReleaseToDevice;
-        ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-                hipEventCreateWithFlags(&ss.fork, ef) == hipSuccess &&
-                hipEventCreateWithFlags(&ss.join, ef) == hipSuccess;
-        (void)hipSetDevice(cur);
-        (void)hipGetLastError();
-    });
-    return g_side[d].ok ? &g_side[d] : nullptr;
-}
 
 constexpr int NT = 256; // 4 waves = 4 rows per workgroup
 
@@ -182,21 +134,14 @@ void launch_nw(const void *x, const hybrid_t *h, const void *wu, const void *wd,
     // waits for them after its own kernels
     SideStream *ss = h->max_ovf > 0 && T > 0 && !tm.t ? side_stream(s) : nullptr;
     std::unique_lock<std::mutex> lk;
-    if (ss) {
-        lk = std::unique_lock<std::mutex>(ss->m);
-        if (hipEventRecord(ss->fork, s) != hipSuccess ||
-            hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
-            (void)hipGetLastError();
-            lk.unlock();
-            ss = nullptr;
-        }
-    }
+    if (ss && !side_fork(ss, s, lk))
+        ss = nullptr;
     launch_bk_fwd((twell_dtype)DT, x, h, wu, wd, dm, y, ws, true, tm, ss ? ss->s : s);
-    const bool join = ss && hipEventRecord(ss->join, ss->s) == hipSuccess;
+    const bool marked = ss && side_mark(ss, 1);
     const size_t off = (bk_workspace(DT, dm, dff, h->max_ovf, false) + 255) & ~(size_t)255;
     launch_hyb_split((twell_dtype)DT, x, h, wu, wd, dm, y, ws + off, status, tm, s);
-    if (ss && (!join || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess))
-        (void)hipStreamSynchronize(ss->s); // cannot order s after the side stream: wait here
+    if (ss)
+        side_wait(ss, 1, marked, s);
 }
 
 template <int DT>
