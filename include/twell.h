@@ -257,6 +257,14 @@ int twell_to_hybrid(const twell_t *h, const hybrid_t *out, int32_t *dev_status,
  * intermediate in the workspace, for bf16 inputs as a hi/lo bf16 pair).
  *   x [T][d_model] dtype dt; y [T][d_model] float32, every row written.
  *   workspace: at least hybrid_fwd_workspace_bytes(...) bytes.
+ * Streams: for large layers (at least 1024 tokens and 16 MB per weight
+ * matrix) the backup rows' products run on a second stream that the library
+ * keeps per device (non-blocking, default priority), ordered after the work
+ * already on `stream` and joined back into it before the call returns: work
+ * queued on `stream` afterwards sees every row of y, as with one stream.
+ * While `stream` is being captured into a graph, and when timing is given,
+ * every kernel runs on `stream`. Calls from several host threads at once
+ * share the second stream (their backup products run one after another).
  * Undefined if the hybrid's OVF_CAPACITY bit was raised.
  * Errors: NULL / SHAPE / DTYPE / ALIGN / WORKSPACE / HIP.
  */
