@@ -81,6 +81,47 @@ def test_hybrid_fwd_training_layer_full(orc):
     assert_close(y, orc.ffn_hybrid(f64(d["x"]), ref, f64(d["wu_t"]), f64(d["wd"])), w.dtype, "y")
 
 
+def test_hybrid_fwd_concurrent_threads(orc):
+    """Two host threads, each on a stream of its own, run the large-layer
+    forward (1029 tokens, 16 MB weights: the backup rows' products go to the
+    library's second stream) at the same time, four calls each: every result
+    equals the one-thread result bit for bit, and no status bit is raised."""
+    import threading
+    announce("hyb fwd two threads")
+    d = synth.make_integer_inputs(1029, 2048, 4096, "bf16", 0.03, skew_rows=51)
+    ref = oracle_hybrid(orc, d, "bf16", 256, 64)
+    assert ref["n_ovf"] > 0
+    hy = upload_hybrid(ref, "bf16")
+    want = run_fwd(d, hy)
+    x, wu, wd = (d[k].to(DEV) for k in ("x", "wu_t", "wd"))
+    torch.cuda.synchronize()
+    got, errors = [[], []], []
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(4):
+                    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+                    got[k].append((tw.hybrid_fwd(x, hy, wu, wd, status=st), st))
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(2):
+        assert len(got[k]) == 4
+        for y, st in got[k]:
+            assert int(st.item()) == 0
+            assert torch.equal(y, want)
+
+
 def test_hybrid_fwd_agrees_with_twell_fwd():
     """On one TwELL, the forward over its hybrid and the TwELL forward are the
     same sums (GPU against GPU; each is checked against the oracle above)."""
