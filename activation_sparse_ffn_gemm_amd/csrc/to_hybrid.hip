@@ -7,13 +7,14 @@
 //   1. rows:   one wave per row sums the tile counts (row_nnz) and, for a row
 //              with row_nnz <= K, concatenates its tiles into ELL row t; the
 //              tiles are in column order, so the ELL row is ascending.
-//   2. backup: R workgroups per block of 256 rows. Each counts the overflow
-//              rows of the blocks before its own (a reduction over row_nnz)
-//              and scans its block's flags, so backup slots follow ascending
-//              row order; the first of the R writes row_slot and ovf_rows (and,
-//              in the last block, n_ovf), and workgroup j builds the block's
-//              backup rows j, j + R, ... (zeros, then the row's entries) in
-//              LDS and stores them with 16-byte lanes. Slots and dense rows
+//   2. backup: R workgroups per block of 256 rows. Each scans its block's
+//              flags; the first of the R, and those with a backup row to
+//              build, then count the overflow rows of the blocks before their
+//              own (a reduction over row_nnz), so backup slots follow
+//              ascending row order. The first writes row_slot and ovf_rows
+//              (and, in the last block, n_ovf), and workgroup j builds the
+//              block's backup rows j, j + R, ... (zeros, then the row's
+//              entries) in LDS and stores them with 16-byte lanes. Slots and dense rows
 //              share the launch, so backup rows cost no launch of their own.
 #include <algorithm>
 
@@ -157,9 +158,23 @@ __global__ __launch_bounds__(SNT) void hyb_backup_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
     const int blk = blockIdx.x / R, j = blockIdx.x % R;
     const int r0 = blk * SNT;
+    // this block: one flag per thread, ranks by a block scan (ballots per
+    // wave, wave totals in LDS)
+    const int t = r0 + tid;
+    const bool f = t < T && row_nnz[t] > K;
+    const unsigned long long m = __ballot(f);
+    if (lane == 0)
+        wsum[wv] = __popcll(m);
     if (tid == 0)
         n_before = 0;
     __syncthreads();
+    int nb = 0, in_blk = 0; // backup rows of this block; of the waves before this one
+    for (int w = 0; w < SNT / 64; ++w) {
+        in_blk += w < wv ? wsum[w] : 0;
+        nb += wsum[w];
+    }
+    if (j != 0 && j >= nb) // uniform: no row to build and not the block's first workgroup
+        return;
     // overflow rows of the blocks before this one: 8 loads per thread in
     // flight (rows clamped, flags masked), per-thread counts summed in LDS
     int mine = 0;
@@ -174,22 +189,12 @@ __global__ __launch_bounds__(SNT) void hyb_backup_kernel(
     }
     if (mine)
         atomicAdd(&n_before, mine);
-    // this block: one flag per thread, slots by a block scan (ballots per
-    // wave, wave totals in LDS)
-    const int t = r0 + tid;
-    const bool f = t < T && row_nnz[t] > K;
-    const unsigned long long m = __ballot(f);
-    if (lane == 0)
-        wsum[wv] = __popcll(m);
-    __syncthreads();
-    int in_blk = 0; // overflow rows of this block before this thread's wave
-    for (int w = 0; w < wv; ++w)
-        in_blk += wsum[w];
-    const int first = n_before;
     const int rank = in_blk + __popcll(m & ((1ull << lane) - 1ull)); // within the block
-    const int slot = first + rank;
     if (f)
         brows[rank] = t;
+    __syncthreads(); // n_before and brows complete
+    const int first = n_before;
+    const int slot = first + rank;
     if (j == 0) {
         if (t < T) {
             row_slot[t] = f ? slot : -1;
@@ -197,18 +202,12 @@ __global__ __launch_bounds__(SNT) void hyb_backup_kernel(
                 ovf_rows[slot] = t;
         }
         if (tid == SNT - 1 && r0 + SNT >= T) { // last block: the true total
-            int total = first;
-            for (int w = 0; w < SNT / 64; ++w)
-                total += wsum[w];
+            const int total = first + nb;
             *n_ovf = total;
             if (total > max_ovf)
                 raise_status(status, TWELL_DEV_OVF_CAPACITY);
         }
     }
-    int nb = 0; // backup rows of this block
-    for (int w = 0; w < SNT / 64; ++w)
-        nb += wsum[w];
-    __syncthreads(); // brows complete
     for (int k = j; k < nb && first + k < max_ovf; k += R)
         build_dense_row<DT>(count, col, val, nt, W, dff, brows[k], first + k, dense, status,
                             rowbuf);
