@@ -79,16 +79,18 @@ def oracle_bwd(orc, d, ref, l1=0.0):
                                                 (150, 192, 384, 12, 9, 0.5),
                                                 (130, 128, 16384, 512, 5, 0.0),
                                                 (1024, 2048, 4096, 256, 51, 0.0),
-                                                (1024, 2304, 4096, 256, 51, 0.0)])
+                                                (1024, 2304, 4096, 256, 51, 0.0),
+                                                (1024, 2048, 2048, 256, 51, 0.0)])
 def test_bwd_integer_exact(orc, dtype, T, dm, dff, K, skew, l1):
     """Integer inputs (and an L1 weight of 0.5): ELL gathers and the backup
     rows' hi/lo MFMA products are exact, so every gradient matches the oracle
     bit for bit. d_ff 16384 gives 256 groups of 64 neurons (the column offsets
     sum many group totals) and 16 mask chunks. The last two shapes (1024
     tokens, 16 MB or more of weights in bf16) take the XCD-local dx pass
-    (slices of 512 and 576 bytes)."""
-    if dtype == "f32" and T == 1024:
-        pytest.skip("one dtype is enough for the two-pass shape")
+    (slices of 512 and 576 bytes); the 1024-token f32 shape (d_model 2048 by
+    d_ff 2048, 16 MB in f32) takes it with float32 MFMA backup products."""
+    if T == 1024 and (dtype == "f32") != (dff == 2048):
+        pytest.skip("one dtype per two-pass shape")
     announce("bwd int", dtype, T, dm, dff, K, skew, l1)
     d = synth.make_integer_inputs(T, dm, dff, dtype, 0.03, with_dy=True, skew_rows=skew)
     ref = oracle_hybrid(orc, d, dtype, K, 64)

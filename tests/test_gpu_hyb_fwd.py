@@ -34,15 +34,18 @@ def run_fwd(d, hy):
 @pytest.mark.parametrize("T,dm,dff,K,skew", [(1, 64, 128, 8, 0), (150, 192, 384, 12, 9),
                                              (300, 512, 1024, 40, 21), (77, 320, 256, 128, 0),
                                              (1029, 2048, 4096, 256, 51),
-                                             (1029, 2304, 4096, 256, 51)])
+                                             (1029, 2304, 4096, 256, 51),
+                                             (1029, 2048, 2048, 256, 51)])
 def test_hybrid_fwd_integer_exact(orc, dtype, T, dm, dff, K, skew):
     """Integer inputs: the ELL gathers and the backup rows' hi/lo MFMA products
-    are exact, so y matches the oracle bit for bit. The last two shapes (1029
-    tokens, 16 MB or more of weights in bf16) take the two-pass XCD-local ELL
-    path, with a ragged last group of tokens: wd's slices read in place
-    (d_model 2048) and from a slice-major copy (d_model 2304)."""
-    if dtype == "f32" and T == 1029:
-        pytest.skip("one dtype is enough for the two-pass shape")
+    are exact, so y matches the oracle bit for bit. The 1029-token shapes with
+    16 MB or more of weights take the two-pass XCD-local ELL path, with a
+    ragged last group of tokens and the backup products on the second stream:
+    in bf16 wd's slices read in place (d_model 2048) and from a slice-major
+    copy (d_model 2304); in f32 (float32 MFMA products, one array per
+    intermediate) d_model 2048 by d_ff 2048."""
+    if T == 1029 and (dtype == "f32") != (dff == 2048):
+        pytest.skip("one dtype per two-pass shape")
     announce("hyb fwd int", dtype, T, dm, dff, K, skew)
     d = synth.make_integer_inputs(T, dm, dff, dtype, 0.03, skew_rows=skew)
     ref = oracle_hybrid(orc, d, dtype, K, 64)
