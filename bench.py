@@ -594,7 +594,11 @@ def train_leg(torch, tw, L, steps, workload, l1, dense=True):
            "step": "gate GEMM + TwELL pack, TwELL->hybrid, forward over the hybrid, hybrid "
                    "backward (dx, dW_g, dW_u, dW_d)",
            "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-           "kernels": kernel_entries(kms, work), "roofline": roofline_of(kms, work, workload)}
+           "kernels": kernel_entries(kms, work), "roofline": roofline_of(kms, work, workload),
+           "kernels_note": "per-kernel times from a separate pass with events between the kernels, "
+                           "every kernel in order on one stream; in the timed step a large "
+                           "layer's backup-row forward products (bk_*) run on a second stream "
+                           "beside its ELL passes"}
     bk = [k for k in kms if (k.startswith("bk_") and k != "bk_out_kernel")
           or (ctx["n_ovf"] > 0 and k in ("prefix_ud_kernel", "fill_dxdw_kernel"))]
     if bk:
