@@ -119,6 +119,38 @@ def test_bwd_gaussian(orc, w):
         assert_close(a, b, w.dtype, n, mag=m)
 
 
+def test_capacity_exceeded_large_layer(orc):
+    """A large layer (1029 tokens, 16 MB of weights: the two-pass forward with
+    its second stream, the XCD-split dx pass) whose backup rows outnumber the
+    capacity: the GPU conversion raises OVF_CAPACITY (and nothing else), the
+    forward and the backward still run to the end, and the rows they keep
+    defined (the ELL rows and the first max_ovf backup rows: y and dx) equal
+    the oracle's over a hybrid with room for every backup row."""
+    announce("capacity exceeded, large layer")
+    T, dm, dff, K, mo = 1029, 2048, 4096, 256, 16
+    d = synth.make_integer_inputs(T, dm, dff, "bf16", 0.03, with_dy=True, skew_rows=51)
+    x64 = f64(d["x"])
+    g = orc.gate(x64, f64(d["wg_t"]))
+    tw_r, (cnt, col, val) = oracle_twell_for_gpu(orc, g, 128, "bf16", DEV)
+    short = orc.to_hybrid(tw_r, K, mo)
+    full = orc.to_hybrid(tw_r, K, T)
+    assert short["capacity_exceeded"] and full["n_ovf"] > mo and not full["capacity_exceeded"]
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    hy = tw.to_hybrid(tw.Twell(cnt, col, val), K, mo, status=st)
+    x, dy, wg, wu, wd = (d[k].to(DEV) for k in ("x", "dy", "wg_t", "wu_t", "wd"))
+    y = tw.hybrid_fwd(x, hy, wu, wd, status=st)
+    dx = tw.ffn_bwd(x, dy, hy, wg, wu, wd, status=st)[0]
+    torch.cuda.synchronize()
+    assert int(st.item()) == tw.DEV_OVF_CAPACITY
+    slot = full["row_slot"]
+    kept = (slot < 0) | (slot < mo)
+    assert kept.sum() == T - (full["n_ovf"] - mo)
+    want_y = orc.ffn_hybrid(x64, full, f64(d["wu_t"]), f64(d["wd"]))
+    want_dx = oracle_bwd(orc, d, full)[0]
+    assert np.array_equal(f64(y)[kept], want_y[kept])
+    assert np.array_equal(f64(dx)[kept], want_dx[kept])
+
+
 def test_bwd_training_layer_full(orc):
     """The skewed 1.5B training layer at full size (T = 8192, 410 backup rows),
     with the recipe's L1 weight 2e-5: every gradient element against the
